@@ -1,0 +1,150 @@
+"""Float64 CPU oracle of the speculative-decoding verify step (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.  The C
+source (``spec_oracle.c``) shares no code with the HIP implementation.
+
+What it computes is stated in ``spec_oracle.c``: the exact accept / residual /
+bonus rule and the greedy case of "Decodificación Especulativa y EAGLE"
+(section "La Regla de Exactitud"), with randomness drawn from Philox4x32-10 by
+counter, so that a result is a pure function of the inputs and the seed.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "spec_oracle.c")
+LIB = os.path.join(HERE, "liboracle_specverify.so")
+
+F32, BF16, F64 = 0, 1, 2
+FLAG_ACCEPT_NEAR_TIE = 1
+FLAG_RACE_NEAR_TIE = 2
+FLAG_RESIDUAL_EMPTY = 4
+
+
+def build(force: bool = False, extra_flags=(), out: str = LIB, src: str = SRC) -> str:
+    """Compile the oracle with gcc (plain IEEE float64, no contraction)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", *extra_flags, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_lib = None
+
+
+def load(path: str = LIB):
+    """Load (building first if needed) and declare the C entry points."""
+    global _lib
+    if path == LIB and _lib is not None:
+        return _lib
+    if path == LIB:
+        build()
+    lib = ctypes.CDLL(path)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_u01.argtypes = [ctypes.c_uint32]
+    lib.oracle_u01.restype = ctypes.c_double
+    lib.oracle_accept_uniform.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32]
+    lib.oracle_accept_uniform.restype = ctypes.c_double
+    lib.oracle_race_exponential.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32]
+    lib.oracle_race_exponential.restype = ctypes.c_double
+    vp = ctypes.c_void_p
+    lib.oracle_spec_verify.argtypes = [
+        ctypes.c_int, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        vp, vp, vp, ctypes.c_uint64, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_spec_verify.restype = ctypes.c_int
+    if path == LIB:
+        _lib = lib
+    return lib
+
+
+def philox4x32_10(ctr, key, lib=None) -> np.ndarray:
+    """Philox4x32-10 block for a 4-word counter and 2-word key."""
+    lib = lib or load()
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    o = (ctypes.c_uint32 * 4)()
+    lib.oracle_philox4x32_10(c, k, o)
+    return np.array(list(o), dtype=np.uint32)
+
+
+def u01(x: int, lib=None) -> float:
+    return (lib or load()).oracle_u01(int(x) & 0xFFFFFFFF)
+
+
+def accept_uniform(seed: int, b: int, t: int, lib=None) -> float:
+    return (lib or load()).oracle_accept_uniform(seed, b, t)
+
+
+def race_exponential(seed: int, b: int, pos: int, v: int, lib=None) -> float:
+    return (lib or load()).oracle_race_exponential(seed, b, pos, v)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def verify(dtype: int, target, draft, offsets, tokens, temperature, seed: int, V: int,
+           max_k: int, reqs=None, lib=None, n_draft_rows=None) -> dict:
+    """Run the oracle over a packed batch (see the workload module for layout).
+
+    Returns numpy arrays: accept_len [B], out_tokens [sum(K_b)+B], p_at / q_at
+    [sum(K_b)] (float64), flags [B], race_best / race_gap [B].  With ``reqs``
+    only the listed requests are evaluated (others keep accept_len == -2).
+    """
+    lib = lib or load()
+    if dtype == F32:
+        target = np.ascontiguousarray(target, dtype=np.float32)
+        draft = None if draft is None else np.ascontiguousarray(draft, dtype=np.float32)
+    elif dtype == BF16:
+        target = np.ascontiguousarray(target, dtype=np.uint16)
+        draft = None if draft is None else np.ascontiguousarray(draft, dtype=np.uint16)
+    elif dtype == F64:
+        target = np.ascontiguousarray(target, dtype=np.float64)
+        draft = None if draft is None else np.ascontiguousarray(draft, dtype=np.float64)
+    else:
+        raise ValueError(f"unknown dtype {dtype}")
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    B = offsets.shape[0] - 1
+    n_d = int(offsets[-1]) if n_draft_rows is None else int(n_draft_rows)
+    if tokens.shape[0] == 0:
+        tokens = np.zeros(1, dtype=np.int32)
+    acc = np.full(B, -2, dtype=np.int32)
+    out = np.full(n_d + B, -2, dtype=np.int32)
+    p_at = np.full(max(n_d, 1), np.nan)
+    q_at = np.full(max(n_d, 1), np.nan)
+    flags = np.zeros(B, dtype=np.uint32)
+    best = np.full(B, np.nan)
+    gap = np.full(B, np.nan)
+    r = None
+    if reqs is not None:
+        r = np.ascontiguousarray(reqs, dtype=np.int32)
+    rc = lib.oracle_spec_verify(dtype, _ptr(target), _ptr(draft), B, V, max_k, n_d,
+                                _ptr(offsets), _ptr(tokens), _ptr(temperature),
+                                ctypes.c_uint64(seed), _ptr(r), 0 if r is None else r.shape[0],
+                                _ptr(acc), _ptr(out), _ptr(p_at), _ptr(q_at), _ptr(flags),
+                                _ptr(best), _ptr(gap))
+    if rc != 0:
+        raise ValueError(f"oracle_spec_verify rejected its arguments (rc={rc})")
+    return dict(accept_len=acc, out_tokens=out, p_at=p_at[:n_d], q_at=q_at[:n_d],
+                flags=flags, race_best=best, race_gap=gap)
+
+
+def verify_batch(batch, reqs=None, greedy_only: bool = False, lib=None) -> dict:
+    """Oracle over a workload ``Batch``; ``greedy_only`` forces T=0 everywhere."""
+    temp = np.zeros_like(batch.temperature) if greedy_only else batch.temperature
+    return verify(batch.dtype, batch.target, None if greedy_only else batch.draft,
+                  batch.offsets, batch.tokens, temp, batch.seed, batch.V, batch.max_k,
+                  reqs=reqs, lib=lib, n_draft_rows=batch.n_draft_rows)

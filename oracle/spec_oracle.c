@@ -1,0 +1,347 @@
+/*
+ * spec_oracle.c -- plain, slow, float64 CPU oracle of the speculative-decoding
+ * verify / accept / resample step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header
+ * or constant table with the HIP implementation; the two meet only through
+ * the seeded inputs.
+ *
+ * What it follows (pages: "Decodificación Especulativa y EAGLE", lesson 25 of
+ * ai-engineering.academy, and Perplexity's "Accelerating Sonar through
+ * speculation"):
+ *   - section "La Regla de Exactitud": for each drafted x_t draw r ~ U(0,1);
+ *     accept iff r < p(x_t)/q(x_t); otherwise draw the replacement from the
+ *     normalised positive part (p - q)+ and stop;
+ *   - section "El Concepto", steps 3-4: scan left to right, keep the longest
+ *     accepted prefix; if every draft is accepted draw a bonus token from the
+ *     target row after the last draft;
+ *   - section "La Regla de Exactitud", greedy case: at temperature 0 accept iff
+ *     argmax(p) == x_t, else emit argmax(p) and stop;
+ *   - the listing in section "Desarrolla": the same temperature divides the
+ *     target and the draft logits before the softmax.
+ * Readings taken where the pages are silent (see the design notes):
+ *   - accept test in product form r*q < p (strict), so q = 0 < p accepts;
+ *   - the residual is the pointwise vector (p - q)+, not p minus the scalar
+ *     q(x_t) (the listing subtracts the scalar; the rule's formula does not);
+ *   - argmax ties go to the lowest index; NaN entries never win a greedy row;
+ *   - sampling is an exponential race: winner = argmax_v (ln w_v - ln E_v)
+ *     with E_v = -ln U_v, U_v from Philox4x32-10 keyed by the seed and
+ *     counter (v >> 2, position, request, 0), word v & 3; the accept uniform
+ *     r_t is word 0 of counter (0, t, request, 1);
+ *   - U(x) = (2*(x >> 9) + 1) * 2^-24, an exact value in (0, 1).
+ *
+ * Philox4x32-10 is written from its published definition (Salmon, Moraes,
+ * Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): ten
+ * rounds of two 32x32->64 multiplies, with a Weyl-sequence key schedule.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_F64 2 /* test-only input type: exact float64 logits */
+
+/* flags written per request */
+#define OR_FLAG_ACCEPT_NEAR_TIE 1u  /* some evaluated |r*q - p| < 1e-6 */
+#define OR_FLAG_RACE_NEAR_TIE 2u    /* best - second < 1e-6 * max(1, |best|) */
+#define OR_FLAG_RESIDUAL_EMPTY 4u   /* no token had p > q; raced on p instead */
+
+/* ---------------------------------------------------------------- Philox */
+
+void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2],
+                          uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u; /* round multipliers */
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u; /* key increments */
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    uint64_t p0 = (uint64_t)M0 * (uint64_t)c0;
+    uint64_t p1 = (uint64_t)M1 * (uint64_t)c2;
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+/* U(x) = (2*(x>>9) + 1) / 2^24: 2^23 equally spaced points strictly in (0,1). */
+double oracle_u01(uint32_t x) {
+  return (2.0 * (double)(x >> 9) + 1.0) / 16777216.0;
+}
+
+static uint32_t philox_word(uint64_t seed, uint32_t c0, uint32_t c1, uint32_t c2,
+                            uint32_t c3, int word) {
+  uint32_t ctr[4] = {c0, c1, c2, c3};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32_10(ctr, key, out);
+  return out[word];
+}
+
+/* Accept uniform r_t for request b, draft position t. */
+double oracle_accept_uniform(uint64_t seed, int32_t b, int32_t t) {
+  return oracle_u01(philox_word(seed, 0u, (uint32_t)t, (uint32_t)b, 1u, 0));
+}
+
+/* Exponential variate E_v = -ln U_v of the race at (request b, position pos). */
+double oracle_race_exponential(uint64_t seed, int32_t b, int32_t pos, int32_t v) {
+  uint32_t x = philox_word(seed, (uint32_t)v >> 2, (uint32_t)pos, (uint32_t)b, 0u, v & 3);
+  return -log(oracle_u01(x));
+}
+
+/* ---------------------------------------------------------------- inputs */
+
+static double logit(const void* base, int dtype, int64_t row, int32_t V, int32_t v) {
+  int64_t i = row * (int64_t)V + v;
+  if (dtype == OR_F32) return (double)((const float*)base)[i];
+  if (dtype == OR_F64) return ((const double*)base)[i];
+  /* bf16: the stored 16 bits are the top half of a float32 */
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Largest non-NaN value of a row (-inf if none). */
+static double row_max(const void* base, int dtype, int64_t row, int32_t V) {
+  double m = -INFINITY;
+  for (int32_t v = 0; v < V; ++v) {
+    double z = logit(base, dtype, row, V, v);
+    if (z > m) m = z;
+  }
+  return m;
+}
+
+/* Greedy argmax: lowest index attaining the maximum; -1 if no finite maximum. */
+static int32_t row_argmax(const void* base, int dtype, int64_t row, int32_t V) {
+  double m = -INFINITY;
+  int32_t idx = -1;
+  for (int32_t v = 0; v < V; ++v) {
+    double z = logit(base, dtype, row, V, v);
+    if (z > m) {
+      m = z;
+      idx = v;
+    }
+  }
+  if (!isfinite(m)) return -1;
+  return idx;
+}
+
+/* log-sum-exp of row/T, max-shifted; NaN/inf results signal a bad row. */
+static double row_lse(const void* base, int dtype, int64_t row, int32_t V, double T) {
+  double m = row_max(base, dtype, row, V);
+  if (!isfinite(m)) return NAN;
+  double s = 0.0;
+  for (int32_t v = 0; v < V; ++v) s += exp(logit(base, dtype, row, V, v) / T - m / T);
+  return m / T + log(s);
+}
+
+/* ---------------------------------------------------------------- one request */
+
+typedef struct {
+  int dtype;
+  const void* target;
+  const void* draft;
+  int32_t B, V, max_k, n_draft_rows;
+  const int32_t* offsets;
+  const int32_t* tokens;
+  const float* temperature;
+  uint64_t seed;
+} oracle_inputs;
+
+typedef struct {
+  int32_t* accept_len;   /* [B] */
+  int32_t* out_tokens;   /* [n_draft_rows + B] */
+  double* p_at;          /* [n_draft_rows] or NULL */
+  double* q_at;          /* [n_draft_rows] or NULL */
+  uint32_t* flags;       /* [B] or NULL */
+  double* race_best;     /* [B] or NULL: winning race key (oracle scale) */
+  double* race_gap;      /* [B] or NULL: best - second-best race key */
+} oracle_outputs;
+
+static void fail_request(const oracle_inputs* in, const oracle_outputs* o, int32_t b,
+                         int offsets_ok) {
+  o->accept_len[b] = -1;
+  if (!offsets_ok) return;
+  int32_t k = in->offsets[b + 1] - in->offsets[b];
+  for (int32_t i = 0; i <= k; ++i) o->out_tokens[in->offsets[b] + b + i] = -1;
+  for (int32_t t = 0; t < k; ++t) {
+    if (o->p_at) o->p_at[in->offsets[b] + t] = NAN;
+    if (o->q_at) o->q_at[in->offsets[b] + t] = NAN;
+  }
+}
+
+void oracle_verify_one(const oracle_inputs* in, const oracle_outputs* o, int32_t b) {
+  const int32_t V = in->V;
+  if (o->flags) o->flags[b] = 0;
+  if (o->race_best) o->race_best[b] = NAN;
+  if (o->race_gap) o->race_gap[b] = NAN;
+
+  /* validate the request's slice of the packed layout */
+  int32_t off = in->offsets[b], off1 = in->offsets[b + 1];
+  int offsets_ok = off >= 0 && off1 <= in->n_draft_rows && off1 - off >= 0 &&
+                   off1 - off <= in->max_k;
+  if (!offsets_ok) {
+    fail_request(in, o, b, 0);
+    return;
+  }
+  const int32_t K = off1 - off;
+  const int64_t trow0 = (int64_t)off + b; /* target row t of b is trow0 + t */
+  const int64_t drow0 = off;              /* draft row t of b is drow0 + t */
+  const double T = (double)in->temperature[b];
+  if (!isfinite(T) || T < 0.0 || (T > 0.0 && in->draft == NULL)) {
+    fail_request(in, o, b, 1);
+    return;
+  }
+  for (int32_t t = 0; t < K; ++t) {
+    int32_t x = in->tokens[off + t];
+    if (x < 0 || x >= V) {
+      fail_request(in, o, b, 1);
+      return;
+    }
+  }
+
+  int32_t n, y;
+  if (T == 0.0) {
+    /* greedy rule: accept x_t iff argmax(p_t) == x_t; emit argmax at the stop */
+    int32_t g[64];
+    for (int32_t t = 0; t <= K; ++t) {
+      g[t] = row_argmax(in->target, in->dtype, trow0 + t, V);
+      if (g[t] < 0) {
+        fail_request(in, o, b, 1);
+        return;
+      }
+    }
+    n = K;
+    for (int32_t t = 0; t < K; ++t) {
+      if (g[t] != in->tokens[off + t]) {
+        n = t;
+        break;
+      }
+    }
+    y = g[n];
+    for (int32_t t = 0; t < K; ++t) {
+      if (o->p_at) o->p_at[off + t] = NAN;
+      if (o->q_at) o->q_at[off + t] = NAN;
+    }
+  } else {
+    /* sampled: p_t = softmax(P_t / T), q_t = softmax(Q_t / T) */
+    double lp[64], lq[64];
+    for (int32_t t = 0; t <= K; ++t) {
+      lp[t] = row_lse(in->target, in->dtype, trow0 + t, V, T);
+      if (!isfinite(lp[t])) {
+        fail_request(in, o, b, 1);
+        return;
+      }
+    }
+    for (int32_t t = 0; t < K; ++t) {
+      lq[t] = row_lse(in->draft, in->dtype, drow0 + t, V, T);
+      if (!isfinite(lq[t])) {
+        fail_request(in, o, b, 1);
+        return;
+      }
+    }
+    /* left-to-right ratio test; every position's p/q is reported */
+    n = K;
+    for (int32_t t = 0; t < K; ++t) {
+      int32_t x = in->tokens[off + t];
+      double p = exp(logit(in->target, in->dtype, trow0 + t, V, x) / T - lp[t]);
+      double q = exp(logit(in->draft, in->dtype, drow0 + t, V, x) / T - lq[t]);
+      if (o->p_at) o->p_at[off + t] = p;
+      if (o->q_at) o->q_at[off + t] = q;
+      if (n < K) continue; /* already stopped: later positions are not tested */
+      double r = oracle_accept_uniform(in->seed, b, t);
+      if (fabs(r * q - p) < 1e-6 && o->flags) o->flags[b] |= OR_FLAG_ACCEPT_NEAR_TIE;
+      if (!(r * q < p)) n = t;
+    }
+
+    /* race: residual (p_n - q_n)+ after a rejection, else bonus from p_K */
+    int residual = n < K;
+    int any_positive = 0;
+    if (residual) {
+      for (int32_t v = 0; v < V && !any_positive; ++v) {
+        double p = exp(logit(in->target, in->dtype, trow0 + n, V, v) / T - lp[n]);
+        double q = exp(logit(in->draft, in->dtype, drow0 + n, V, v) / T - lq[n]);
+        if (p - q > 0.0) any_positive = 1;
+      }
+      if (!any_positive && o->flags) o->flags[b] |= OR_FLAG_RESIDUAL_EMPTY;
+    }
+    double best = -INFINITY, second = -INFINITY;
+    y = -1;
+    for (int32_t v = 0; v < V; ++v) {
+      double key;
+      double e = oracle_race_exponential(in->seed, b, n, v);
+      if (residual && any_positive) {
+        double p = exp(logit(in->target, in->dtype, trow0 + n, V, v) / T - lp[n]);
+        double q = exp(logit(in->draft, in->dtype, drow0 + n, V, v) / T - lq[n]);
+        double w = p - q;
+        if (!(w > 0.0)) continue;
+        key = log(w) - log(e);
+      } else {
+        key = logit(in->target, in->dtype, trow0 + n, V, v) / T - log(e);
+      }
+      if (key > best) {
+        second = best;
+        best = key;
+        y = v;
+      } else if (key > second) {
+        second = key;
+      }
+    }
+    if (o->race_best) o->race_best[b] = best;
+    if (o->race_gap) o->race_gap[b] = best - second;
+    if (best - second < 1e-6 * fmax(1.0, fabs(best)) && o->flags)
+      o->flags[b] |= OR_FLAG_RACE_NEAR_TIE;
+  }
+
+  o->accept_len[b] = n;
+  for (int32_t i = 0; i < n; ++i) o->out_tokens[trow0 + i] = in->tokens[off + i];
+  o->out_tokens[trow0 + n] = y;
+  for (int32_t i = n + 1; i <= K; ++i) o->out_tokens[trow0 + i] = -1;
+}
+
+/*
+ * Batch entry: evaluates the requests listed in `reqs` (all B when reqs is
+ * NULL), each with its own request index b (the Philox counter uses b).
+ * Output arrays are laid out for the whole batch; entries of requests not
+ * evaluated are left untouched.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_spec_verify(int dtype, const void* target, const void* draft, int32_t B, int32_t V,
+                       int32_t max_k, int32_t n_draft_rows, const int32_t* offsets,
+                       const int32_t* tokens, const float* temperature, uint64_t seed,
+                       const int32_t* reqs, int32_t n_reqs, int32_t* accept_len,
+                       int32_t* out_tokens, double* p_at, double* q_at, uint32_t* flags,
+                       double* race_best, double* race_gap) {
+  if (!target || !offsets || !temperature || !accept_len || !out_tokens) return -1;
+  if (B < 1 || V < 1 || max_k < 0 || max_k > 63) return -1;
+  if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_F64) return -1;
+  oracle_inputs in = {dtype, target, draft, B, V, max_k, n_draft_rows, offsets, tokens,
+                      temperature, seed};
+  oracle_outputs o = {accept_len, out_tokens, p_at, q_at, flags, race_best, race_gap};
+  if (reqs) {
+    for (int32_t i = 0; i < n_reqs; ++i) {
+      if (reqs[i] < 0 || reqs[i] >= B) return -1;
+      oracle_verify_one(&in, &o, reqs[i]);
+    }
+  } else {
+    for (int32_t b = 0; b < B; ++b) oracle_verify_one(&in, &o, b);
+  }
+  return 0;
+}

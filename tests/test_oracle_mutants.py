@@ -1,0 +1,87 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Every case below copies the oracle's C source, plants one plausible mistake by
+text substitution, builds the copy in a temporary directory and runs the pins
+of tests/oracle_pins.py against it.  A mistake that no pin notices would mean
+the pins cannot vouch for that part of the oracle.  The committed oracle is
+never modified.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+MUTANTS = {
+    # residual drops the draft term: raced on p instead of (p - q)+
+    "residual_without_q": ("double w = p - q;", "double w = p;"),
+    # the lesson listing's slip: subtract the scalar q(x_t) from the vector p
+    "residual_minus_scalar_q": (
+        "double w = p - q;",
+        "double w = p - exp(logit(in->draft, in->dtype, drow0 + n, V, "
+        "in->tokens[off + n]) / T - lq[n]);"),
+    # ratio test with its operands transposed
+    "accept_transposed": ("if (!(r * q < p)) n = t;", "if (!(r * p < q)) n = t;"),
+    # one uniform reused for every position
+    "accept_uniform_reused": ("oracle_accept_uniform(in->seed, b, t)",
+                              "oracle_accept_uniform(in->seed, b, 0)"),
+    # draft logits not divided by the temperature
+    "draft_untempered": (
+        "lq[t] = row_lse(in->draft, in->dtype, drow0 + t, V, T);",
+        "lq[t] = row_lse(in->draft, in->dtype, drow0 + t, V, 1.0);"),
+    # the max shift of the log-sum-exp applied without the temperature
+    "lse_shift_untempered": ("/ T - m / T);", "/ T - m);"),
+    # greedy ties resolved to the last index
+    "greedy_last_tie": ("if (z > m) {\n      m = z;\n      idx = v;",
+                        "if (z >= m) {\n      m = z;\n      idx = v;"),
+    # target rows addressed like draft rows (missing the per-request +b)
+    "target_row_alignment": ("const int64_t trow0 = (int64_t)off + b;",
+                             "const int64_t trow0 = (int64_t)off;"),
+    # bonus drawn from the last drafted position instead of the one after it
+    "bonus_wrong_row": ("key = logit(in->target, in->dtype, trow0 + n, V, v) / T - log(e);",
+                        "key = logit(in->target, in->dtype, trow0 + (n > 0 ? n - 1 : 0), V, v)"
+                        " / T - log(e);"),
+    # exponential race with the wrong sign on the exponential variate
+    "race_sign": ("key = log(w) - log(e);", "key = log(w) + log(e);"),
+    # Philox: wrong multiplier in the first lane
+    "philox_multiplier": ("uint64_t p0 = (uint64_t)M0 * (uint64_t)c0;",
+                          "uint64_t p0 = (uint64_t)M1 * (uint64_t)c0;"),
+    # Philox: wrong key increment
+    "philox_key_schedule": ("k1 += W1;", "k1 += W0;"),
+    # uniform map that can return 0
+    "u01_map": ("return (2.0 * (double)(x >> 9) + 1.0) / 16777216.0;",
+                "return (double)(x >> 8) / 16777216.0;"),
+}
+
+# cheap pins first; the first failing pin ends a case
+ORDER = [P.pin_philox_kat, P.pin_u01, P.pin_softmax_vs_scipy, P.pin_greedy_vs_numpy,
+         P.pin_temperature_invariance, P.pin_identical_draft_accepts,
+         P.pin_disjoint_draft_rejects, P.pin_faults, P.pin_plain_sampling,
+         P.pin_exact_enumeration, P.pin_closed_form]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    src = src.replace(old, new)
+    d = tempfile.mkdtemp(prefix=f"mutant_{name}_")
+    c_path = os.path.join(d, "mutant.c")
+    so_path = os.path.join(d, "mutant.so")
+    with open(c_path, "w") as f:
+        f.write(src)
+    oracle.build(force=True, out=so_path, src=c_path, extra_flags=("-w",))
+    lib = oracle.load(so_path)
+    caught = None
+    for pin in ORDER:
+        try:
+            pin(lib)
+        except Exception:  # an assertion, or a pin that cannot even digest the output
+            caught = pin.__name__
+            break
+    assert caught is not None, f"no pin catches the planted mistake {name}"
+    print(f"{name}: caught by {caught}")
