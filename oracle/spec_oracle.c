@@ -45,7 +45,7 @@
 #define OR_F64 2 /* test-only input type: exact float64 logits */
 
 /* flags written per request */
-#define OR_FLAG_ACCEPT_NEAR_TIE 1u  /* some evaluated |r*q - p| < 1e-6 */
+#define OR_FLAG_ACCEPT_NEAR_TIE 1u  /* some evaluated |r*q - p| < 1e-6 * max(p, r*q) */
 #define OR_FLAG_RACE_NEAR_TIE 2u    /* best - second < 1e-6 * max(1, |best|) */
 #define OR_FLAG_RESIDUAL_EMPTY 4u   /* no token had p > q; raced on p instead */
 
@@ -206,7 +206,7 @@ void oracle_verify_one(const oracle_inputs* in, const oracle_outputs* o, int32_t
   const int64_t trow0 = (int64_t)off + b; /* target row t of b is trow0 + t */
   const int64_t drow0 = off;              /* draft row t of b is drow0 + t */
   const double T = (double)in->temperature[b];
-  if (!isfinite(T) || T < 0.0 || (T > 0.0 && in->draft == NULL)) {
+  if (!isfinite(T) || T < 0.0 || (T > 0.0 && K > 0 && in->draft == NULL)) {
     fail_request(in, o, b, 1);
     return;
   }
@@ -268,7 +268,9 @@ void oracle_verify_one(const oracle_inputs* in, const oracle_outputs* o, int32_t
       if (o->q_at) o->q_at[off + t] = q;
       if (n < K) continue; /* already stopped: later positions are not tested */
       double r = oracle_accept_uniform(in->seed, b, t);
-      if (fabs(r * q - p) < 1e-6 && o->flags) o->flags[b] |= OR_FLAG_ACCEPT_NEAR_TIE;
+      /* relative: two tiny probabilities are not a near-tie by themselves */
+      if (fabs(r * q - p) < 1e-6 * fmax(p, r * q) && o->flags)
+        o->flags[b] |= OR_FLAG_ACCEPT_NEAR_TIE;
       if (!(r * q < p)) n = t;
     }
 
