@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = one spec_verify_sample call over the whole synthetic batch of the
+Llama-class workload (B=64 requests, K=4 drafts each, V=128256, bf16 logits;
+half the requests sampled at T=1, half greedy).  Inputs are resident in HBM
+before timing starts; the step rotates over enough copies of the logits
+(>= 1.25 GB) that every step streams from HBM rather than from the 256 MB
+Infinity Cache.  Prints one JSON line.
+
+Reported:
+  value          verified draft positions per second (sum of K_b per step / time)
+  roofline       the row-statistics kernel (all of the HBM traffic): algorithmic
+                 bytes per launch / its mean duration from HIP events recorded on
+                 the launch stream, against 8 TB/s
+  cpu_baseline   the float64 oracle on a bounded sample of the same batch
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "verified draft positions/sec + HBM GB/s (% peak), B=64 K=4 V=128256 bf16"
+SRC = os.path.join(ROOT, "rejection_sampling_verify_scaled_amd", "csrc", "spec_verify.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="synthetic workload number (2: Llama-class, the metric's)")
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(batch) -> int:
+    """Each needed logit read once: (2K+1) rows per sampled request, K+1 per greedy."""
+    esz = 2 if batch.dtype == 1 else 4
+    tot = 0
+    for b in range(batch.B):
+        k = int(batch.offsets[b + 1] - batch.offsets[b])
+        rows = (2 * k + 1) if batch.temperature[b] > 0 else (k + 1)
+        tot += rows * batch.V * esz
+    return tot
+
+
+class Hip:
+    """The few HIP runtime calls the per-kernel timing needs (events)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (binds libamdhip64 to torch's runtime first)
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+
+def traffic_record(workload: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_row_stats_workload{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a HIP GPU")
+    from rejection_sampling_verify_scaled_amd import binding
+    from rejection_sampling_verify_scaled_amd import workloads as W
+
+    lib = binding.load_library()
+    hip = Hip()
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    batch = W.make_batch(args.workload, 0)
+    d = binding.to_device_batch(batch, dev)
+    B, V, K = batch.B, batch.V, batch.max_k
+    n_d = batch.n_draft_rows
+    positions = int(batch.k.sum())
+    alg = algorithmic_bytes(batch)
+    per_copy = d["target"].numel() * d["target"].element_size() + \
+        d["draft"].numel() * d["draft"].element_size()
+    copies = args.copies or max(1, math.ceil(1.25e9 / per_copy))
+    targets = [d["target"]] + [d["target"].clone() for _ in range(copies - 1)]
+    drafts = [d["draft"]] + [d["draft"].clone() for _ in range(copies - 1)]
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(n_d + B, dtype=torch.int32, device=dev)
+    pa = torch.empty(n_d, dtype=torch.float32, device=dev)
+    qa = torch.empty(n_d, dtype=torch.float32, device=dev)
+    ws_n = binding.workspace_bytes(B, V, K)
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    dtype = binding.SV_BF16 if d["target"].dtype == torch.bfloat16 else binding.SV_F32
+    vp = ctypes.c_void_p
+    argsets = []
+    for c in range(copies):
+        argsets.append((vp(targets[c].data_ptr()), vp(drafts[c].data_ptr()), dtype, B, V, K, n_d,
+                        vp(d["offsets"].data_ptr()), vp(d["tokens"].data_ptr()),
+                        vp(d["temperature"].data_ptr()), ctypes.c_uint64(batch.seed),
+                        vp(acc.data_ptr()), vp(out.data_ptr()), vp(pa.data_ptr()),
+                        vp(qa.data_ptr()), vp(ws.data_ptr()), ws_n, sh))
+    call = lib.spec_verify_sample
+    torch.cuda.synchronize()
+    print(f"[bench] B={B} K={K} V={V} copies={copies} ({copies * per_copy / 1e9:.2f} GB); "
+          f"warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        rc = call(*argsets[i % copies])
+        if rc != 0:
+            raise SystemExit(f"spec_verify_sample returned {rc}")
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, synchronised on both sides
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        call(*argsets[i % copies])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = positions / (ms_per_step * 1e-3)
+    print(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / args.steps * 1e6:.2f} us/step)",
+          file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations from events recorded between the two launches
+    n_t = min(args.steps, 200)
+    evs = [[hip.event() for _ in range(3)] for _ in range(n_t)]
+    timed = lib.spec_verify_sample_timed
+    timed.argtypes = list(lib.spec_verify_sample.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
+    timed.restype = ctypes.c_int
+    arrs = [(ctypes.c_void_p * 3)(*[e.value for e in trip]) for trip in evs]
+    for i in range(n_t):
+        rc = timed(*argsets[i % copies], arrs[i])
+        if rc != 0:
+            raise SystemExit(f"spec_verify_sample_timed returned {rc}")
+    torch.cuda.synchronize()
+    k1 = [hip.elapsed_ms(t[0], t[1]) for t in evs]
+    k2 = [hip.elapsed_ms(t[1], t[2]) for t in evs]
+    k1_us = 1e3 * sum(k1) / n_t
+    k2_us = 1e3 * sum(k2) / n_t
+    achieved = alg / (k1_us * 1e-6) / 1e9
+    print(f"[bench] row_stats {k1_us:.2f} us, accept_race {k2_us:.2f} us", file=sys.stderr,
+          flush=True)
+
+    # ---- correctness spot check of this exact launch configuration
+    call(*argsets[0])
+    torch.cuda.synchronize()
+    gpu_acc = acc.cpu().numpy()
+    gpu_out = out.cpu().numpy()
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dtype == binding.SV_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": batch.label, "B": B, "K": K, "V": V,
+                   "sampled_requests": int((batch.temperature > 0).sum()),
+                   "greedy_requests": int((batch.temperature == 0).sum()),
+                   "input_copies_rotated": copies},
+        "hbm_gbs_step": alg / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_step": alg / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": alg,
+        "bytes_per_verified_position": alg / positions,
+        "kernel_us": {"sv_row_stats": k1_us, "sv_accept_race": k2_us},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(args.workload),
+                     "kernel": "sv_row_stats"},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
+              flush=True)
+        olib = oracle.load()
+        t0 = time.perf_counter()
+        passes = 0
+        res = None
+        while True:
+            res = oracle.verify_batch(batch, lib=olib)
+            passes += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - t0
+        greedy = batch.temperature == 0
+        mism = 0
+        for b in range(B):
+            base = int(batch.offsets[b]) + b
+            k = int(batch.offsets[b + 1] - batch.offsets[b])
+            same = gpu_acc[b] == res["accept_len"][b] and \
+                (gpu_out[base:base + k + 1] == res["out_tokens"][base:base + k + 1]).all()
+            flagged = (not greedy[b]) and res["flags"][b] != 0
+            if not same and not flagged:
+                mism += 1
+        line["cpu_baseline"] = {
+            "value": positions * passes / cpu_s, "unit": "positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} passes over the full {B}-request batch of the same workload "
+                      f"(single-threaded float64 C oracle, {cpu_s:.1f} s)"}
+        line["parity_check"] = {"requests": B, "unflagged_mismatches": int(mism),
+                                "flagged": int((res["flags"] != 0).sum())}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

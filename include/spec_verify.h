@@ -1,0 +1,139 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-decoding verify step.
+ *
+ * The operation (pages: "Decodificación Especulativa y EAGLE", ai-engineering.academy
+ * Phase 10 lesson 25; Perplexity, "Accelerating Sonar through speculation"):
+ * a drafter proposed K_b tokens x_0..x_{K_b-1} for request b; the target model
+ * scored the K_b + 1 positions in one forward pass.  This library decides how
+ * many drafts to keep and which token follows them:
+ *   - sampled requests (temperature T_b > 0), section "La Regla de Exactitud":
+ *     with p_t = softmax(target_t / T_b), q_t = softmax(draft_t / T_b), accept
+ *     x_t iff r_t * q_t(x_t) < p_t(x_t) for a uniform r_t, scanning t = 0, 1, ...
+ *     and stopping at the first rejection n; the stop token is drawn from
+ *     (p_n - q_n)+ normalised; if all K_b drafts pass, a bonus token is drawn
+ *     from p_{K_b} (section "El Concepto", steps 3-4);
+ *   - greedy requests (T_b == 0), same section, greedy case: accept x_t iff
+ *     argmax p_t == x_t (lowest index on ties); the stop token is argmax p_n.
+ * The blog post calls this the sampler that finds the accepted length and
+ * samples one extra target token (section "Objetivo-Borrador").
+ *
+ * Randomness is a pure function of (seed, request index b, position, token):
+ *   r_t        = U(Philox4x32-10(key = seed, counter = (0, t, b, 1)).word0)
+ *   E_v (race) = -ln U(Philox4x32-10(key = seed, counter = (v >> 2, pos, b, 0)).word[v & 3])
+ *   U(x)       = (2 * (x >> 9) + 1) * 2^-24,  key = (low 32 bits, high 32 bits) of seed
+ * and every draw from a distribution w is the exponential race
+ *   argmax_v (ln w_v - ln E_v)   (lowest v on exact ties),
+ * so results do not depend on the launch shape or the GPU.
+ *
+ * Layout (packed, row-major, stride V elements; all DEVICE pointers unless noted):
+ *   draft_offsets [B + 1] int32   K_b = draft_offsets[b+1] - draft_offsets[b]
+ *   target_logits [n_draft_rows + B][V]  row t of request b at draft_offsets[b] + b + t,
+ *                                 t = 0..K_b; row t is the target distribution
+ *                                 after the prefix x_0..x_{t-1}
+ *   draft_logits  [n_draft_rows][V]      row t of request b at draft_offsets[b] + t,
+ *                                 the distribution x_t was drawn from
+ *   draft_tokens  [n_draft_rows] int32   x_t of request b at draft_offsets[b] + t
+ *   out_tokens    [n_draft_rows + B] int32 (output)  request b's slot i at
+ *                                 draft_offsets[b] + b + i: x_0..x_{n-1}, then the
+ *                                 stop token, then -1 up to i = K_b
+ *   accept_len    [B] int32 (output)  n_b in [0, K_b] (accepted drafts; n_b + 1
+ *                                 tokens are emitted), or -1 for a failed request
+ *   Logits are float32 (SV_F32) or bfloat16 bit patterns (SV_BF16).
+ *
+ * Ownership: the caller owns every buffer, the workspace included.  The library
+ * allocates nothing, keeps no state between calls, never synchronises, and only
+ * enqueues kernels on `stream` (a hipStream_t; NULL is the default stream).
+ * Outputs are valid once the stream reaches the end of the call's work.  Two
+ * calls that may run concurrently need separate workspaces.
+ *
+ * Errors: a negative return value means nothing was enqueued (except
+ * SV_ERR_LAUNCH, which reports a launch failure).  Per-request problems found
+ * on the device -- K_b outside [0, max_k], a slice outside [0, n_draft_rows),
+ * a draft token outside [0, V), a temperature that is negative, NaN or
+ * infinite, a needed row whose maximum is not finite, or a NaN in a row that
+ * a sampled request reads -- set accept_len[b] = -1 and fill request b's output
+ * slots with -1 (when its slice is valid); other requests are unaffected.
+ */
+#ifndef SPEC_VERIFY_H_
+#define SPEC_VERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_KMAX 8 /* largest per-request draft length */
+
+enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
+
+enum sv_status {
+  SV_OK = 0,
+  SV_ERR_NULL = -1,      /* a required pointer is NULL */
+  SV_ERR_SHAPE = -2,     /* B < 1, V < 1, max_k outside [0, SV_KMAX], n_draft_rows < 0,
+                            or the launch grid would be too large */
+  SV_ERR_DTYPE = -3,     /* dtype is not SV_F32 or SV_BF16 */
+  SV_ERR_WORKSPACE = -4, /* workspace smaller than spec_verify_workspace_bytes() or
+                            not 16-byte aligned */
+  SV_ERR_LAUNCH = -5     /* the HIP runtime rejected a kernel launch */
+};
+
+/* Host function.  Bytes of device workspace a call with these sizes needs
+ * (valid for both dtypes).  Returns 0 for sizes the library rejects. */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t V, int32_t max_k);
+
+/* All-greedy verify (every request follows the temperature-0 rule of section
+ * "La Regla de Exactitud").  Draft logits are not needed and not read.
+ *   target_logits  device, [n_draft_rows + B][V] of `dtype`
+ *   dtype          SV_F32 or SV_BF16 (host scalar)
+ *   B, V, max_k, n_draft_rows   host scalars; max_k bounds every K_b
+ *   draft_offsets, draft_tokens, accept_len, out_tokens   device, see layout
+ *   workspace      device, >= spec_verify_workspace_bytes(B, V, max_k) bytes
+ *   stream         hipStream_t to enqueue on
+ * Returns SV_OK or a negative sv_status. */
+int spec_verify_greedy(const void* target_logits, int32_t dtype, int32_t B, int32_t V,
+                       int32_t max_k, int32_t n_draft_rows, const int32_t* draft_offsets,
+                       const int32_t* draft_tokens, int32_t* accept_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Mixed verify: requests with temperature[b] > 0 follow the sampled rule,
+ * requests with temperature[b] == 0 the greedy rule (their draft rows are not
+ * read, and their greedy results equal spec_verify_greedy's bit for bit).
+ *   draft_logits   device, [n_draft_rows][V] of `dtype`
+ *   temperature    device, [B] float32
+ *   seed           host; Philox key (low word, high word)
+ *   p_at_draft, q_at_draft   optional device outputs [n_draft_rows] float32:
+ *                  p_t(x_t) and q_t(x_t) for every position of a sampled
+ *                  request (also past its first rejection); NaN for greedy or
+ *                  failed requests.  Either may be NULL.
+ * Other arguments as for spec_verify_greedy. */
+int spec_verify_sample(const void* target_logits, const void* draft_logits, int32_t dtype,
+                       int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows,
+                       const int32_t* draft_offsets, const int32_t* draft_tokens,
+                       const float* temperature, uint64_t seed, int32_t* accept_len,
+                       int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify_sample, plus HIP events (hipEvent_t handles created by the
+ * caller) recorded on `stream` around the library's two kernels, so a caller
+ * can measure each kernel's duration on the stream it runs on:
+ *   events[0] before the row-statistics kernel, events[1] between the
+ *   row-statistics and accept/race kernels, events[2] after the latter.
+ * events must point to 3 valid events.  Same results as spec_verify_sample. */
+int spec_verify_sample_timed(const void* target_logits, const void* draft_logits, int32_t dtype,
+                             int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows,
+                             const int32_t* draft_offsets, const int32_t* draft_tokens,
+                             const float* temperature, uint64_t seed, int32_t* accept_len,
+                             int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events);
+
+/* Host function.  Static description of a status code. */
+const char* spec_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H_ */

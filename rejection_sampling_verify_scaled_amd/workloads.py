@@ -24,8 +24,10 @@ round-to-nearest-even.  Both sides of every parity test read these exact bits.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -111,12 +113,14 @@ def storage_to_f64(a: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def _draft_choice(rng: np.random.Generator, draft_row_f64: np.ndarray, T: float) -> int:
-    """The drafter's own token choice: argmax at T=0, else x ~ softmax(row/T)."""
+    """The drafter's own token choice: argmax at T=0, else x ~ softmax(row/T)
+    by inverse CDF (one uniform against the running sum of the weights)."""
     if T == 0.0:
         return int(np.argmax(draft_row_f64))
     z = draft_row_f64 / T
-    w = np.exp(z - z.max())
-    return int(rng.choice(draft_row_f64.shape[0], p=w / w.sum()))
+    c = np.cumsum(np.exp(z - z.max()))
+    i = int(np.searchsorted(c, rng.random() * c[-1], side="right"))
+    return min(i, draft_row_f64.shape[0] - 1)
 
 
 @dataclasses.dataclass
@@ -177,12 +181,19 @@ def _per_request_params(w: Workload, rng: np.random.Generator):
     return k.astype(np.int64), sigma, temp.astype(np.float32)
 
 
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def make_batch(cfg: int, step: int = 0, B: Optional[int] = None,
                temperature_override: Optional[float] = None,
-               progress: bool = False) -> Batch:
+               progress: bool = False, workers: Optional[int] = None) -> Batch:
     """Generate workload ``cfg`` (1..5) at ``step``; ``B`` may shrink the batch.
 
-    Seeds: numpy PCG64 ``default_rng([0x5356, cfg, step])``; Philox key
+    Seeds: the per-request parameters (K_b, sigma_b, T_b) come from numpy PCG64
+    ``default_rng([0x5356, cfg, step])``; request b's rows and draft tokens from
+    its own stream ``default_rng([0x5356, cfg, step, b])``, so requests are
+    generated independently (and in parallel).  The Philox key is
     ``1000*cfg + step``.  Target row t ~ N(0, sigma_t^2) with round(peak_frac*V)
     distinct entries (uniform without replacement) raised by peak_boost; draft
     row t = target row t (before rounding) + N(0, sigma_b^2); both rounded to
@@ -207,23 +218,32 @@ def make_batch(cfg: int, step: int = 0, B: Optional[int] = None,
     draft = np.empty((n_d, V), dtype=sdt)
     tokens = np.empty(n_d, dtype=np.int32)
     n_pk = w.n_peaks
-    for b in range(Bn):
+
+    def one(b: int) -> None:
+        r = np.random.default_rng([GEN_TAG, cfg, step, b])
         kb = int(k[b])
-        z = rng.standard_normal((kb + 1, V), dtype=np.float32) * np.float32(w.target_sigma)
+        z = r.standard_normal((kb + 1, V), dtype=np.float32) * np.float32(w.target_sigma)
         if n_pk > 0:
             for t in range(kb + 1):
-                idx = rng.choice(V, size=n_pk, replace=False)
-                z[t, idx] += np.float32(w.peak_boost)
-        d = z[:kb] + rng.standard_normal((kb, V), dtype=np.float32) * np.float32(sigma[b])
+                z[t, r.choice(V, size=n_pk, replace=False)] += np.float32(w.peak_boost)
+        d = z[:kb] + r.standard_normal((kb, V), dtype=np.float32) * np.float32(sigma[b])
         t0 = int(offsets[b]) + b
         target[t0:t0 + kb + 1] = to_storage(z, w.dtype)
         d0 = int(offsets[b])
         draft[d0:d0 + kb] = to_storage(d, w.dtype)
         for t in range(kb):
-            tokens[d0 + t] = _draft_choice(rng, storage_to_f64(draft[d0 + t], w.dtype),
+            tokens[d0 + t] = _draft_choice(r, storage_to_f64(draft[d0 + t], w.dtype),
                                            float(temp[b]))
-        if progress and (b + 1) % 256 == 0:
-            print(f"  generated {b + 1}/{Bn} requests", flush=True)
+
+    nw = workers or _workers()
+    if nw == 1 or Bn < 8:
+        for b in range(Bn):
+            one(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(nw) as ex:
+            for i, _ in enumerate(ex.map(one, range(Bn))):
+                if progress and (i + 1) % 256 == 0:
+                    print(f"  generated {i + 1}/{Bn} requests", flush=True)
     return Batch(dtype=w.dtype, B=Bn, V=V, max_k=w.max_k, target=target, draft=draft,
                  offsets=offsets.astype(np.int32), tokens=tokens, temperature=temp,
                  seed=philox_seed(cfg, step), sigma=sigma, label=w.name)

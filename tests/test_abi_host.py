@@ -1,0 +1,88 @@
+"""C ABI checks that need no GPU: the library loads, exports what the header
+declares, sizes workspaces, and rejects bad arguments before any HIP call."""
+import ctypes
+
+import pytest
+
+from rejection_sampling_verify_scaled_amd import binding
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = binding.header_functions()
+    assert {"spec_verify_greedy", "spec_verify_sample", "spec_verify_workspace_bytes",
+            "spec_verify_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/spec_verify.h but not exported"
+
+
+def test_workspace_bytes(lib):
+    assert lib.spec_verify_workspace_bytes(64, 128256, 4) > 0
+    assert lib.spec_verify_workspace_bytes(64, 128256, 4) % 256 == 0
+    assert lib.spec_verify_workspace_bytes(1024, 152064, 8) >= \
+        lib.spec_verify_workspace_bytes(64, 152064, 8)
+    for bad in ((0, 10, 1), (1, 0, 1), (1, 10, -1), (1, 10, 9)):
+        assert lib.spec_verify_workspace_bytes(*bad) == 0
+
+
+def _fake(n):  # host addresses are fine: these calls must fail before touching them
+    buf = (ctypes.c_char * n)()
+    return ctypes.cast(buf, ctypes.c_void_p), buf
+
+
+@pytest.mark.parametrize("case", ["null_target", "null_offsets", "null_out", "null_ws",
+                                  "null_draft", "null_temp", "B0", "V0", "maxk9", "maxk_neg",
+                                  "ndraft_neg", "dtype", "ws_small", "ws_misaligned"])
+def test_sample_rejects_bad_arguments(lib, case):
+    B, V, max_k, nd = 4, 64, 2, 8
+    keep = []
+    def p(n=4096):
+        ptr, buf = _fake(n + 64)
+        keep.append(buf)
+        return ctypes.c_void_p((ptr.value + 15) // 16 * 16)
+    ws_n = lib.spec_verify_workspace_bytes(B, V, max_k)
+    args = dict(target=p(), draft=p(), dtype=1, B=B, V=V, max_k=max_k, nd=nd, offs=p(),
+                toks=p(), temp=p(), seed=1, acc=p(), out=p(), pa=None, qa=None,
+                ws=p(ws_n), ws_n=ws_n)
+    expect = {"null_target": -1, "null_offsets": -1, "null_out": -1, "null_ws": -1,
+              "null_draft": -1, "null_temp": -1, "B0": -2, "V0": -2, "maxk9": -2,
+              "maxk_neg": -2, "ndraft_neg": -2, "dtype": -3, "ws_small": -4,
+              "ws_misaligned": -4}[case]
+    if case == "null_target": args["target"] = None
+    if case == "null_offsets": args["offs"] = None
+    if case == "null_out": args["out"] = None
+    if case == "null_ws": args["ws"] = None
+    if case == "null_draft": args["draft"] = None
+    if case == "null_temp": args["temp"] = None
+    if case == "B0": args["B"] = 0
+    if case == "V0": args["V"] = 0
+    if case == "maxk9": args["max_k"] = 9
+    if case == "maxk_neg": args["max_k"] = -1
+    if case == "ndraft_neg": args["nd"] = -1
+    if case == "dtype": args["dtype"] = 7
+    if case == "ws_small": args["ws_n"] = ws_n - 1
+    if case == "ws_misaligned": args["ws"] = ctypes.c_void_p(args["ws"].value + 4)
+    a = args
+    rc = lib.spec_verify_sample(a["target"], a["draft"], a["dtype"], a["B"], a["V"], a["max_k"],
+                                a["nd"], a["offs"], a["toks"], a["temp"], a["seed"], a["acc"],
+                                a["out"], a["pa"], a["qa"], a["ws"], a["ws_n"], None)
+    assert rc == expect, (case, rc)
+    assert lib.spec_verify_status_string(rc)
+
+
+def test_greedy_rejects_bad_arguments(lib):
+    ptr, buf = _fake(1 << 16)
+    base = ctypes.c_void_p((ptr.value + 15) // 16 * 16)
+    ws = lib.spec_verify_workspace_bytes(2, 32, 1)
+    assert lib.spec_verify_greedy(None, 1, 2, 32, 1, 2, base, base, base, base, base, ws,
+                                  None) == -1
+    assert lib.spec_verify_greedy(base, 1, 2, 32, 11, 2, base, base, base, base, base, ws,
+                                  None) == -2
+    assert lib.spec_verify_greedy(base, 5, 2, 32, 1, 2, base, base, base, base, base, ws,
+                                  None) == -3
+    assert lib.spec_verify_greedy(base, 1, 2, 32, 1, 2, base, base, base, base, base, 16,
+                                  None) == -4

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Every test prints the case it is about to launch before touching the GPU.
+Workload numbers follow the synthetic workload table (1 tiny, 2 Llama-class,
+3 large-batch fp32, 4 MTP K=1, 5 ragged).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import Tally, compare, run_gpu
+from rejection_sampling_verify_scaled_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rejection_sampling_verify_scaled_amd import binding
+    binding.load_library()
+    yield
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+
+def test_tiny_1000_steps():
+    """Workload 1: 1000 independent B=1 steps, sampled at T=1 and greedy on the same inputs."""
+    tally_s, tally_g = Tally(), Tally()
+    say("tiny: 1000 steps x (sample T=1, greedy via both entry points)")
+    for step in range(1000):
+        b = W.make_batch(1, step)
+        orc = oracle.verify_batch(b)
+        compare(b, run_gpu(b, "sample"), orc, tally=tally_s)
+        og = oracle.verify_batch(b, greedy_only=True)
+        compare(b, run_gpu(b, "greedy"), og, greedy_only=True, tally=tally_g)
+        bz = W.make_batch(1, step, temperature_override=0.0)
+        compare(bz, run_gpu(bz, "sample"), og, tally=tally_g)
+    print(tally_s, tally_g)
+    assert tally_s.flagged <= 0.001 * tally_s.sampled + 1
+
+
+def _full(cfg, reqs=None, step=0):
+    say(f"workload {cfg}: generating")
+    b = W.make_batch(cfg, step)
+    say(f"workload {cfg}: B={b.B} V={b.V} rows={b.target.shape[0]}+{b.draft.shape[0]} launch")
+    gpu = run_gpu(b, "sample")
+    orc = oracle.verify_batch(b, reqs=reqs)
+    tally = compare(b, gpu, orc, reqs=reqs)
+    print(f"workload {cfg}:", tally)
+    n = tally.sampled
+    assert tally.flagged <= max(1, 0.001 * n), tally
+    return b, gpu, orc, tally
+
+
+def test_llama_b64_k4_bf16_full():
+    b, gpu, orc, tally = _full(2)
+    assert tally.greedy == 32 and tally.sampled == 32
+
+
+def test_large_batch_b256_k8_f32():
+    reqs = list(range(0, 256, 8)) + [255]
+    _full(3, reqs=reqs)
+
+
+def test_mtp_b512_k1_bf16_full():
+    b, gpu, orc, tally = _full(4)
+    assert tally.greedy == 256 and tally.sampled == 256
+
+
+def test_ragged_b1024_bf16():
+    reqs = list(range(0, 1024, 16)) + [1, 2, 3, 1023]
+    _full(5, reqs=reqs)
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
+@pytest.mark.parametrize("V", [1, 3, 37, 1000, 4099, 40001, 70000])
+def test_ragged_vocab_and_k(dtype, V):
+    """Any V (vector and scalar paths, several chunks, ragged tails), K_b in 0..8."""
+    rng = np.random.default_rng(V * 7 + dtype)
+    B = 24
+    ks = [int(x) for x in rng.integers(0, 9, size=B)]
+    temps = rng.choice([0.0, 0.5, 1.0, 1.7], size=B)
+    b = W.make_custom_batch(rng, dtype, V, ks, temps, seed=V + 17, max_k=8)
+    say(f"ragged V={V} dtype={dtype} ks={ks}")
+    gpu = run_gpu(b, "sample")
+    compare(b, gpu, oracle.verify_batch(b))
+    gg = run_gpu(b, "greedy")
+    compare(b, gg, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
+
+
+def test_plain_sampling_k0():
+    """max_k = 0: every request is plain sampling from softmax(z / T)."""
+    rng = np.random.default_rng(3)
+    b = W.make_custom_batch(rng, W.DTYPE_BF16, 5000, [0] * 64, [1.0] * 32 + [0.0] * 32,
+                            seed=99, max_k=0)
+    say("k=0 plain sampling")
+    compare(b, run_gpu(b, "sample"), oracle.verify_batch(b))
+
+
+def test_greedy_ties_bf16():
+    """Planted ties at the row maximum: lowest index must win, bit-exact."""
+    rng = np.random.default_rng(11)
+    V, B = 20000, 48
+    ks = [int(x) for x in rng.integers(1, 9, size=B)]
+    b = W.make_custom_batch(rng, W.DTYPE_BF16, V, ks, [0.0] * B, seed=5, max_k=8)
+    for r in range(b.target.shape[0]):
+        row = W.bf16_bits_to_f32(b.target[r])
+        top = np.float32(row.max() + 2.0)
+        idx = rng.choice(V, size=int(rng.integers(2, 6)), replace=False)
+        b.target[r, idx] = W.f32_to_bf16_bits(np.full(len(idx), top, np.float32))
+    # make some drafts hit the first tied index, some a later tied index
+    for bb in range(B):
+        for t in range(ks[bb]):
+            row = W.bf16_bits_to_f32(b.target_row(bb, t))
+            ties = np.flatnonzero(row == row.max())
+            b.tokens[b.offsets[bb] + t] = ties[0] if rng.random() < 0.8 else ties[-1]
+    say("greedy ties")
+    og = oracle.verify_batch(b, greedy_only=True)
+    compare(b, run_gpu(b, "greedy"), og, greedy_only=True)
+    compare(b, run_gpu(b, "sample"), og)
+
+
+def test_faults_are_per_request():
+    """Bad requests fail alone (accept_len -1, tokens -1); the rest are exact."""
+    rng = np.random.default_rng(12)
+    V, B = 3000, 12
+    ks = [3] * B
+    temps = np.array([1.0] * 6 + [0.0] * 6, dtype=np.float32)
+    b = W.make_custom_batch(rng, W.DTYPE_F32, V, ks, temps, seed=8, max_k=3)
+    b.tokens[b.offsets[1] + 2] = V          # token out of range (sampled)
+    b.tokens[b.offsets[7] + 0] = -5         # token out of range (greedy)
+    b.temperature[2] = -1.0                 # negative temperature
+    b.temperature[3] = np.nan               # NaN temperature
+    b.temperature[4] = np.inf               # infinite temperature
+    b.target[b.offsets[8] + 8 + 1, :] = -np.inf   # greedy row with no finite maximum
+    b.draft[b.offsets[5] + 1, 17] = np.nan        # NaN in a sampled draft row
+    b.target[b.offsets[9] + 9 + 0, 5] = np.nan    # NaN in a greedy row: never wins
+    b.target[b.offsets[10] + 10 + 3, :] = np.inf  # greedy row with +inf maximum
+    say("faults")
+    orc = oracle.verify_batch(b)
+    gpu = run_gpu(b, "sample")
+    tally = compare(b, gpu, orc)
+    assert tally.failed == 8, tally
+    assert gpu["accept_len"][9] >= 0
+
+
+def test_bad_offsets_do_not_read_out_of_bounds():
+    """K_b > max_k and slices past n_draft_rows fail without touching other requests."""
+    rng = np.random.default_rng(13)
+    V = 512
+    b = W.make_custom_batch(rng, W.DTYPE_BF16, V, [2, 3, 2, 2], [1.0, 1.0, 0.0, 1.0], seed=4,
+                            max_k=3)
+    b.max_k = 2  # request 1 (K=3) now exceeds max_k
+    say("bad offsets (k > max_k)")
+    compare(b, run_gpu(b, "sample"), oracle.verify_batch(b))
+
+
+def test_misaligned_base_pointer():
+    """A base pointer that is not 16-byte aligned takes the scalar-load path."""
+    import torch
+    from rejection_sampling_verify_scaled_amd import binding
+    rng = np.random.default_rng(14)
+    V = 4096
+    b = W.make_custom_batch(rng, W.DTYPE_BF16, V, [4] * 8, [1.0] * 4 + [0.0] * 4, seed=21,
+                            max_k=4)
+    d = binding.to_device_batch(b)
+    flat_t = torch.empty(d["target"].numel() + 1, dtype=torch.bfloat16, device="cuda")
+    flat_t[1:] = d["target"].reshape(-1)
+    tgt = flat_t[1:].view(-1, V)
+    flat_d = torch.empty(d["draft"].numel() + 1, dtype=torch.bfloat16, device="cuda")
+    flat_d[1:] = d["draft"].reshape(-1)
+    dr = flat_d[1:].view(-1, V)
+    assert tgt.data_ptr() % 16 != 0
+    say("misaligned base pointers")
+    acc, out, _, _ = binding.spec_verify_sample(tgt, dr, d["offsets"], d["tokens"],
+                                                d["temperature"], b.seed, b.max_k)
+    gpu = dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy())
+    compare(b, gpu, oracle.verify_batch(b), check_pq=False)
+
+
+def test_determinism_and_launch_shape_independence():
+    """Same inputs twice, and a larger max_k (a different grid): identical outputs."""
+    b = W.make_batch(2, 1, B=16)
+    say("determinism")
+    g1 = run_gpu(b, "sample")
+    g2 = run_gpu(b, "sample")
+    b.max_k = 8
+    g3 = run_gpu(b, "sample")
+    for k in ("accept_len", "out_tokens", "p_at", "q_at"):
+        assert np.array_equal(g1[k], g2[k], equal_nan=True), k
+        assert np.array_equal(g1[k], g3[k], equal_nan=True), k
+
+
+def test_greedy_entry_matches_sample_entry():
+    b = W.make_batch(4, 2, B=64, temperature_override=0.0)
+    say("greedy entry == sample entry at T=0")
+    g1 = run_gpu(b, "greedy")
+    g2 = run_gpu(b, "sample")
+    assert np.array_equal(g1["accept_len"], g2["accept_len"])
+    assert np.array_equal(g1["out_tokens"], g2["out_tokens"])
+    compare(b, g1, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
+
+
+def test_workspace_reuse_across_sizes():
+    """One workspace, calls of decreasing size in a row (counters restart each call)."""
+    import torch
+    from rejection_sampling_verify_scaled_amd import binding
+    big = W.make_batch(5, 3, B=96)
+    ws = torch.zeros(binding.workspace_bytes(big.B, big.V, big.max_k), dtype=torch.uint8,
+                     device="cuda")
+    for B in (96, 40, 7, 96):
+        b = W.make_batch(5, 3, B=B)
+        say(f"workspace reuse B={B}")
+        compare(b, run_gpu(b, "sample", workspace=ws), oracle.verify_batch(b))
+
+
+def test_closed_form_on_gpu():
+    """Controlled-alpha rows: mean emitted tokens match (1 - a^(K+1)) / (1 - a)."""
+    import oracle_pins as P
+    rng = np.random.default_rng(77)
+    alpha, K, V, N = 0.8, 4, 64, 20000
+    target, draft, offsets, tokens = P.controlled_alpha_batch(rng, alpha, K, V, N)
+    with np.errstate(invalid="ignore"):
+        tgt32 = np.where(np.isfinite(target), target, -1e30).astype(np.float32)
+        dr32 = np.where(np.isfinite(draft), draft, -1e30).astype(np.float32)
+    b = W.Batch(dtype=W.DTYPE_F32, B=N, V=V, max_k=K, target=tgt32, draft=dr32,
+                offsets=offsets, tokens=tokens, temperature=np.ones(N, np.float32), seed=2024,
+                sigma=np.zeros(N))
+    say("closed form on GPU")
+    gpu = run_gpu(b, "sample")
+    L = gpu["accept_len"].astype(np.float64) + 1
+    pj = np.array([alpha ** j for j in range(K + 1)])
+    se = math.sqrt((sum((2 * j + 1) * pj[j] for j in range(K + 1)) - pj.sum() ** 2) / N)
+    assert abs(L.mean() - P.expected_tokens(alpha, K)) < 4 * se
+    reqs = list(range(0, N, 97))
+    compare(b, gpu, oracle.verify_batch(b, reqs=reqs), reqs=reqs)
