@@ -10,9 +10,9 @@ Infinity Cache.  Prints one JSON line.
 
 Reported:
   value          verified draft positions per second (sum of K_b per step / time)
-  roofline       the row-statistics kernel (all of the HBM traffic): algorithmic
-                 bytes per launch / its mean duration from HIP events recorded on
-                 the launch stream, against 8 TB/s
+  roofline       the single verify kernel: algorithmic bytes per launch / its
+                 mean duration from HIP events recorded on the launch stream,
+                 against 8 TB/s
   cpu_baseline   the float64 oracle on a bounded sample of the same batch
 """
 from __future__ import annotations
@@ -87,7 +87,7 @@ class Hip:
 def traffic_record(workload: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_row_stats_workload{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_sv_verify_workload{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -171,25 +171,18 @@ def main():
     print(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / args.steps * 1e6:.2f} us/step)",
           file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations from events recorded between the two launches
+    # ---- kernel duration from events the library records around its launch
     n_t = min(args.steps, 200)
-    evs = [[hip.event() for _ in range(3)] for _ in range(n_t)]
+    evs = [(hip.event(), hip.event()) for _ in range(n_t)]
     timed = lib.spec_verify_sample_timed
-    timed.argtypes = list(lib.spec_verify_sample.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
-    timed.restype = ctypes.c_int
-    arrs = [(ctypes.c_void_p * 3)(*[e.value for e in trip]) for trip in evs]
     for i in range(n_t):
-        rc = timed(*argsets[i % copies], arrs[i])
+        rc = timed(*argsets[i % copies], evs[i][0], evs[i][1])
         if rc != 0:
             raise SystemExit(f"spec_verify_sample_timed returned {rc}")
     torch.cuda.synchronize()
-    k1 = [hip.elapsed_ms(t[0], t[1]) for t in evs]
-    k2 = [hip.elapsed_ms(t[1], t[2]) for t in evs]
-    k1_us = 1e3 * sum(k1) / n_t
-    k2_us = 1e3 * sum(k2) / n_t
-    achieved = alg / (k1_us * 1e-6) / 1e9
-    print(f"[bench] row_stats {k1_us:.2f} us, accept_race {k2_us:.2f} us", file=sys.stderr,
-          flush=True)
+    k_us = 1e3 * sum(hip.elapsed_ms(a, b) for a, b in evs) / n_t
+    achieved = alg / (k_us * 1e-6) / 1e9
+    print(f"[bench] sv_verify kernel {k_us:.2f} us (events)", file=sys.stderr, flush=True)
 
     # ---- correctness spot check of this exact launch configuration
     call(*argsets[0])
@@ -218,10 +211,10 @@ def main():
         "hbm_frac_step": alg / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg,
         "bytes_per_verified_position": alg / positions,
-        "kernel_us": {"sv_row_stats": k1_us, "sv_accept_race": k2_us},
+        "kernel_us": {"sv_verify": k_us},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(args.workload),
-                     "kernel": "sv_row_stats"},
+                     "kernel": "sv_verify"},
     }
 
     if not args.no_cpu_baseline:

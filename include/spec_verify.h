@@ -41,13 +41,19 @@
  *   Logits are float32 (SV_F32) or bfloat16 bit patterns (SV_BF16).
  *
  * Ownership: the caller owns every buffer, the workspace included.  The library
- * allocates nothing, keeps no state between calls, never synchronises, and only
- * enqueues kernels on `stream` (a hipStream_t; NULL is the default stream).
- * Outputs are valid once the stream reaches the end of the call's work.  Two
+ * allocates nothing, keeps no host state between calls, never synchronises, and
+ * only enqueues one kernel on `stream` (a hipStream_t; NULL is the default
+ * stream).  Outputs are valid once the stream reaches the end of the call's
+ * work.  The workspace carries per-request counters between the kernel's
+ * workgroups: it must be zero-filled once before its first use (hipMemset),
+ * and every call leaves it zero-filled again when it completes, so it can be
+ * reused by later calls of any size up to the one it was sized for.  Two
  * calls that may run concurrently need separate workspaces.
  *
  * Errors: a negative return value means nothing was enqueued (except
- * SV_ERR_LAUNCH, which reports a launch failure).  Per-request problems found
+ * SV_ERR_LAUNCH, which reports a launch failure).  accept_len[b] = -1 with
+ * tokens left unwritten would mean a bounded wait inside the kernel expired
+ * (the device stopped making progress); zero the workspace again after that.  Per-request problems found
  * on the device -- K_b outside [0, max_k], a slice outside [0, n_draft_rows),
  * a draft token outside [0, V), a temperature that is negative, NaN or
  * infinite, a needed row whose maximum is not finite, or a NaN in a row that
@@ -80,7 +86,8 @@ enum sv_status {
 };
 
 /* Host function.  Bytes of device workspace a call with these sizes needs
- * (valid for both dtypes).  Returns 0 for sizes the library rejects. */
+ * (valid for both dtypes; zero-fill it before first use).  Returns 0 for sizes
+ * the library rejects. */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t V, int32_t max_k);
 
 /* All-greedy verify (every request follows the temperature-0 rule of section
@@ -115,19 +122,17 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, int3
                        int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* spec_verify_sample, plus HIP events (hipEvent_t handles created by the
- * caller) recorded on `stream` around the library's two kernels, so a caller
- * can measure each kernel's duration on the stream it runs on:
- *   events[0] before the row-statistics kernel, events[1] between the
- *   row-statistics and accept/race kernels, events[2] after the latter.
- * events must point to 3 valid events.  Same results as spec_verify_sample. */
+/* spec_verify_sample, plus two HIP events (hipEvent_t handles created by the
+ * caller) recorded on `stream` immediately before and after the library's
+ * kernel, so a caller can time the kernel on the stream it runs on.  Both
+ * events must be valid.  Same results as spec_verify_sample. */
 int spec_verify_sample_timed(const void* target_logits, const void* draft_logits, int32_t dtype,
                              int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows,
                              const int32_t* draft_offsets, const int32_t* draft_tokens,
                              const float* temperature, uint64_t seed, int32_t* accept_len,
                              int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
                              void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* events);
+                             void* event_start, void* event_end);
 
 /* Host function.  Static description of a status code. */
 const char* spec_verify_status_string(int status);

@@ -52,6 +52,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_sample.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, u64, vp, vp,
                                        vp, vp, vp, sz, vp]
     lib.spec_verify_sample.restype = ctypes.c_int
+    lib.spec_verify_sample_timed.argtypes = list(lib.spec_verify_sample.argtypes) + [vp, vp]
+    lib.spec_verify_sample_timed.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -69,6 +71,11 @@ def header_functions(header: str = HEADER):
 
 def workspace_bytes(B: int, V: int, max_k: int) -> int:
     return int(load_library().spec_verify_workspace_bytes(B, V, max_k))
+
+
+def new_workspace(B: int, V: int, max_k: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for calls up to these sizes."""
+    return torch.zeros(workspace_bytes(B, V, max_k), dtype=torch.uint8, device=device)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -122,8 +129,8 @@ def _prepare(target, offsets, tokens, max_k, accept_len, out_tokens, workspace):
     _check(accept_len, "accept_len", torch.int32, (B,), device)
     _check(out_tokens, "out_tokens", torch.int32, (n_d + B,), device)
     need = workspace_bytes(B, V, max_k)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:  # zero-filled once; every completed call leaves it zeroed
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     return B, V, n_d, accept_len, out_tokens, workspace

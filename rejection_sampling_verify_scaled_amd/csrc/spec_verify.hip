@@ -1,24 +1,33 @@
-// spec_verify.hip -- gfx950 kernels and C ABI of the speculative-decoding verify step.
+// spec_verify.hip -- gfx950 kernel and C ABI of the speculative-decoding verify step.
 //
 // What is computed is stated in include/spec_verify.h (the accept / residual /
 // bonus rule of "Decodificación Especulativa y EAGLE", section "La Regla de
-// Exactitud", and its greedy case).  How it runs on MI355X:
+// Exactitud", and its greedy case).  How it runs on MI355X: one launch, two
+// kinds of workgroup.
 //
-//   launch 1, sv_row_stats -- one workgroup per (request, row slot, V-chunk).
-//     Streams the chunk with 16-byte loads and reduces it to one 8-byte
-//     partial: (max, sum of 2^((z - max) * log2(e) / T)) for rows a sampled
-//     request needs, (max, lowest argmax index) for rows of a greedy request.
-//     Draft rows of greedy requests are never read.  This launch carries all
-//     of the HBM traffic and is bound by it.
-//   launch 2, sv_accept_race -- one workgroup per (request, race chunk).
-//     Every workgroup of a request folds the partials into per-row (max, lse),
-//     gathers p_t(x_t), q_t(x_t), draws r_t and finds the first rejection n
-//     with a wave ballot (redundantly, so no workgroup waits for another).  It
-//     then runs the exponential race over its chunk of row n: residual
-//     (p_n - q_n)+ after a rejection, bonus p_K otherwise.  The last
-//     workgroup of a request to finish (atomic counter) folds the chunk
-//     winners and writes the request's outputs.  Greedy requests are finished
-//     by their first workgroup from the argmax partials.
+//   row-statistics workgroups, one per (request, row slot, V-chunk), first in
+//     the grid.  Each streams its chunk with 16-byte loads and reduces it to
+//     one 8-byte partial: (max, sum of 2^((z - max) * log2(e) / T)) for rows a
+//     sampled request needs, (max, lowest argmax index) for rows of a greedy
+//     request.  Draft rows of greedy requests are never read.  These carry
+//     all of the HBM traffic.  The last of a request's workgroups to finish
+//     (atomic counter; nobody waits) becomes the request's finisher: it folds
+//     the partials into per-row (max, log2 sum), and
+//       greedy:  finds the first draft that differs from the row argmax and
+//                writes the request's outputs;
+//       sampled: gathers p_t(x_t), q_t(x_t), draws r_t, finds the first
+//                rejection n with a wave ballot, and publishes n with the
+//                statistics of row n.
+//   race workgroups, one per (sampled request, race chunk), last in the grid.
+//     Each waits for its request's publication, runs the exponential race
+//     over its chunk of row n -- residual (p_n - q_n)+ after a rejection,
+//     bonus p_K otherwise -- and the last of them folds the chunk winners
+//     and writes the outputs.
+//
+// Forward progress: a race workgroup only waits for row-statistics
+// workgroups, which have lower indices and never wait, so with in-order
+// dispatch the wait always ends.  The wait is also bounded (kSpinLimit polls);
+// if it ever expired the request would report accept_len = -1.
 //
 // Race keys are kept in base-2 logs: key_v = log2 w_v - log2(-log2 U_v), a
 // strictly increasing function of the natural-log key ln w_v - ln E_v, so the
@@ -33,11 +42,14 @@
 
 namespace {
 
-constexpr int kThreads = 256;                  // 4 wave64s per workgroup
+constexpr int kThreads = 256;  // 4 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kStatsVecs = 8;                  // 16-byte loads per thread per stats chunk
-constexpr int kRaceGroups = 4;                 // 4-token Philox groups per thread per race chunk
+constexpr int kStatsVecs = 8;   // 16-byte loads per thread per statistics chunk
+constexpr int kRaceGroups = 4;  // 4-token Philox groups per thread per race chunk
 constexpr int kRaceChunk = kThreads * kRaceGroups * 4;  // tokens per race chunk
+constexpr int kRowsMax = 2 * SV_KMAX + 1;               // row slots per request
+constexpr int kRowsPerWave = (kRowsMax + kWaves - 1) / kWaves;
+constexpr unsigned kSpinLimit = 1u << 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
@@ -127,16 +139,49 @@ __device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
   }
 }
 
+// All threads end with the workgroup's (key, idx) winner.
+__device__ __forceinline__ void block_argmax(float& key, int& idx, float* sh_k, int* sh_i) {
+  wave_merge_argmax(key, idx);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    sh_k[wave] = key;
+    sh_i[wave] = idx;
+  }
+  __syncthreads();
+  key = sh_k[0];
+  idx = sh_i[0];
+  for (int w = 1; w < kWaves; ++w) merge_argmax(key, idx, sh_k[w], sh_i[w]);
+}
+
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// ------------------------------------------------------------------ workspace
+
+enum : int32_t { kStatusOk = 0, kStatusFault = 1 };
+
+// What a sampled request's finisher publishes for its race workgroups.
+struct Published {
+  int32_t n;       // first rejected position (K when every draft passed)
+  int32_t status;  // kStatusOk / kStatusFault
+  float mp, lsp;   // target row n: max and log2 of its scaled sum
+  float mq, lsq;   // draft row n (residual race only)
+  float cf;        // log2(e) / T
+  int32_t pad;
+};
+
 struct Layout {
-  int J;        // row slots per request: target 0..max_k, then draft 0..max_k-1
-  int nc1;      // stats chunks per row
-  int nc2;      // race chunks per row
-  size_t stats_off, race_off, count_off, total;
+  int J;    // row slots per request: target 0..max_k, then draft 0..max_k-1
+  int nc1;  // statistics chunks per row
+  int nc2;  // race chunks per row
+  size_t stats_off, race_off, pub_off, count_off, total;
 };
 
 __host__ __device__ inline int ceil_div(int64_t a, int64_t b) {
   return static_cast<int>((a + b - 1) / b);
 }
+
+inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 Layout make_layout(int32_t B, int32_t V, int32_t max_k, bool bf16) {
   Layout L;
@@ -144,63 +189,240 @@ Layout make_layout(int32_t B, int32_t V, int32_t max_k, bool bf16) {
   L.nc1 = ceil_div(V, stats_chunk(bf16));
   L.nc2 = ceil_div(V, kRaceChunk);
   L.stats_off = 0;
-  const size_t stats_bytes = static_cast<size_t>(B) * L.J * ceil_div(V, stats_chunk(false)) * 8;
-  L.race_off = (stats_bytes + 255) / 256 * 256;
-  const size_t race_bytes = static_cast<size_t>(B) * L.nc2 * 8;
-  L.count_off = L.race_off + (race_bytes + 255) / 256 * 256;
-  L.total = L.count_off + (static_cast<size_t>(B) * 4 + 255) / 256 * 256;
+  const size_t stats_bytes =
+      static_cast<size_t>(B) * L.J * ceil_div(V, stats_chunk(false)) * sizeof(float2);
+  L.race_off = round256(stats_bytes);
+  L.pub_off = L.race_off + round256(static_cast<size_t>(B) * L.nc2 * sizeof(float2));
+  L.count_off = L.pub_off + round256(static_cast<size_t>(B) * sizeof(Published));
+  L.total = L.count_off + round256(static_cast<size_t>(B) * 3 * sizeof(uint32_t));
   return L;
 }
 
-// ------------------------------------------------------------------ launch 1
+struct Params {
+  const void* target;
+  const void* draft;
+  const int32_t* offsets;
+  const int32_t* tokens;
+  const float* temperature;  // NULL: every request greedy
+  uint32_t k0, k1;           // Philox key
+  int32_t B, V, max_k, n_draft_rows, nc1, nc2;
+  int64_t n_stats_slots;
+  float2* part;          // [B][J][nc1] row-statistics partials
+  float2* race_part;     // [B][nc2] race chunk winners (key, index bits)
+  Published* pub;        // [B]
+  uint32_t* done;        // [B] finished row-statistics workgroups
+  uint32_t* ready;       // [B] finisher has published
+  uint32_t* race_done;   // [B] finished race workgroups
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* p_at;
+  float* q_at;
+};
+
+// Per-request checks every workgroup can make from the request's scalars.
+struct Req {
+  int32_t off0, K;
+  float T;
+  bool slice_ok, temp_ok, greedy;
+};
+
+__device__ __forceinline__ Req load_req(const Params& p, int b) {
+  Req r;
+  r.off0 = p.offsets[b];
+  const int32_t off1 = p.offsets[b + 1];
+  r.K = off1 - r.off0;
+  r.slice_ok = r.off0 >= 0 && off1 <= p.n_draft_rows && r.K >= 0 && r.K <= p.max_k;
+  r.T = p.temperature ? p.temperature[b] : 0.f;
+  r.greedy = r.T == 0.f;
+  r.temp_ok = (r.T >= 0.f) && (r.T < INFINITY) && (r.greedy || r.K == 0 || p.draft != nullptr);
+  return r;
+}
+
+// Outputs of a failed request (its slice is valid).
+__device__ void write_fault(const Params& p, int b, const Req& r) {
+  const int tid = threadIdx.x;
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  if (tid <= r.K) p.out_tokens[trow0 + tid] = -1;
+  if (tid < r.K) {
+    if (p.p_at) p.p_at[r.off0 + tid] = NAN;
+    if (p.q_at) p.q_at[r.off0 + tid] = NAN;
+  }
+  if (tid == 0) p.accept_len[b] = -1;
+}
+
+// ------------------------------------------------------------------ finisher
+
+template <bool BF16>
+__device__ void finish_request(const Params& p, int b, const Req& r) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = r.K;
+  const int J = 2 * p.max_k + 1;
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  const int64_t drow0 = r.off0;
+  const bool greedy = r.greedy;
+  const float cf = greedy ? 0.f : kLog2e / r.T;
+  const int nrows = greedy ? K + 1 : 2 * K + 1;  // rows 0..K target, K+1..2K draft 0..K-1
+
+  __shared__ int sh_bad;
+  __shared__ float sh_m[kRowsMax];
+  __shared__ float sh_ls[kRowsMax];  // greedy: argmax index bits
+  __shared__ int sh_n;
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  int32_t x = 0;
+  if (tid < K) {
+    x = p.tokens[r.off0 + tid];
+    if (x < 0 || x >= p.V) atomicOr(&sh_bad, 1);
+  }
+
+  // fold the partials: wave w takes rows w, w+4, ...; lanes take chunks
+  float a[kRowsPerWave], s[kRowsPerWave];
+  int ia[kRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    a[i] = -INFINITY;
+    s[i] = 0.f;
+    ia[i] = INT_MAX;
+  }
+  for (int c0 = 0; c0 < p.nc1; c0 += 64) {
+    const int c = c0 + lane;
+    float2 v[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int row = wave + i * kWaves;
+      v[i] = make_float2(-INFINITY, 0.f);
+      if (row < nrows && c < p.nc1) {
+        const int j = (row <= K) ? row : p.max_k + 1 + (row - K - 1);
+        v[i] = p.part[(static_cast<int64_t>(b) * J + j) * p.nc1 + c];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if (greedy) {
+        if (v[i].x > -INFINITY) merge_argmax(a[i], ia[i], v[i].x, __float_as_int(v[i].y));
+      } else {
+        merge_stats(a[i], s[i], v[i].x, v[i].y, cf);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int row = wave + i * kWaves;
+    if (greedy)
+      wave_merge_argmax(a[i], ia[i]);
+    else
+      wave_merge_stats(a[i], s[i], cf);
+    if (lane == 0 && row < nrows) {
+      const bool finite_max = a[i] > -INFINITY && a[i] < INFINITY;
+      if (greedy) {
+        if (!finite_max) atomicOr(&sh_bad, 1);
+        sh_ls[row] = __int_as_float(ia[i]);
+      } else {
+        if (!finite_max || !(s[i] < INFINITY)) atomicOr(&sh_bad, 1);
+        sh_m[row] = a[i];
+        sh_ls[row] = fast_log2(s[i]);
+      }
+    }
+  }
+  __syncthreads();
+
+  if (sh_bad) {
+    write_fault(p, b, r);
+    if (tid == 0) {
+      if (!greedy) {
+        p.pub[b].status = kStatusFault;
+        __hip_atomic_store(&p.ready[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      p.done[b] = 0u;
+    }
+    return;
+  }
+
+  if (greedy) {
+    // first t < K whose draft differs from the argmax; the stop token is argmax row n
+    const bool mismatch = tid < K && __float_as_int(sh_ls[tid]) != x;
+    const uint64_t mask = __ballot(mismatch);
+    if (tid == 0) sh_n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
+    __syncthreads();
+    const int n = sh_n;
+    if (tid <= K) {
+      const int32_t y = __float_as_int(sh_ls[n]);
+      p.out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? y : -1);
+    }
+    if (tid < K) {
+      if (p.p_at) p.p_at[drow0 + tid] = NAN;
+      if (p.q_at) p.q_at[drow0 + tid] = NAN;
+    }
+    if (tid == 0) {
+      p.accept_len[b] = n;
+      p.done[b] = 0u;
+    }
+    return;
+  }
+
+  // ratio test r_t * q_t(x_t) < p_t(x_t), left to right (wave 0 holds t < K <= 8)
+  bool reject = false;
+  if (tid < K) {
+    const float zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
+    const float zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
+    const float pp = fast_exp2((zp - sh_m[tid]) * cf - sh_ls[tid]);
+    const float qq = fast_exp2((zq - sh_m[K + 1 + tid]) * cf - sh_ls[K + 1 + tid]);
+    const float u = uniform_open01(philox4x32_10(0u, tid, b, 1u, p.k0, p.k1).w[0]);
+    reject = !(u * qq < pp);
+    if (p.p_at) p.p_at[drow0 + tid] = pp;
+    if (p.q_at) p.q_at[drow0 + tid] = qq;
+  }
+  const uint64_t mask = __ballot(reject);
+  if (tid == 0) {
+    const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
+    Published& pub = p.pub[b];
+    pub.n = n;
+    pub.status = kStatusOk;
+    pub.mp = sh_m[n];
+    pub.lsp = sh_ls[n];
+    pub.mq = n < K ? sh_m[K + 1 + n] : 0.f;
+    pub.lsq = n < K ? sh_ls[K + 1 + n] : 0.f;
+    pub.cf = cf;
+    p.done[b] = 0u;
+    __hip_atomic_store(&p.ready[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ------------------------------------------------------------------ row statistics
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void sv_row_stats(
-    const void* __restrict__ target, const void* __restrict__ draft,
-    const int32_t* __restrict__ offsets, const float* __restrict__ temperature, int32_t B,
-    int32_t V, int32_t max_k, int32_t n_draft_rows, int32_t nc1, float2* __restrict__ part,
-    uint32_t* __restrict__ counters) {
+__device__ void stats_slot(const Params& p, int64_t bid) {
   constexpr int EPV = elems_per_vec(BF16);
   constexpr int CHUNK = stats_chunk(BF16);
-  const int J = 2 * max_k + 1;
-  const int64_t bid = blockIdx.x;
-  const int c = static_cast<int>(bid % nc1);
-  const int j = static_cast<int>((bid / nc1) % J);
-  const int b = static_cast<int>(bid / (static_cast<int64_t>(nc1) * J));
-  const int tid = threadIdx.x;
+  const int J = 2 * p.max_k + 1;
+  const int c = static_cast<int>(bid % p.nc1);
+  const int j = static_cast<int>((bid / p.nc1) % J);
+  const int b = static_cast<int>(bid / (static_cast<int64_t>(p.nc1) * J));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // launch 2 counts finished race chunks per request from zero
-  if (bid == 0)
-    for (int i = tid; i < B; i += kThreads) counters[i] = 0u;
-
-  const int32_t off0 = offsets[b];
-  const int32_t off1 = offsets[b + 1];
-  const int32_t K = off1 - off0;
-  if (off0 < 0 || off1 > n_draft_rows || K < 0 || K > max_k) return;
-  const float T = temperature ? temperature[b] : 0.f;
-  if (!(T >= 0.f) || !(T < INFINITY)) return;  // launch 2 reports the failure
-  const bool greedy = (T == 0.f);
+  const Req r = load_req(p, b);
+  if (!r.slice_ok || !r.temp_ok) return;  // reported by the request's race workgroup 0
   const void* base;
   int64_t row;
-  if (j <= max_k) {
-    if (j > K) return;
-    base = target;
-    row = static_cast<int64_t>(off0) + b + j;
+  if (j <= p.max_k) {
+    if (j > r.K) return;
+    base = p.target;
+    row = static_cast<int64_t>(r.off0) + b + j;
   } else {
-    const int t = j - max_k - 1;
-    if (greedy || t >= K || draft == nullptr) return;
-    base = draft;
-    row = static_cast<int64_t>(off0) + t;
+    const int t = j - p.max_k - 1;
+    if (r.greedy || t >= r.K) return;
+    base = p.draft;
+    row = static_cast<int64_t>(r.off0) + t;
   }
 
   const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
-  const int64_t e_end = (e0 + CHUNK < V) ? e0 + CHUNK : V;
+  const int64_t e_end = (e0 + CHUNK < p.V) ? e0 + CHUNK : p.V;
 
-  // gather this thread's elements in increasing index order
+  // this thread's elements, in increasing index order
   float x[kStatsVecs * EPV];
   if constexpr (VEC) {
     const uint4* rowv = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(base) + row * static_cast<int64_t>(V) * (BF16 ? 2 : 4));
+        static_cast<const char*>(base) + row * static_cast<int64_t>(p.V) * (BF16 ? 2 : 4));
     uint4 buf[kStatsVecs];
 #pragma unroll
     for (int u = 0; u < kStatsVecs; ++u) {
@@ -227,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void sv_row_stats(
       }
     }
   } else {
-    const int64_t rbase = row * static_cast<int64_t>(V);
+    const int64_t rbase = row * static_cast<int64_t>(p.V);
 #pragma unroll
     for (int u = 0; u < kStatsVecs; ++u) {
 #pragma unroll
@@ -240,11 +462,8 @@ __global__ __launch_bounds__(kThreads) void sv_row_stats(
 
   __shared__ float sh_a[kWaves];
   __shared__ float sh_b[kWaves];
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   float2 result;
-
-  if (greedy) {
+  if (r.greedy) {
     float best = -INFINITY;
     int idx = INT_MAX;
 #pragma unroll
@@ -269,28 +488,24 @@ __global__ __launch_bounds__(kThreads) void sv_row_stats(
       result = make_float2(best, __int_as_float(idx));
     }
   } else {
-    const float cf = kLog2e / T;
+    const float cf = kLog2e / r.T;
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kStatsVecs * EPV; ++i) m = fmaxf(m, x[i]);
-    const float ms = (m == -INFINITY) ? 0.f : m;  // keeps NaN visible when no finite max
+    const float ms = (m == -INFINITY) ? 0.f : m;  // keeps a NaN visible when no finite max
     float acc[kStatsVecs];
 #pragma unroll
     for (int u = 0; u < kStatsVecs; ++u) {
-      float a = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) a += fast_exp2((x[u * EPV + k] - ms) * cf);
-      acc[u] = a;
+      for (int k = 0; k < EPV; ++k) sum += fast_exp2((x[u * EPV + k] - ms) * cf);
+      acc[u] = sum;
     }
 #pragma unroll
     for (int h = kStatsVecs / 2; h >= 1; h >>= 1)
 #pragma unroll
       for (int u = 0; u < h; ++u) acc[u] += acc[u + h];
     float s = acc[0];
-    if (m == -INFINITY) {
-      // all of this thread's elements are -inf or NaN: s is 0 or NaN already
-      m = -INFINITY;
-    }
     wave_merge_stats(m, s, cf);
     if (lane == 0) {
       sh_a[wave] = m;
@@ -302,10 +517,22 @@ __global__ __launch_bounds__(kThreads) void sv_row_stats(
       result = make_float2(m, s);
     }
   }
-  if (tid == 0) part[(static_cast<int64_t>(b) * J + j) * nc1 + c] = result;
+
+  __shared__ int sh_last;
+  if (tid == 0) {
+    p.part[(static_cast<int64_t>(b) * J + j) * p.nc1 + c] = result;
+    const uint32_t need = static_cast<uint32_t>((r.greedy ? r.K + 1 : 2 * r.K + 1) * p.nc1);
+    const uint32_t before =
+        __hip_atomic_fetch_add(&p.done[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = (before + 1 == need) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  acquire_agent();
+  finish_request<BF16>(p, b, r);
 }
 
-// ------------------------------------------------------------------ launch 2
+// ------------------------------------------------------------------ race
 
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend, float out[4]) {
@@ -329,229 +556,157 @@ __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend,
   }
 }
 
-// Race over tokens [v_begin, v_end) of one row.  residual: w_v = p_v - q_v
-// (tokens with w_v <= 0 are out); otherwise log2 w_v = (z_v - mp) * cf.
-template <bool BF16, bool VEC>
-__device__ void race_span(const void* prow, const void* qrow, bool residual, float mp, float lsp,
-                          float mq, float lsq, float cf, int64_t v_begin, int64_t v_end,
-                          uint32_t pos, uint32_t b, uint32_t k0, uint32_t k1, float& best_key,
-                          int& best_idx) {
-  for (int64_t g = v_begin / 4 + threadIdx.x; g * 4 < v_end; g += kThreads) {
-    const int64_t v = g * 4;
-    float zp[4], zq[4];
-    load4<BF16, VEC>(prow, v, v_end, zp);
-    if (residual) load4<BF16, VEC>(qrow, v, v_end, zq);
-    const Philox4 r = philox4x32_10(static_cast<uint32_t>(g), pos, b, 0u, k0, k1);
+// Race keys of tokens 4g..4g+3 folded into (best_key, best_idx); tokens are
+// visited in increasing order, so a strict > keeps the lowest index on ties.
+__device__ __forceinline__ void race_group(const float zp[4], const float zq[4], bool residual,
+                                           const Published& pub, int64_t g, int64_t v_end,
+                                           uint32_t b, uint32_t k0, uint32_t k1,
+                                           float& best_key, int& best_idx) {
+  const Philox4 r = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(pub.n), b, 0u,
+                                  k0, k1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (v + k >= v_end) break;
-      const float e2 = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
-      float lw;
-      if (residual) {
-        const float p = fast_exp2((zp[k] - mp) * cf - lsp);
-        const float q = fast_exp2((zq[k] - mq) * cf - lsq);
-        const float w = p - q;
-        if (!(w > 0.f)) continue;
-        lw = fast_log2(w);
-      } else {
-        lw = (zp[k] - mp) * cf;
-      }
-      const float key = lw - fast_log2(e2);
-      if (key > best_key) {
-        best_key = key;
-        best_idx = static_cast<int>(v + k);
-      }
+  for (int k = 0; k < 4; ++k) {
+    const int64_t v = g * 4 + k;
+    if (v >= v_end) break;
+    const float e2 = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
+    float lw;
+    if (residual) {
+      const float pv = fast_exp2((zp[k] - pub.mp) * pub.cf - pub.lsp);
+      const float qv = fast_exp2((zq[k] - pub.mq) * pub.cf - pub.lsq);
+      const float w = pv - qv;
+      if (!(w > 0.f)) continue;
+      lw = fast_log2(w);
+    } else {
+      lw = (zp[k] - pub.mp) * pub.cf;
+    }
+    const float key = lw - fast_log2(e2);
+    if (key > best_key) {
+      best_key = key;
+      best_idx = static_cast<int>(v);
     }
   }
 }
 
-__device__ __forceinline__ void block_argmax(float& key, int& idx, float* sh_k, int* sh_i) {
-  wave_merge_argmax(key, idx);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) {
-    sh_k[wave] = key;
-    sh_i[wave] = idx;
-  }
-  __syncthreads();
-  key = sh_k[0];
-  idx = sh_i[0];
-  for (int w = 1; w < kWaves; ++w) merge_argmax(key, idx, sh_k[w], sh_i[w]);
-}
-
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void sv_accept_race(
-    const void* __restrict__ target, const void* __restrict__ draft,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tokens,
-    const float* __restrict__ temperature, uint32_t k0, uint32_t k1, int32_t V, int32_t max_k,
-    int32_t n_draft_rows, int32_t nc1, int32_t nc2, const float2* __restrict__ part,
-    float2* __restrict__ race_part, uint32_t* __restrict__ counters,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ p_at, float* __restrict__ q_at) {
-  const int b = blockIdx.x / nc2;
-  const int c = blockIdx.x % nc2;
+__device__ void race_slot(const Params& p, int64_t rid) {
+  const int b = static_cast<int>(rid / p.nc2);
+  const int c = static_cast<int>(rid % p.nc2);
   const int tid = threadIdx.x;
-  const int J = 2 * max_k + 1;
-
-  const int32_t off0 = offsets[b];
-  const int32_t off1 = offsets[b + 1];
-  const int32_t K = off1 - off0;
-  if (off0 < 0 || off1 > n_draft_rows || K < 0 || K > max_k) {
-    if (c == 0 && tid == 0) accept_len[b] = -1;
+  const Req r = load_req(p, b);
+  if (!r.slice_ok) {
+    if (c == 0 && tid == 0) p.accept_len[b] = -1;
     return;
   }
-  const float T = temperature ? temperature[b] : 0.f;
-  const bool greedy = (T == 0.f);
-  if (greedy && c != 0) return;
-  const int64_t trow0 = static_cast<int64_t>(off0) + b;  // target row t: trow0 + t
-  const int64_t drow0 = off0;                            // draft row t: drow0 + t
+  if (!r.temp_ok) {
+    if (c == 0) write_fault(p, b, r);
+    return;
+  }
+  if (r.greedy) return;  // finished by its row-statistics finisher
 
-  __shared__ int sh_bad;
-  __shared__ float sh_m[2 * SV_KMAX + 1];
-  __shared__ float sh_ls[2 * SV_KMAX + 1];  // log2 of the row's scaled sum; greedy: argmax
-  __shared__ int sh_n;
+  __shared__ int sh_flag;
+  if (tid == 0) {
+    unsigned it = 0;
+    while (__hip_atomic_load(&p.ready[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (++it > kSpinLimit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    sh_flag = (it > kSpinLimit) ? 1 : 0;
+  }
+  __syncthreads();
+  if (sh_flag) {
+    if (c == 0 && tid == 0) p.accept_len[b] = -1;
+    return;
+  }
+  acquire_agent();
+  const Published pub = p.pub[b];
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  const int64_t drow0 = r.off0;
+  const int64_t esz = BF16 ? 2 : 4;
+  const void* prow = static_cast<const char*>(p.target) + (trow0 + pub.n) * p.V * esz;
+  const bool residual = pub.n < r.K;
+  const void* qrow =
+      residual ? static_cast<const char*>(p.draft) + (drow0 + pub.n) * p.V * esz : nullptr;
+
   __shared__ float sh_key[kWaves];
   __shared__ int sh_idx[kWaves];
-  __shared__ int sh_last;
-
-  if (tid == 0)
-    sh_bad = (!(T >= 0.f) || !(T < INFINITY) || (!greedy && K > 0 && draft == nullptr)) ? 1 : 0;
-  __syncthreads();
-  const float cf = greedy ? 0.f : kLog2e / T;
-  if (tid < K) {
-    const int32_t x = tokens[off0 + tid];
-    if (x < 0 || x >= V) atomicOr(&sh_bad, 1);
-  }
-  const int nrows = greedy ? K + 1 : 2 * K + 1;
-  if (tid < nrows) {  // reads stay inside request b's partials even for a bad request
-    // rows 0..K are target rows, rows K+1..2K draft rows 0..K-1
-    const int j = (tid <= K) ? tid : (max_k + 1 + tid - K - 1);
-    const float2* pp = part + (static_cast<int64_t>(b) * J + j) * nc1;
-    if (greedy) {
-      float best = -INFINITY;
-      int idx = INT_MAX;
-      for (int i = 0; i < nc1; ++i) {
-        const float2 r = pp[i];
-        merge_argmax(best, idx, r.x, __float_as_int(r.y));
-      }
-      if (!(best > -INFINITY && best < INFINITY)) atomicOr(&sh_bad, 1);
-      sh_ls[tid] = __int_as_float(idx);
-    } else {
-      float m = -INFINITY, s = 0.f;
-      for (int i = 0; i < nc1; ++i) {
-        const float2 r = pp[i];
-        merge_stats(m, s, r.x, r.y, cf);
-      }
-      if (!(m > -INFINITY && m < INFINITY) || !(s < INFINITY)) atomicOr(&sh_bad, 1);
-      sh_m[tid] = m;
-      sh_ls[tid] = fast_log2(s);
-    }
-  }
-  __syncthreads();
-
-  if (sh_bad) {
-    if (c == 0) {
-      if (tid <= K) out_tokens[trow0 + tid] = -1;
-      if (tid < K) {
-        if (p_at) p_at[drow0 + tid] = NAN;
-        if (q_at) q_at[drow0 + tid] = NAN;
-      }
-      if (tid == 0) accept_len[b] = -1;
-    }
-    return;
-  }
-
-  if (greedy) {
-    // first t < K whose draft differs from the argmax; stop token argmax row n
-    bool mismatch = false;
-    int32_t x = 0;
-    if (tid < K) {
-      x = tokens[off0 + tid];
-      mismatch = (__float_as_int(sh_ls[tid]) != x);
-    }
-    const uint64_t mask = __ballot(mismatch);
-    if (tid < 64 && tid == 0) sh_n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
-    __syncthreads();
-    const int n = sh_n;
-    if (tid <= K) {
-      const int32_t y = __float_as_int(sh_ls[n]);
-      out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? y : -1);
-    }
-    if (tid < K) {
-      if (p_at) p_at[drow0 + tid] = NAN;
-      if (q_at) q_at[drow0 + tid] = NAN;
-    }
-    if (tid == 0) accept_len[b] = n;
-    return;
-  }
-
-  // ratio test r_t * q_t(x_t) < p_t(x_t), left to right (wave 0 holds t < K <= 8)
-  bool reject = false;
-  int32_t x = 0;
-  if (tid < K) {
-    x = tokens[off0 + tid];
-    const float zp = load_logit<BF16>(target, (trow0 + tid) * V + x);
-    const float zq = load_logit<BF16>(draft, (drow0 + tid) * V + x);
-    const float p = fast_exp2((zp - sh_m[tid]) * cf - sh_ls[tid]);
-    const float q = fast_exp2((zq - sh_m[K + 1 + tid]) * cf - sh_ls[K + 1 + tid]);
-    const float r = uniform_open01(philox4x32_10(0u, tid, b, 1u, k0, k1).w[0]);
-    reject = !(r * q < p);
-    if (c == 0) {
-      if (p_at) p_at[drow0 + tid] = p;
-      if (q_at) q_at[drow0 + tid] = q;
-    }
-  }
-  const uint64_t mask = __ballot(reject);
-  if (tid == 0) sh_n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
-  __syncthreads();
-  const int n = sh_n;
-  const bool residual = n < K;
-
-  const void* prow = static_cast<const char*>(target) + (trow0 + n) * V * (BF16 ? 2 : 4);
-  const void* qrow =
-      residual ? static_cast<const char*>(draft) + (drow0 + n) * V * (BF16 ? 2 : 4) : nullptr;
-  const float mp = sh_m[n], lsp = sh_ls[n];
-  const float mq = residual ? sh_m[K + 1 + n] : 0.f;
-  const float lsq = residual ? sh_ls[K + 1 + n] : 0.f;
-
   float key = -INFINITY;
   int idx = INT_MAX;
-  const int64_t v_begin = static_cast<int64_t>(c) * kRaceChunk;
-  const int64_t v_end = (v_begin + kRaceChunk < V) ? v_begin + kRaceChunk : V;
-  race_span<BF16, VEC>(prow, qrow, residual, mp, lsp, mq, lsq, cf, v_begin, v_end, n, b, k0, k1,
-                       key, idx);
-  block_argmax(key, idx, sh_key, sh_idx);
+  if (pub.status == kStatusOk) {
+    const int64_t v_begin = static_cast<int64_t>(c) * kRaceChunk;
+    const int64_t v_end = (v_begin + kRaceChunk < p.V) ? v_begin + kRaceChunk : p.V;
+    float zp[kRaceGroups][4], zq[kRaceGroups][4];
+#pragma unroll
+    for (int gi = 0; gi < kRaceGroups; ++gi) {  // issue every load before any math
+      const int64_t g = v_begin / 4 + gi * kThreads + tid;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) zq[gi][k] = 0.f;
+      if (g * 4 < v_end) {
+        load4<BF16, VEC>(prow, g * 4, v_end, zp[gi]);
+        if (residual) load4<BF16, VEC>(qrow, g * 4, v_end, zq[gi]);
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < kRaceGroups; ++gi) {
+      const int64_t g = v_begin / 4 + gi * kThreads + tid;
+      if (g * 4 < v_end)
+        race_group(zp[gi], zq[gi], residual, pub, g, v_end, b, p.k0, p.k1, key, idx);
+    }
+    block_argmax(key, idx, sh_key, sh_idx);
+  }
 
+  __shared__ int sh_last;
   if (tid == 0) {
-    race_part[static_cast<int64_t>(b) * nc2 + c] = make_float2(key, __int_as_float(idx));
-    const uint32_t done = __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (done == static_cast<uint32_t>(nc2 - 1)) ? 1 : 0;
+    if (pub.status == kStatusOk)
+      p.race_part[static_cast<int64_t>(b) * p.nc2 + c] = make_float2(key, __int_as_float(idx));
+    const uint32_t before =
+        __hip_atomic_fetch_add(&p.race_done[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = (before + 1 == static_cast<uint32_t>(p.nc2)) ? 1 : 0;
   }
   __syncthreads();
   if (!sh_last) return;
-  __threadfence();
+  acquire_agent();
 
-  // last workgroup of request b: fold the chunk winners
-  key = -INFINITY;
-  idx = INT_MAX;
-  for (int i = tid; i < nc2; i += kThreads) {
-    const float2 r = race_part[static_cast<int64_t>(b) * nc2 + i];
-    merge_argmax(key, idx, r.x, __float_as_int(r.y));
-  }
-  block_argmax(key, idx, sh_key, sh_idx);
-  if (idx == INT_MAX) {
-    // no token had p > q (rounding can only cause this when p == q): race on p_n
+  if (pub.status == kStatusOk) {
     key = -INFINITY;
-    race_span<BF16, VEC>(prow, nullptr, false, mp, lsp, 0.f, 0.f, cf, 0, V, n, b, k0, k1, key,
-                         idx);
+    idx = INT_MAX;
+    for (int i = tid; i < p.nc2; i += kThreads) {
+      const float2 w = p.race_part[static_cast<int64_t>(b) * p.nc2 + i];
+      merge_argmax(key, idx, w.x, __float_as_int(w.y));
+    }
     block_argmax(key, idx, sh_key, sh_idx);
+    if (idx == INT_MAX) {
+      // no token had p > q (rounding can only cause this when p == q): race on p_n
+      key = -INFINITY;
+      for (int64_t g = tid; g * 4 < p.V; g += kThreads) {
+        float zp[4];
+        const float zq[4] = {0.f, 0.f, 0.f, 0.f};
+        load4<BF16, VEC>(prow, g * 4, p.V, zp);
+        race_group(zp, zq, false, pub, g, p.V, b, p.k0, p.k1, key, idx);
+      }
+      block_argmax(key, idx, sh_key, sh_idx);
+    }
+    const int n = pub.n;
+    if (tid <= r.K) {
+      const int32_t xt = (tid < n) ? p.tokens[r.off0 + tid] : 0;
+      p.out_tokens[trow0 + tid] = (tid < n) ? xt : (tid == n ? idx : -1);
+    }
+    if (tid == 0) p.accept_len[b] = n;
   }
-  if (tid <= K) out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? idx : -1);
   if (tid == 0) {
-    accept_len[b] = n;
-    counters[b] = 0u;
+    p.ready[b] = 0u;
+    p.race_done[b] = 0u;
   }
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
+  const int64_t bid = blockIdx.x;
+  if (bid < p.n_stats_slots)
+    stats_slot<BF16, VEC>(p, bid);
+  else
+    race_slot<BF16, VEC>(p, bid - p.n_stats_slots);
 }
 
 // ------------------------------------------------------------------ host side
@@ -563,35 +718,13 @@ bool shape_ok(int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <bool BF16, bool VEC>
-int launch_all(const void* target, const void* draft, int32_t B, int32_t V, int32_t max_k,
-               int32_t n_draft_rows, const int32_t* offsets, const int32_t* tokens,
-               const float* temperature, uint64_t seed, int32_t* accept_len,
-               int32_t* out_tokens, float* p_at, float* q_at, void* workspace,
-               hipStream_t stream, bool all_greedy, void* const* events) {
-  const Layout L = make_layout(B, V, max_k, BF16);
-  char* ws = static_cast<char*>(workspace);
-  float2* part = reinterpret_cast<float2*>(ws + L.stats_off);
-  float2* race_part = reinterpret_cast<float2*>(ws + L.race_off);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.count_off);
-  const int64_t grid1 = static_cast<int64_t>(B) * L.J * L.nc1;
-  const int nc2 = all_greedy ? 1 : L.nc2;
-  const int64_t grid2 = static_cast<int64_t>(B) * nc2;
-  if (grid1 > INT32_MAX || grid2 > INT32_MAX) return SV_ERR_SHAPE;
-  if (events && hipEventRecord(static_cast<hipEvent_t>(events[0]), stream) != hipSuccess)
+int launch(const Params& prm, int64_t grid, hipStream_t stream, void* ev0, void* ev1) {
+  if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), stream) != hipSuccess)
     return SV_ERR_LAUNCH;
-  hipLaunchKernelGGL((sv_row_stats<BF16, VEC>), dim3(static_cast<uint32_t>(grid1)),
-                     dim3(kThreads), 0, stream, target, draft, offsets, temperature, B, V, max_k,
-                     n_draft_rows, L.nc1, part, counters);
+  hipLaunchKernelGGL((sv_verify<BF16, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
+                     0, stream, prm);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-  if (events && hipEventRecord(static_cast<hipEvent_t>(events[1]), stream) != hipSuccess)
-    return SV_ERR_LAUNCH;
-  hipLaunchKernelGGL((sv_accept_race<BF16, VEC>), dim3(static_cast<uint32_t>(grid2)),
-                     dim3(kThreads), 0, stream, target, draft, offsets, tokens, temperature,
-                     static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), V, max_k,
-                     n_draft_rows, L.nc1, nc2, part, race_part, counters, accept_len, out_tokens,
-                     p_at, q_at);
-  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-  if (events && hipEventRecord(static_cast<hipEvent_t>(events[2]), stream) != hipSuccess)
+  if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), stream) != hipSuccess)
     return SV_ERR_LAUNCH;
   return SV_OK;
 }
@@ -600,7 +733,7 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
              int32_t max_k, int32_t n_draft_rows, const int32_t* offsets, const int32_t* tokens,
              const float* temperature, uint64_t seed, int32_t* accept_len, int32_t* out_tokens,
              float* p_at, float* q_at, void* workspace, size_t workspace_bytes, void* stream,
-             bool all_greedy, void* const* events) {
+             bool all_greedy, void* ev0, void* ev1) {
   if (!target || !offsets || !accept_len || !out_tokens || !workspace) return SV_ERR_NULL;
   if (!all_greedy && (!temperature || (n_draft_rows > 0 && !draft))) return SV_ERR_NULL;
   if (n_draft_rows > 0 && !tokens) return SV_ERR_NULL;
@@ -609,23 +742,43 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   if (workspace_bytes < spec_verify_workspace_bytes(B, V, max_k) || !aligned16(workspace))
     return SV_ERR_WORKSPACE;
   const bool bf16 = dtype == SV_BF16;
+  const Layout L = make_layout(B, V, max_k, bf16);
+  char* ws = static_cast<char*>(workspace);
+  Params prm;
+  prm.target = target;
+  prm.draft = all_greedy ? nullptr : draft;
+  prm.offsets = offsets;
+  prm.tokens = tokens;
+  prm.temperature = all_greedy ? nullptr : temperature;
+  prm.k0 = static_cast<uint32_t>(seed);
+  prm.k1 = static_cast<uint32_t>(seed >> 32);
+  prm.B = B;
+  prm.V = V;
+  prm.max_k = max_k;
+  prm.n_draft_rows = n_draft_rows;
+  prm.nc1 = L.nc1;
+  prm.nc2 = L.nc2;
+  prm.n_stats_slots = static_cast<int64_t>(B) * L.J * L.nc1;
+  prm.part = reinterpret_cast<float2*>(ws + L.stats_off);
+  prm.race_part = reinterpret_cast<float2*>(ws + L.race_off);
+  prm.pub = reinterpret_cast<Published*>(ws + L.pub_off);
+  prm.done = reinterpret_cast<uint32_t*>(ws + L.count_off);
+  prm.ready = prm.done + B;
+  prm.race_done = prm.done + 2 * static_cast<int64_t>(B);
+  prm.accept_len = accept_len;
+  prm.out_tokens = out_tokens;
+  prm.p_at = p_at;
+  prm.q_at = q_at;
+  const int64_t grid = prm.n_stats_slots + (all_greedy ? 0 : static_cast<int64_t>(B) * L.nc2);
+  if (grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 && aligned16(target) && (!draft || aligned16(draft));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (bf16) {
-    return vec ? launch_all<true, true>(target, draft, B, V, max_k, n_draft_rows, offsets, tokens,
-                                        temperature, seed, accept_len, out_tokens, p_at, q_at,
-                                        workspace, s, all_greedy, events)
-               : launch_all<true, false>(target, draft, B, V, max_k, n_draft_rows, offsets,
-                                         tokens, temperature, seed, accept_len, out_tokens, p_at,
-                                         q_at, workspace, s, all_greedy, events);
-  }
-  return vec ? launch_all<false, true>(target, draft, B, V, max_k, n_draft_rows, offsets, tokens,
-                                       temperature, seed, accept_len, out_tokens, p_at, q_at,
-                                       workspace, s, all_greedy, events)
-             : launch_all<false, false>(target, draft, B, V, max_k, n_draft_rows, offsets, tokens,
-                                        temperature, seed, accept_len, out_tokens, p_at, q_at,
-                                        workspace, s, all_greedy, events);
+  if (bf16)
+    return vec ? launch<true, true>(prm, grid, s, ev0, ev1)
+               : launch<true, false>(prm, grid, s, ev0, ev1);
+  return vec ? launch<false, true>(prm, grid, s, ev0, ev1)
+             : launch<false, false>(prm, grid, s, ev0, ev1);
 }
 
 }  // namespace
@@ -643,7 +796,7 @@ int spec_verify_greedy(const void* target_logits, int32_t dtype, int32_t B, int3
                        void* workspace, size_t workspace_bytes, void* stream) {
   return dispatch(target_logits, nullptr, dtype, B, V, max_k, n_draft_rows, draft_offsets,
                   draft_tokens, nullptr, 0, accept_len, out_tokens, nullptr, nullptr, workspace,
-                  workspace_bytes, stream, true, nullptr);
+                  workspace_bytes, stream, true, nullptr, nullptr);
 }
 
 int spec_verify_sample(const void* target_logits, const void* draft_logits, int32_t dtype,
@@ -654,7 +807,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, int3
                        void* workspace, size_t workspace_bytes, void* stream) {
   return dispatch(target_logits, draft_logits, dtype, B, V, max_k, n_draft_rows, draft_offsets,
                   draft_tokens, temperature, seed, accept_len, out_tokens, p_at_draft,
-                  q_at_draft, workspace, workspace_bytes, stream, false, nullptr);
+                  q_at_draft, workspace, workspace_bytes, stream, false, nullptr, nullptr);
 }
 
 int spec_verify_sample_timed(const void* target_logits, const void* draft_logits, int32_t dtype,
@@ -663,11 +816,11 @@ int spec_verify_sample_timed(const void* target_logits, const void* draft_logits
                              const float* temperature, uint64_t seed, int32_t* accept_len,
                              int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
                              void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* events) {
-  if (!events || !events[0] || !events[1] || !events[2]) return SV_ERR_NULL;
+                             void* event_start, void* event_end) {
+  if (!event_start || !event_end) return SV_ERR_NULL;
   return dispatch(target_logits, draft_logits, dtype, B, V, max_k, n_draft_rows, draft_offsets,
                   draft_tokens, temperature, seed, accept_len, out_tokens, p_at_draft,
-                  q_at_draft, workspace, workspace_bytes, stream, false, events);
+                  q_at_draft, workspace, workspace_bytes, stream, false, event_start, event_end);
 }
 
 const char* spec_verify_status_string(int status) {

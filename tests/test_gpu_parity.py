@@ -4,6 +4,7 @@ Every test prints the case it is about to launch before touching the GPU.
 Workload numbers follow the synthetic workload table (1 tiny, 2 Llama-class,
 3 large-batch fp32, 4 MTP K=1, 5 ragged).
 """
+import copy
 import math
 
 import numpy as np
@@ -43,7 +44,8 @@ def test_tiny_1000_steps():
         compare(b, run_gpu(b, "sample"), orc, tally=tally_s)
         og = oracle.verify_batch(b, greedy_only=True)
         compare(b, run_gpu(b, "greedy"), og, greedy_only=True, tally=tally_g)
-        bz = W.make_batch(1, step, temperature_override=0.0)
+        bz = copy.deepcopy(b)  # same tokens; every request greedy
+        bz.temperature[:] = 0.0
         compare(bz, run_gpu(bz, "sample"), og, tally=tally_g)
     print(tally_s, tally_g)
     assert tally_s.flagged <= 0.001 * tally_s.sampled + 1
