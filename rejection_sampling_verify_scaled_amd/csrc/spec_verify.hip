@@ -29,6 +29,14 @@
 // dispatch the wait always ends.  The wait is also bounded (kSpinLimit polls);
 // if it ever expired the request would report accept_len = -1.
 //
+// Cross-workgroup data (partials, published records, flags) moves only
+// through device-coherent stores and loads (agent-scope relaxed atomics,
+// i.e. sc1 accesses that bypass the per-XCD L2 for these lines), and each
+// data store is drained (s_waitcnt) before the counter increment that
+// announces it.  No agent-scope release/acquire fence is used: on gfx950
+// those write back or invalidate the whole L2 of the XCD, which thousands of
+// workgroups per call cannot afford.
+//
 // Race keys are kept in base-2 logs: key_v = log2 w_v - log2(-log2 U_v), a
 // strictly increasing function of the natural-log key ln w_v - ln E_v, so the
 // winner is the same token.
@@ -154,7 +162,41 @@ __device__ __forceinline__ void block_argmax(float& key, int& idx, float* sh_k, 
   for (int w = 1; w < kWaves; ++w) merge_argmax(key, idx, sh_k[w], sh_i[w]);
 }
 
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Device-coherent 8-byte store / load of a float2 (bypasses stale L2 lines).
+__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
+  const uint64_t bits = static_cast<uint64_t>(__float_as_uint(v.x)) |
+                        (static_cast<uint64_t>(__float_as_uint(v.y)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 load_coherent(const float2* p) {
+  const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(bits)),
+                     __uint_as_float(static_cast<uint32_t>(bits >> 32)));
+}
+
+__device__ __forceinline__ void store_coherent_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t load_coherent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Drain this thread's outstanding memory operations, so a device-coherent
+// store is visible before the atomic that follows announces it.  The signal
+// fences keep the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void drain_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ uint32_t count_one(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ------------------------------------------------------------------ workspace
 
@@ -169,12 +211,38 @@ struct Published {
   float cf;        // log2(e) / T
   int32_t pad;
 };
+static_assert(sizeof(Published) == 4 * sizeof(float2), "Published moves as four float2");
 
+__device__ __forceinline__ void publish(Published* dst, const Published& v) {
+  const float2* src = reinterpret_cast<const float2*>(&v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store_coherent(reinterpret_cast<float2*>(dst) + i, src[i]);
+}
+
+__device__ __forceinline__ Published read_published(const Published* src) {
+  Published v;
+  float2* dst = reinterpret_cast<float2*>(&v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = load_coherent(reinterpret_cast<const float2*>(src) + i);
+  return v;
+}
+
+// Data regions grow from the start of the workspace and depend on the call's
+// sizes; the per-request counters sit in 16-byte slots at the end of the
+// caller's buffer (slot b at end - 16 (b + 1)), so their addresses do not
+// move between calls that share a buffer.
 struct Layout {
   int J;    // row slots per request: target 0..max_k, then draft 0..max_k-1
   int nc1;  // statistics chunks per row
   int nc2;  // race chunks per row
-  size_t stats_off, race_off, pub_off, count_off, total;
+  size_t stats_off, race_off, pub_off, data_end, total;
+};
+
+struct Counters {
+  uint32_t done;       // finished row-statistics workgroups
+  uint32_t ready;      // the finisher has published
+  uint32_t race_done;  // finished race workgroups
+  uint32_t pad;
 };
 
 __host__ __device__ inline int ceil_div(int64_t a, int64_t b) {
@@ -193,8 +261,8 @@ Layout make_layout(int32_t B, int32_t V, int32_t max_k, bool bf16) {
       static_cast<size_t>(B) * L.J * ceil_div(V, stats_chunk(false)) * sizeof(float2);
   L.race_off = round256(stats_bytes);
   L.pub_off = L.race_off + round256(static_cast<size_t>(B) * L.nc2 * sizeof(float2));
-  L.count_off = L.pub_off + round256(static_cast<size_t>(B) * sizeof(Published));
-  L.total = L.count_off + round256(static_cast<size_t>(B) * 3 * sizeof(uint32_t));
+  L.data_end = L.pub_off + round256(static_cast<size_t>(B) * sizeof(Published));
+  L.total = L.data_end + static_cast<size_t>(B) * sizeof(Counters) + 16;
   return L;
 }
 
@@ -210,14 +278,14 @@ struct Params {
   float2* part;          // [B][J][nc1] row-statistics partials
   float2* race_part;     // [B][nc2] race chunk winners (key, index bits)
   Published* pub;        // [B]
-  uint32_t* done;        // [B] finished row-statistics workgroups
-  uint32_t* ready;       // [B] finisher has published
-  uint32_t* race_done;   // [B] finished race workgroups
+  Counters* cnt_end;     // request b's counters at cnt_end[-1 - b]
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_at;
   float* q_at;
 };
+
+__device__ __forceinline__ Counters& counters(const Params& p, int b) { return p.cnt_end[-1 - b]; }
 
 // Per-request checks every workgroup can make from the request's scalars.
 struct Req {
@@ -293,7 +361,7 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
       v[i] = make_float2(-INFINITY, 0.f);
       if (row < nrows && c < p.nc1) {
         const int j = (row <= K) ? row : p.max_k + 1 + (row - K - 1);
-        v[i] = p.part[(static_cast<int64_t>(b) * J + j) * p.nc1 + c];
+        v[i] = load_coherent(p.part + (static_cast<int64_t>(b) * J + j) * p.nc1 + c);
       }
     }
 #pragma unroll
@@ -329,11 +397,15 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
   if (sh_bad) {
     write_fault(p, b, r);
     if (tid == 0) {
+      Counters& cn = counters(p, b);
+      store_coherent_u32(&cn.done, 0u);
       if (!greedy) {
-        p.pub[b].status = kStatusFault;
-        __hip_atomic_store(&p.ready[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        Published pub = {};
+        pub.status = kStatusFault;
+        publish(p.pub + b, pub);
+        drain_memory();
+        store_coherent_u32(&cn.ready, 1u);
       }
-      p.done[b] = 0u;
     }
     return;
   }
@@ -355,7 +427,7 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
     }
     if (tid == 0) {
       p.accept_len[b] = n;
-      p.done[b] = 0u;
+      store_coherent_u32(&counters(p, b).done, 0u);
     }
     return;
   }
@@ -375,7 +447,7 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
   const uint64_t mask = __ballot(reject);
   if (tid == 0) {
     const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
-    Published& pub = p.pub[b];
+    Published pub;
     pub.n = n;
     pub.status = kStatusOk;
     pub.mp = sh_m[n];
@@ -383,8 +455,12 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
     pub.mq = n < K ? sh_m[K + 1 + n] : 0.f;
     pub.lsq = n < K ? sh_ls[K + 1 + n] : 0.f;
     pub.cf = cf;
-    p.done[b] = 0u;
-    __hip_atomic_store(&p.ready[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    pub.pad = 0;
+    publish(p.pub + b, pub);
+    Counters& cn = counters(p, b);
+    store_coherent_u32(&cn.done, 0u);
+    drain_memory();
+    store_coherent_u32(&cn.ready, 1u);
   }
 }
 
@@ -520,15 +596,13 @@ __device__ void stats_slot(const Params& p, int64_t bid) {
 
   __shared__ int sh_last;
   if (tid == 0) {
-    p.part[(static_cast<int64_t>(b) * J + j) * p.nc1 + c] = result;
+    store_coherent(p.part + (static_cast<int64_t>(b) * J + j) * p.nc1 + c, result);
+    drain_memory();
     const uint32_t need = static_cast<uint32_t>((r.greedy ? r.K + 1 : 2 * r.K + 1) * p.nc1);
-    const uint32_t before =
-        __hip_atomic_fetch_add(&p.done[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (before + 1 == need) ? 1 : 0;
+    sh_last = (count_one(&counters(p, b).done) + 1 == need) ? 1 : 0;
   }
   __syncthreads();
   if (!sh_last) return;
-  acquire_agent();
   finish_request<BF16>(p, b, r);
 }
 
@@ -603,10 +677,11 @@ __device__ void race_slot(const Params& p, int64_t rid) {
   }
   if (r.greedy) return;  // finished by its row-statistics finisher
 
+  Counters& cn = counters(p, b);
   __shared__ int sh_flag;
   if (tid == 0) {
     unsigned it = 0;
-    while (__hip_atomic_load(&p.ready[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    while (load_coherent_u32(&cn.ready) == 0u) {
       if (++it > kSpinLimit) break;
       __builtin_amdgcn_s_sleep(2);
     }
@@ -617,8 +692,7 @@ __device__ void race_slot(const Params& p, int64_t rid) {
     if (c == 0 && tid == 0) p.accept_len[b] = -1;
     return;
   }
-  acquire_agent();
-  const Published pub = p.pub[b];
+  const Published pub = read_published(p.pub + b);
   const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
   const int64_t drow0 = r.off0;
   const int64_t esz = BF16 ? 2 : 4;
@@ -656,21 +730,21 @@ __device__ void race_slot(const Params& p, int64_t rid) {
 
   __shared__ int sh_last;
   if (tid == 0) {
-    if (pub.status == kStatusOk)
-      p.race_part[static_cast<int64_t>(b) * p.nc2 + c] = make_float2(key, __int_as_float(idx));
-    const uint32_t before =
-        __hip_atomic_fetch_add(&p.race_done[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (before + 1 == static_cast<uint32_t>(p.nc2)) ? 1 : 0;
+    if (pub.status == kStatusOk) {
+      store_coherent(p.race_part + static_cast<int64_t>(b) * p.nc2 + c,
+                     make_float2(key, __int_as_float(idx)));
+      drain_memory();
+    }
+    sh_last = (count_one(&cn.race_done) + 1 == static_cast<uint32_t>(p.nc2)) ? 1 : 0;
   }
   __syncthreads();
   if (!sh_last) return;
-  acquire_agent();
 
   if (pub.status == kStatusOk) {
     key = -INFINITY;
     idx = INT_MAX;
     for (int i = tid; i < p.nc2; i += kThreads) {
-      const float2 w = p.race_part[static_cast<int64_t>(b) * p.nc2 + i];
+      const float2 w = load_coherent(p.race_part + static_cast<int64_t>(b) * p.nc2 + i);
       merge_argmax(key, idx, w.x, __float_as_int(w.y));
     }
     block_argmax(key, idx, sh_key, sh_idx);
@@ -693,8 +767,8 @@ __device__ void race_slot(const Params& p, int64_t rid) {
     if (tid == 0) p.accept_len[b] = n;
   }
   if (tid == 0) {
-    p.ready[b] = 0u;
-    p.race_done[b] = 0u;
+    store_coherent_u32(&cn.ready, 0u);
+    store_coherent_u32(&cn.race_done, 0u);
   }
 }
 
@@ -762,9 +836,9 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.part = reinterpret_cast<float2*>(ws + L.stats_off);
   prm.race_part = reinterpret_cast<float2*>(ws + L.race_off);
   prm.pub = reinterpret_cast<Published*>(ws + L.pub_off);
-  prm.done = reinterpret_cast<uint32_t*>(ws + L.count_off);
-  prm.ready = prm.done + B;
-  prm.race_done = prm.done + 2 * static_cast<int64_t>(B);
+  const uintptr_t end = (reinterpret_cast<uintptr_t>(ws) + workspace_bytes) & ~uintptr_t{15};
+  prm.cnt_end = reinterpret_cast<Counters*>(end);
+  if (reinterpret_cast<char*>(prm.cnt_end - B) < ws + L.data_end) return SV_ERR_WORKSPACE;
   prm.accept_len = accept_len;
   prm.out_tokens = out_tokens;
   prm.p_at = p_at;
