@@ -18,11 +18,13 @@
 //       sampled: gathers p_t(x_t), q_t(x_t), draws r_t, finds the first
 //                rejection n with a wave ballot, and publishes n with the
 //                statistics of row n.
-//   race workgroups, one per (sampled request, race chunk), last in the grid.
-//     Each waits for its request's publication, runs the exponential race
-//     over its chunk of row n -- residual (p_n - q_n)+ after a rejection,
-//     bonus p_K otherwise -- and the last of them folds the chunk winners
-//     and writes the outputs.
+//   race workgroups, one per (sampled request, race chunk).  Each waits for
+//     its request's publication, runs the exponential race over its chunk of
+//     row n -- residual (p_n - q_n)+ after a rejection, bonus p_K otherwise --
+//     and the last of them folds the chunk winners and writes the outputs.
+//     Request b's race workgroups sit in the grid right after the row
+//     statistics of request b + lag (lag ~ one residency's worth of
+//     workgroups), so race arithmetic overlaps the streaming of later rows.
 //
 // Forward progress: a race workgroup only waits for row-statistics
 // workgroups, which have lower indices and never wait, so with in-order
@@ -37,9 +39,13 @@
 // those write back or invalidate the whole L2 of the XCD, which thousands of
 // workgroups per call cannot afford.
 //
-// Race keys are kept in base-2 logs: key_v = log2 w_v - log2(-log2 U_v), a
-// strictly increasing function of the natural-log key ln w_v - ln E_v, so the
-// winner is the same token.
+// Race keys: the winner maximises ln w_v - ln E_v, i.e. w_v / E_v.  Inside a
+// thread candidates are compared by cross-multiplication (w_a e_b > w_b e_a)
+// with e = -log2 U = E / ln 2 (a common factor); a thread's best becomes the
+// float key w / e for the merges across threads, waves and chunks.  Weights
+// are 2^(z c - fl(m c)) with c = log2(e) / T, fl(m c) the rounded product
+// for the row's maximum m; the same rounded offset is used when the row's
+// sum is formed, so it cancels exactly from p = w / sum.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -58,6 +64,9 @@ constexpr int kRaceChunk = kThreads * kRaceGroups * 4;  // tokens per race chunk
 constexpr int kRowsMax = 2 * SV_KMAX + 1;               // row slots per request
 constexpr int kRowsPerWave = (kRowsMax + kWaves - 1) / kWaves;
 constexpr unsigned kSpinLimit = 1u << 16;
+#ifndef SV_RACE_LAG_SLOTS
+#define SV_RACE_LAG_SLOTS 1536  // grid slots between a request's statistics and its race
+#endif
 constexpr float kLog2e = 1.4426950408889634f;
 
 __host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
@@ -111,12 +120,23 @@ __device__ __forceinline__ float uniform_open01(uint32_t x) {
   return __fmaf_rn(static_cast<float>(x >> 9), 0x1p-23f, 0x1p-24f);
 }
 
-// Larger max wins; a chunk's sum is rescaled to the common max.  A side with
-// max == -inf contributes 0 * s, which keeps a NaN sum NaN.
+// fl(m * c): the row-maximum offset, rounded once and never contracted, so
+// every place that needs it gets the identical float.
+__device__ __forceinline__ float scaled_max(float m, float cf) { return __fmul_rn(m, cf); }
+
+// log2 of the unnormalised weight 2^(z c - fl(m c)).
+__device__ __forceinline__ float scaled_logit(float z, float cf, float mc) {
+  return __fmaf_rn(z, cf, -mc);
+}
+
+// (max, sum) pairs; a sum s is relative to fl(max * c).  Larger max wins and
+// the other sum is rescaled by 2^(fl(m c) - fl(M c)).  A side with max == -inf
+// contributes 0 * s, which keeps a NaN sum NaN.
 __device__ __forceinline__ void merge_stats(float& m, float& s, float m2, float s2, float cf) {
   const float M = fmaxf(m, m2);
-  const float f1 = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * cf);
-  const float f2 = (m2 == -INFINITY) ? 0.f : fast_exp2((m2 - M) * cf);
+  const float Mc = scaled_max(M, cf);
+  const float f1 = (m == -INFINITY) ? 0.f : fast_exp2(scaled_max(m, cf) - Mc);
+  const float f2 = (m2 == -INFINITY) ? 0.f : fast_exp2(scaled_max(m2, cf) - Mc);
   s = s * f1 + s2 * f2;
   m = M;
 }
@@ -206,8 +226,8 @@ enum : int32_t { kStatusOk = 0, kStatusFault = 1 };
 struct Published {
   int32_t n;       // first rejected position (K when every draft passed)
   int32_t status;  // kStatusOk / kStatusFault
-  float mp, lsp;   // target row n: max and log2 of its scaled sum
-  float mq, lsq;   // draft row n (residual race only)
+  float mcp, lsp;  // target row n: fl(max * c) and log2 of its sum
+  float mcq, lsq;  // draft row n (residual race only)
   float cf;        // log2(e) / T
   int32_t pad;
 };
@@ -262,7 +282,7 @@ Layout make_layout(int32_t B, int32_t V, int32_t max_k, bool bf16) {
   L.race_off = round256(stats_bytes);
   L.pub_off = L.race_off + round256(static_cast<size_t>(B) * L.nc2 * sizeof(float2));
   L.data_end = L.pub_off + round256(static_cast<size_t>(B) * sizeof(Published));
-  L.total = L.data_end + static_cast<size_t>(B) * sizeof(Counters) + 16;
+  L.total = round256(L.data_end + static_cast<size_t>(B) * sizeof(Counters) + 16);
   return L;
 }
 
@@ -274,7 +294,8 @@ struct Params {
   const float* temperature;  // NULL: every request greedy
   uint32_t k0, k1;           // Philox key
   int32_t B, V, max_k, n_draft_rows, nc1, nc2;
-  int64_t n_stats_slots;
+  int32_t lag;      // request b's race follows the statistics of request b + lag
+  int64_t S;        // statistics slots per request: (2 max_k + 1) * nc1
   float2* part;          // [B][J][nc1] row-statistics partials
   float2* race_part;     // [B][nc2] race chunk winners (key, index bits)
   Published* pub;        // [B]
@@ -437,8 +458,10 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
   if (tid < K) {
     const float zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
     const float zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
-    const float pp = fast_exp2((zp - sh_m[tid]) * cf - sh_ls[tid]);
-    const float qq = fast_exp2((zq - sh_m[K + 1 + tid]) * cf - sh_ls[K + 1 + tid]);
+    const float pp =
+        fast_exp2(scaled_logit(zp, cf, scaled_max(sh_m[tid], cf)) - sh_ls[tid]);
+    const float qq =
+        fast_exp2(scaled_logit(zq, cf, scaled_max(sh_m[K + 1 + tid], cf)) - sh_ls[K + 1 + tid]);
     const float u = uniform_open01(philox4x32_10(0u, tid, b, 1u, p.k0, p.k1).w[0]);
     reject = !(u * qq < pp);
     if (p.p_at) p.p_at[drow0 + tid] = pp;
@@ -450,9 +473,9 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
     Published pub;
     pub.n = n;
     pub.status = kStatusOk;
-    pub.mp = sh_m[n];
+    pub.mcp = scaled_max(sh_m[n], cf);
     pub.lsp = sh_ls[n];
-    pub.mq = n < K ? sh_m[K + 1 + n] : 0.f;
+    pub.mcq = n < K ? scaled_max(sh_m[K + 1 + n], cf) : 0.f;
     pub.lsq = n < K ? sh_ls[K + 1 + n] : 0.f;
     pub.cf = cf;
     pub.pad = 0;
@@ -467,13 +490,12 @@ __device__ void finish_request(const Params& p, int b, const Req& r) {
 // ------------------------------------------------------------------ row statistics
 
 template <bool BF16, bool VEC>
-__device__ void stats_slot(const Params& p, int64_t bid) {
+__device__ void stats_slot(const Params& p, int b, int slot) {
   constexpr int EPV = elems_per_vec(BF16);
   constexpr int CHUNK = stats_chunk(BF16);
   const int J = 2 * p.max_k + 1;
-  const int c = static_cast<int>(bid % p.nc1);
-  const int j = static_cast<int>((bid / p.nc1) % J);
-  const int b = static_cast<int>(bid / (static_cast<int64_t>(p.nc1) * J));
+  const int c = slot % p.nc1;
+  const int j = slot / p.nc1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   const Req r = load_req(p, b);
@@ -568,13 +590,14 @@ __device__ void stats_slot(const Params& p, int64_t bid) {
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kStatsVecs * EPV; ++i) m = fmaxf(m, x[i]);
-    const float ms = (m == -INFINITY) ? 0.f : m;  // keeps a NaN visible when no finite max
+    // offset 0 when there is no finite max keeps a NaN visible in the sum
+    const float mc = (m == -INFINITY) ? 0.f : scaled_max(m, cf);
     float acc[kStatsVecs];
 #pragma unroll
     for (int u = 0; u < kStatsVecs; ++u) {
       float sum = 0.f;
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) sum += fast_exp2((x[u * EPV + k] - ms) * cf);
+      for (int k = 0; k < EPV; ++k) sum += fast_exp2(scaled_logit(x[u * EPV + k], cf, mc));
       acc[u] = sum;
     }
 #pragma unroll
@@ -630,41 +653,37 @@ __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend,
   }
 }
 
-// Race keys of tokens 4g..4g+3 folded into (best_key, best_idx); tokens are
-// visited in increasing order, so a strict > keeps the lowest index on ties.
+// Race candidates of tokens 4g..4g+3 folded into this thread's best
+// (bw / be, bidx); tokens arrive in increasing order, so a strict > keeps the
+// lowest index on ties.
 __device__ __forceinline__ void race_group(const float zp[4], const float zq[4], bool residual,
                                            const Published& pub, int64_t g, int64_t v_end,
-                                           uint32_t b, uint32_t k0, uint32_t k1,
-                                           float& best_key, int& best_idx) {
+                                           uint32_t b, uint32_t k0, uint32_t k1, float& bw,
+                                           float& be, int& bidx) {
   const Philox4 r = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(pub.n), b, 0u,
                                   k0, k1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t v = g * 4 + k;
     if (v >= v_end) break;
-    const float e2 = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
-    float lw;
-    if (residual) {
-      const float pv = fast_exp2((zp[k] - pub.mp) * pub.cf - pub.lsp);
-      const float qv = fast_exp2((zq[k] - pub.mq) * pub.cf - pub.lsq);
-      const float w = pv - qv;
-      if (!(w > 0.f)) continue;
-      lw = fast_log2(w);
-    } else {
-      lw = (zp[k] - pub.mp) * pub.cf;
-    }
-    const float key = lw - fast_log2(e2);
-    if (key > best_key) {
-      best_key = key;
-      best_idx = static_cast<int>(v);
+    const float e = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
+    float w = fast_exp2(scaled_logit(zp[k], pub.cf, pub.mcp) - pub.lsp);
+    if (residual) w -= fast_exp2(scaled_logit(zq[k], pub.cf, pub.mcq) - pub.lsq);
+    if (w * be > bw * e) {
+      bw = w;
+      be = e;
+      bidx = static_cast<int>(v);
     }
   }
 }
 
+// A thread's best as a float key for merging (-inf when it has none).
+__device__ __forceinline__ float race_key(float bw, float be, int bidx) {
+  return bidx == INT_MAX ? -INFINITY : bw / be;
+}
+
 template <bool BF16, bool VEC>
-__device__ void race_slot(const Params& p, int64_t rid) {
-  const int b = static_cast<int>(rid / p.nc2);
-  const int c = static_cast<int>(rid % p.nc2);
+__device__ void race_slot(const Params& p, int b, int c) {
   const int tid = threadIdx.x;
   const Req r = load_req(p, b);
   if (!r.slice_ok) {
@@ -706,6 +725,7 @@ __device__ void race_slot(const Params& p, int64_t rid) {
   float key = -INFINITY;
   int idx = INT_MAX;
   if (pub.status == kStatusOk) {
+    float bw = 0.f, be = 1.f;  // any w > 0 beats the empty candidate
     const int64_t v_begin = static_cast<int64_t>(c) * kRaceChunk;
     const int64_t v_end = (v_begin + kRaceChunk < p.V) ? v_begin + kRaceChunk : p.V;
     float zp[kRaceGroups][4], zq[kRaceGroups][4];
@@ -723,8 +743,9 @@ __device__ void race_slot(const Params& p, int64_t rid) {
     for (int gi = 0; gi < kRaceGroups; ++gi) {
       const int64_t g = v_begin / 4 + gi * kThreads + tid;
       if (g * 4 < v_end)
-        race_group(zp[gi], zq[gi], residual, pub, g, v_end, b, p.k0, p.k1, key, idx);
+        race_group(zp[gi], zq[gi], residual, pub, g, v_end, b, p.k0, p.k1, bw, be, idx);
     }
+    key = race_key(bw, be, idx);
     block_argmax(key, idx, sh_key, sh_idx);
   }
 
@@ -750,13 +771,14 @@ __device__ void race_slot(const Params& p, int64_t rid) {
     block_argmax(key, idx, sh_key, sh_idx);
     if (idx == INT_MAX) {
       // no token had p > q (rounding can only cause this when p == q): race on p_n
-      key = -INFINITY;
+      float bw = 0.f, be = 1.f;
       for (int64_t g = tid; g * 4 < p.V; g += kThreads) {
         float zp[4];
         const float zq[4] = {0.f, 0.f, 0.f, 0.f};
         load4<BF16, VEC>(prow, g * 4, p.V, zp);
-        race_group(zp, zq, false, pub, g, p.V, b, p.k0, p.k1, key, idx);
+        race_group(zp, zq, false, pub, g, p.V, b, p.k0, p.k1, bw, be, idx);
       }
+      key = race_key(bw, be, idx);
       block_argmax(key, idx, sh_key, sh_idx);
     }
     const int n = pub.n;
@@ -774,13 +796,31 @@ __device__ void race_slot(const Params& p, int64_t rid) {
 
 // ------------------------------------------------------------------ kernel
 
+// Grid order (S statistics slots per request, nc2 race slots per request,
+// d = min(lag, B)):
+//   [stats 0] .. [stats d-1]
+//   [stats d][race 0] [stats d+1][race 1] .. [stats B-1][race B-1-d]
+//   [race B-d] .. [race B-1]
+// so every race slot comes after all statistics slots of its request.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
-  const int64_t bid = blockIdx.x;
-  if (bid < p.n_stats_slots)
-    stats_slot<BF16, VEC>(p, bid);
-  else
-    race_slot<BF16, VEC>(p, bid - p.n_stats_slots);
+  const int64_t g = blockIdx.x;
+  const int64_t d = p.lag < p.B ? p.lag : p.B;
+  const int64_t head = d * p.S;
+  const int64_t seg = p.S + p.nc2;
+  const int64_t body = head + (p.B - d) * seg;
+  if (g < head) {
+    stats_slot<BF16, VEC>(p, static_cast<int>(g / p.S), static_cast<int>(g % p.S));
+  } else if (g < body) {
+    const int64_t k = (g - head) / seg, o = (g - head) % seg;
+    if (o < p.S)
+      stats_slot<BF16, VEC>(p, static_cast<int>(d + k), static_cast<int>(o));
+    else
+      race_slot<BF16, VEC>(p, static_cast<int>(k), static_cast<int>(o - p.S));
+  } else {
+    const int64_t h = g - body;
+    race_slot<BF16, VEC>(p, static_cast<int>(p.B - d + h / p.nc2), static_cast<int>(h % p.nc2));
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -831,8 +871,9 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.max_k = max_k;
   prm.n_draft_rows = n_draft_rows;
   prm.nc1 = L.nc1;
-  prm.nc2 = L.nc2;
-  prm.n_stats_slots = static_cast<int64_t>(B) * L.J * L.nc1;
+  prm.nc2 = all_greedy ? 0 : L.nc2;
+  prm.S = static_cast<int64_t>(L.J) * L.nc1;
+  prm.lag = all_greedy ? B : ceil_div(SV_RACE_LAG_SLOTS, prm.S);
   prm.part = reinterpret_cast<float2*>(ws + L.stats_off);
   prm.race_part = reinterpret_cast<float2*>(ws + L.race_off);
   prm.pub = reinterpret_cast<Published*>(ws + L.pub_off);
@@ -843,7 +884,7 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.out_tokens = out_tokens;
   prm.p_at = p_at;
   prm.q_at = q_at;
-  const int64_t grid = prm.n_stats_slots + (all_greedy ? 0 : static_cast<int64_t>(B) * L.nc2);
+  const int64_t grid = static_cast<int64_t>(B) * (prm.S + prm.nc2);
   if (grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 && aligned16(target) && (!draft || aligned16(draft));
