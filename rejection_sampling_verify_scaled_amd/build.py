@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
+    # no implicit multiply-add fusion: the kernel relies on fl(m*c) being the
+    # same rounded product everywhere it appears; every intended fma is explicit
+    "-ffp-contract=off",
     # packed-FP32 instructions stay off: hipcc would otherwise form them itself
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
