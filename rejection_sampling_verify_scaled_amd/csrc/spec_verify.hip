@@ -2,52 +2,58 @@
 //
 // What is computed is stated in include/spec_verify.h (the accept / residual /
 // bonus rule of "Decodificación Especulativa y EAGLE", section "La Regla de
-// Exactitud", and its greedy case).  How it runs on MI355X: one launch, two
-// kinds of workgroup.
+// Exactitud", and its greedy case).  How it runs on MI355X: one launch whose
+// workgroups each take one job from a fixed schedule.
 //
-//   row-statistics workgroups, one per (request, row slot, V-chunk), first in
-//     the grid.  Each streams its chunk with 16-byte loads and reduces it to
-//     one 8-byte partial: (max, sum of 2^((z - max) * log2(e) / T)) for rows a
-//     sampled request needs, (max, lowest argmax index) for rows of a greedy
-//     request.  Draft rows of greedy requests are never read.  These carry
-//     all of the HBM traffic.  The last of a request's workgroups to finish
-//     (atomic counter; nobody waits) becomes the request's finisher: it folds
-//     the partials into per-row (max, log2 sum), and
-//       greedy:  finds the first draft that differs from the row argmax and
-//                writes the request's outputs;
-//       sampled: gathers p_t(x_t), q_t(x_t), draws r_t, finds the first
-//                rejection n with a wave ballot, and publishes n with the
-//                statistics of row n.
-//   race workgroups, one per (sampled request, race chunk).  Each waits for
-//     its request's publication, runs the exponential race over its chunk of
-//     row n -- residual (p_n - q_n)+ after a rejection, bonus p_K otherwise --
-//     and the last of them folds the chunk winners and writes the outputs.
-//     Request b's race workgroups sit in the grid right after the row
-//     statistics of request b + lag (lag ~ one residency's worth of
-//     workgroups), so race arithmetic overlaps the streaming of later rows.
+// Jobs of request b:
+//   SA  statistics of a sampled request: one job per (row, 64 KiB V-chunk) of
+//       its K+1 target and K draft rows.  Streams the chunk with 16-byte
+//       loads and reduces it to one 8-byte partial (max, sum of
+//       2^(z c - fl(max c))), c = log2(e) / T, then stores it and exits.
+//   FA  finisher of a sampled request: collects the partials, folds them into
+//       per-row (max, log2 sum), gathers p_t(x_t) and q_t(x_t), draws r_t,
+//       finds the first rejection n with a wave ballot, and publishes n with
+//       the statistics of row n.
+//   R   race of a sampled request: one job per 4096-token chunk of row n, the
+//       exponential race over the residual (p_n - q_n)+ after a rejection or
+//       over p_K otherwise, plus one job that folds the chunk winners and
+//       writes the outputs.
+//   SB  statistics of a greedy request: (max, lowest argmax index) per chunk
+//       of its K+1 target rows (draft rows are never read).
+//   FB  finisher of a greedy request: first draft that differs from the row
+//       argmax; writes the outputs.  Also reports requests with a bad slice
+//       or temperature.
+// A job that does not apply to request b (e.g. SA of a greedy request) exits
+// at once.
 //
-// Forward progress: a race workgroup only waits for row-statistics
-// workgroups, which have lower indices and never wait, so with in-order
-// dispatch the wait always ends.  The wait is also bounded (kSpinLimit polls);
-// if it ever expired the request would report accept_len = -1.
+// Schedule: request b's SA jobs sit at "time" b, FA at b + d1, R at b + d2,
+// SB at B + b and FB at B + b + d1; the grid lists times in order and, inside
+// a time, the jobs in the order SA, FA, R, SB, FB.  So every job comes after
+// the jobs it depends on, sampled requests stream first, and their finishing
+// and races overlap the streaming of greedy requests and of later sampled
+// requests.
 //
-// Cross-workgroup data (partials, published records, flags) moves only
-// through device-coherent stores and loads (agent-scope relaxed atomics,
-// i.e. sc1 accesses that bypass the per-XCD L2 for these lines), and each
-// data store is drained (s_waitcnt) before the counter increment that
-// announces it.  No agent-scope release/acquire fence is used: on gfx950
-// those write back or invalidate the whole L2 of the XCD, which thousands of
-// workgroups per call cannot afford.
+// Hand-offs between workgroups use 8-byte slots in the workspace that are
+// all-zero until written (a written slot never has all-zero bits: +0.0 is
+// stored as -0.0).  Producers store with a device-coherent (sc1) store and
+// exit; consumers poll with device-coherent loads, then write the slot back
+// to zero, so the workspace is all-zero again after every call.  No
+// agent-scope release/acquire fence is used (on gfx950 those write back or
+// invalidate the XCD's whole L2).  A consumer only waits for jobs that come
+// earlier in the grid; the earliest waiting job waits only for jobs that
+// never wait, so with in-order dispatch every wait ends.  Waits are also
+// bounded (kSpinLimit polls); an expired wait reports accept_len = -1.
 //
 // Race keys: the winner maximises ln w_v - ln E_v, i.e. w_v / E_v.  Inside a
 // thread candidates are compared by cross-multiplication (w_a e_b > w_b e_a)
 // with e = -log2 U = E / ln 2 (a common factor); a thread's best becomes the
 // float key w / e for the merges across threads, waves and chunks.  Weights
-// are 2^(z c - fl(m c)) with c = log2(e) / T, fl(m c) the rounded product
-// for the row's maximum m; the same rounded offset is used when the row's
-// sum is formed, so it cancels exactly from p = w / sum.
+// are 2^(z c - fl(m c)) with fl(m c) the rounded product for the row maximum
+// m; the same rounded offset is used when the row's sum is formed, so it
+// cancels exactly from p = w / sum.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -58,16 +64,19 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kStatsVecs = 8;   // 16-byte loads per thread per statistics chunk
+constexpr int kStatsVecs = 16;  // 16-byte loads per thread per statistics chunk
 constexpr int kRaceGroups = 4;  // 4-token Philox groups per thread per race chunk
 constexpr int kRaceChunk = kThreads * kRaceGroups * 4;  // tokens per race chunk
 constexpr int kRowsMax = 2 * SV_KMAX + 1;               // row slots per request
 constexpr int kRowsPerWave = (kRowsMax + kWaves - 1) / kWaves;
 constexpr unsigned kSpinLimit = 1u << 16;
-#ifndef SV_RACE_LAG_SLOTS
-#define SV_RACE_LAG_SLOTS 1536  // grid slots between a request's statistics and its race
-#endif
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef SV_FINISH_LAG_SLOTS
+#define SV_FINISH_LAG_SLOTS 1024  // grid slots between a request's statistics and its finisher
+#endif
+#ifndef SV_RACE_LAG_SLOTS
+#define SV_RACE_LAG_SLOTS 2048  // grid slots between a request's statistics and its race
+#endif
 
 __host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
 __host__ __device__ constexpr int stats_chunk(bool bf16) {
@@ -120,9 +129,9 @@ __device__ __forceinline__ float uniform_open01(uint32_t x) {
   return __fmaf_rn(static_cast<float>(x >> 9), 0x1p-23f, 0x1p-24f);
 }
 
-// fl(m * c): the row-maximum offset, rounded once and never contracted, so
-// every place that needs it gets the identical float.
-__device__ __forceinline__ float scaled_max(float m, float cf) { return __fmul_rn(m, cf); }
+// fl(m * c): the row-maximum offset, rounded once (the build disables
+// contraction), so every place that needs it gets the identical float.
+__device__ __forceinline__ float scaled_max(float m, float cf) { return m * cf; }
 
 // log2 of the unnormalised weight 2^(z c - fl(m c)).
 __device__ __forceinline__ float scaled_logit(float z, float cf, float mc) {
@@ -182,109 +191,87 @@ __device__ __forceinline__ void block_argmax(float& key, int& idx, float* sh_k, 
   for (int w = 1; w < kWaves; ++w) merge_argmax(key, idx, sh_k[w], sh_i[w]);
 }
 
-// Device-coherent 8-byte store / load of a float2 (bypasses stale L2 lines).
-__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
-  const uint64_t bits = static_cast<uint64_t>(__float_as_uint(v.x)) |
-                        (static_cast<uint64_t>(__float_as_uint(v.y)) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
+// ------------------------------------------------------------------ hand-off slots
 
-__device__ __forceinline__ float2 load_coherent(const float2* p) {
-  const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float(static_cast<uint32_t>(bits)),
-                     __uint_as_float(static_cast<uint32_t>(bits >> 32)));
+// (float, word) packed so a written slot is never all-zero bits.
+__device__ __forceinline__ uint64_t pack_slot(float a, uint32_t b) {
+  uint32_t ab = __float_as_uint(a);
+  if (ab == 0u) ab = 0x80000000u;  // +0.0 -> -0.0 (equal as a number)
+  return static_cast<uint64_t>(ab) | (static_cast<uint64_t>(b) << 32);
 }
+__device__ __forceinline__ float slot_f(uint64_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v));
+}
+__device__ __forceinline__ uint32_t slot_w(uint64_t v) { return static_cast<uint32_t>(v >> 32); }
 
-__device__ __forceinline__ void store_coherent_u32(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ void slot_store(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ uint32_t load_coherent_u32(const uint32_t* p) {
+__device__ __forceinline__ uint64_t slot_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Drain this thread's outstanding memory operations, so a device-coherent
-// store is visible before the atomic that follows announces it.  The signal
-// fences keep the compiler from moving memory accesses across the wait.
+// Poll until the slot is written; 0 if the bounded wait expires.
+__device__ uint64_t slot_wait(const uint64_t* p) {
+  uint64_t v = slot_load(p);
+  for (unsigned it = 0; v == 0u && it < kSpinLimit; ++it) {
+    __builtin_amdgcn_s_sleep(2);
+    v = slot_load(p);
+  }
+  return v;
+}
+
+// Drain this thread's outstanding memory operations, so device-coherent
+// stores made so far are visible before the next one.  The signal fences keep
+// the compiler from moving memory accesses across the wait.
 __device__ __forceinline__ void drain_memory() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-__device__ __forceinline__ uint32_t count_one(uint32_t* counter) {
-  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ------------------------------------------------------------------ workspace
 
-enum : int32_t { kStatusOk = 0, kStatusFault = 1 };
+enum : uint32_t { kStatusOk = 1, kStatusFault = 2 };
 
-// What a sampled request's finisher publishes for its race workgroups.
-struct Published {
-  int32_t n;       // first rejected position (K when every draft passed)
-  int32_t status;  // kStatusOk / kStatusFault
-  float mcp, lsp;  // target row n: fl(max * c) and log2 of its sum
-  float mcq, lsq;  // draft row n (residual race only)
-  float cf;        // log2(e) / T
-  int32_t pad;
-};
-static_assert(sizeof(Published) == 4 * sizeof(float2), "Published moves as four float2");
-
-__device__ __forceinline__ void publish(Published* dst, const Published& v) {
-  const float2* src = reinterpret_cast<const float2*>(&v);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) store_coherent(reinterpret_cast<float2*>(dst) + i, src[i]);
-}
-
-__device__ __forceinline__ Published read_published(const Published* src) {
-  Published v;
-  float2* dst = reinterpret_cast<float2*>(&v);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = load_coherent(reinterpret_cast<const float2*>(src) + i);
-  return v;
-}
-
-// Data regions grow from the start of the workspace and depend on the call's
-// sizes; the per-request counters sit in 16-byte slots at the end of the
-// caller's buffer (slot b at end - 16 (b + 1)), so their addresses do not
-// move between calls that share a buffer.
 struct Layout {
   int J;    // row slots per request: target 0..max_k, then draft 0..max_k-1
   int nc1;  // statistics chunks per row
   int nc2;  // race chunks per row
-  size_t stats_off, race_off, pub_off, data_end, total;
+  size_t stats_off, race_off, pub_off, total;
 };
 
-struct Counters {
-  uint32_t done;       // finished row-statistics workgroups
-  uint32_t ready;      // the finisher has published
-  uint32_t race_done;  // finished race workgroups
-  uint32_t pad;
-};
-
-__host__ __device__ inline int ceil_div(int64_t a, int64_t b) {
-  return static_cast<int>((a + b - 1) / b);
-}
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 Layout make_layout(int32_t B, int32_t V, int32_t max_k, bool bf16) {
   Layout L;
   L.J = 2 * max_k + 1;
-  L.nc1 = ceil_div(V, stats_chunk(bf16));
-  L.nc2 = ceil_div(V, kRaceChunk);
+  L.nc1 = static_cast<int>(ceil_div(V, stats_chunk(bf16)));
+  L.nc2 = static_cast<int>(ceil_div(V, kRaceChunk));
   L.stats_off = 0;
+  // sized with the float32 chunk (the smaller one) so either dtype fits
   const size_t stats_bytes =
-      static_cast<size_t>(B) * L.J * ceil_div(V, stats_chunk(false)) * sizeof(float2);
+      static_cast<size_t>(B) * L.J * ceil_div(V, stats_chunk(false)) * sizeof(uint64_t);
   L.race_off = round256(stats_bytes);
-  L.pub_off = L.race_off + round256(static_cast<size_t>(B) * L.nc2 * sizeof(float2));
-  L.data_end = L.pub_off + round256(static_cast<size_t>(B) * sizeof(Published));
-  L.total = round256(L.data_end + static_cast<size_t>(B) * sizeof(Counters) + 16);
+  L.pub_off = L.race_off + round256(static_cast<size_t>(B) * L.nc2 * sizeof(uint64_t));
+  L.total = L.pub_off + round256(static_cast<size_t>(B) * 4 * sizeof(uint64_t));
   return L;
 }
+
+// Jobs in schedule order inside one time step.
+enum Job : int { kSA = 0, kFA = 1, kR = 2, kSB = 3, kFB = 4, kJobs = 5 };
+
+// A run of time steps with the same set of jobs present.
+struct Region {
+  int64_t g0;    // first grid slot
+  int32_t k0;    // first time step
+  int32_t seg;   // slots per time step
+  int32_t mask;  // jobs present (bit per Job)
+  int32_t pad;
+};
+constexpr int kMaxRegions = 12;
 
 struct Params {
   const void* target;
@@ -294,25 +281,27 @@ struct Params {
   const float* temperature;  // NULL: every request greedy
   uint32_t k0, k1;           // Philox key
   int32_t B, V, max_k, n_draft_rows, nc1, nc2;
-  int32_t lag;      // request b's race follows the statistics of request b + lag
-  int64_t S;        // statistics slots per request: (2 max_k + 1) * nc1
-  float2* part;          // [B][J][nc1] row-statistics partials
-  float2* race_part;     // [B][nc2] race chunk winners (key, index bits)
-  Published* pub;        // [B]
-  Counters* cnt_end;     // request b's counters at cnt_end[-1 - b]
+  uint64_t* part;       // [B][J][nc1] statistics partials
+  uint64_t* race_part;  // [B][nc2] race chunk winners
+  uint64_t* pub;        // [B][4] published record: (fl(m c), log2 sum) of target row n,
+                        // the same of draft row n, (c, n), (1, status) -- last written
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_at;
   float* q_at;
+  int32_t job_len[kJobs];  // slots each job kind takes per request
+  int32_t job_off[kJobs];  // time step of request 0's job
+  int32_t n_regions;
+  Region reg[kMaxRegions];
 };
 
-__device__ __forceinline__ Counters& counters(const Params& p, int b) { return p.cnt_end[-1 - b]; }
-
-// Per-request checks every workgroup can make from the request's scalars.
+// Per-request checks every job can make from the request's scalars.
 struct Req {
   int32_t off0, K;
   float T;
   bool slice_ok, temp_ok, greedy;
+  __device__ bool sampled() const { return slice_ok && temp_ok && !greedy; }
+  __device__ bool greedy_ok() const { return slice_ok && temp_ok && greedy; }
 };
 
 __device__ __forceinline__ Req load_req(const Params& p, int b) {
@@ -339,167 +328,23 @@ __device__ void write_fault(const Params& p, int b, const Req& r) {
   if (tid == 0) p.accept_len[b] = -1;
 }
 
-// ------------------------------------------------------------------ finisher
-
-template <bool BF16>
-__device__ void finish_request(const Params& p, int b, const Req& r) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = r.K;
-  const int J = 2 * p.max_k + 1;
-  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
-  const int64_t drow0 = r.off0;
-  const bool greedy = r.greedy;
-  const float cf = greedy ? 0.f : kLog2e / r.T;
-  const int nrows = greedy ? K + 1 : 2 * K + 1;  // rows 0..K target, K+1..2K draft 0..K-1
-
-  __shared__ int sh_bad;
-  __shared__ float sh_m[kRowsMax];
-  __shared__ float sh_ls[kRowsMax];  // greedy: argmax index bits
-  __shared__ int sh_n;
-  if (tid == 0) sh_bad = 0;
-  __syncthreads();
-  int32_t x = 0;
-  if (tid < K) {
-    x = p.tokens[r.off0 + tid];
-    if (x < 0 || x >= p.V) atomicOr(&sh_bad, 1);
-  }
-
-  // fold the partials: wave w takes rows w, w+4, ...; lanes take chunks
-  float a[kRowsPerWave], s[kRowsPerWave];
-  int ia[kRowsPerWave];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    a[i] = -INFINITY;
-    s[i] = 0.f;
-    ia[i] = INT_MAX;
-  }
-  for (int c0 = 0; c0 < p.nc1; c0 += 64) {
-    const int c = c0 + lane;
-    float2 v[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int row = wave + i * kWaves;
-      v[i] = make_float2(-INFINITY, 0.f);
-      if (row < nrows && c < p.nc1) {
-        const int j = (row <= K) ? row : p.max_k + 1 + (row - K - 1);
-        v[i] = load_coherent(p.part + (static_cast<int64_t>(b) * J + j) * p.nc1 + c);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      if (greedy) {
-        if (v[i].x > -INFINITY) merge_argmax(a[i], ia[i], v[i].x, __float_as_int(v[i].y));
-      } else {
-        merge_stats(a[i], s[i], v[i].x, v[i].y, cf);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int row = wave + i * kWaves;
-    if (greedy)
-      wave_merge_argmax(a[i], ia[i]);
-    else
-      wave_merge_stats(a[i], s[i], cf);
-    if (lane == 0 && row < nrows) {
-      const bool finite_max = a[i] > -INFINITY && a[i] < INFINITY;
-      if (greedy) {
-        if (!finite_max) atomicOr(&sh_bad, 1);
-        sh_ls[row] = __int_as_float(ia[i]);
-      } else {
-        if (!finite_max || !(s[i] < INFINITY)) atomicOr(&sh_bad, 1);
-        sh_m[row] = a[i];
-        sh_ls[row] = fast_log2(s[i]);
-      }
-    }
-  }
-  __syncthreads();
-
-  if (sh_bad) {
-    write_fault(p, b, r);
-    if (tid == 0) {
-      Counters& cn = counters(p, b);
-      store_coherent_u32(&cn.done, 0u);
-      if (!greedy) {
-        Published pub = {};
-        pub.status = kStatusFault;
-        publish(p.pub + b, pub);
-        drain_memory();
-        store_coherent_u32(&cn.ready, 1u);
-      }
-    }
-    return;
-  }
-
-  if (greedy) {
-    // first t < K whose draft differs from the argmax; the stop token is argmax row n
-    const bool mismatch = tid < K && __float_as_int(sh_ls[tid]) != x;
-    const uint64_t mask = __ballot(mismatch);
-    if (tid == 0) sh_n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
-    __syncthreads();
-    const int n = sh_n;
-    if (tid <= K) {
-      const int32_t y = __float_as_int(sh_ls[n]);
-      p.out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? y : -1);
-    }
-    if (tid < K) {
-      if (p.p_at) p.p_at[drow0 + tid] = NAN;
-      if (p.q_at) p.q_at[drow0 + tid] = NAN;
-    }
-    if (tid == 0) {
-      p.accept_len[b] = n;
-      store_coherent_u32(&counters(p, b).done, 0u);
-    }
-    return;
-  }
-
-  // ratio test r_t * q_t(x_t) < p_t(x_t), left to right (wave 0 holds t < K <= 8)
-  bool reject = false;
-  if (tid < K) {
-    const float zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
-    const float zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
-    const float pp =
-        fast_exp2(scaled_logit(zp, cf, scaled_max(sh_m[tid], cf)) - sh_ls[tid]);
-    const float qq =
-        fast_exp2(scaled_logit(zq, cf, scaled_max(sh_m[K + 1 + tid], cf)) - sh_ls[K + 1 + tid]);
-    const float u = uniform_open01(philox4x32_10(0u, tid, b, 1u, p.k0, p.k1).w[0]);
-    reject = !(u * qq < pp);
-    if (p.p_at) p.p_at[drow0 + tid] = pp;
-    if (p.q_at) p.q_at[drow0 + tid] = qq;
-  }
-  const uint64_t mask = __ballot(reject);
-  if (tid == 0) {
-    const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
-    Published pub;
-    pub.n = n;
-    pub.status = kStatusOk;
-    pub.mcp = scaled_max(sh_m[n], cf);
-    pub.lsp = sh_ls[n];
-    pub.mcq = n < K ? scaled_max(sh_m[K + 1 + n], cf) : 0.f;
-    pub.lsq = n < K ? sh_ls[K + 1 + n] : 0.f;
-    pub.cf = cf;
-    pub.pad = 0;
-    publish(p.pub + b, pub);
-    Counters& cn = counters(p, b);
-    store_coherent_u32(&cn.done, 0u);
-    drain_memory();
-    store_coherent_u32(&cn.ready, 1u);
-  }
+__device__ __forceinline__ uint64_t* part_slot(const Params& p, int b, int j, int c) {
+  return p.part + (static_cast<int64_t>(b) * (2 * p.max_k + 1) + j) * p.nc1 + c;
 }
 
-// ------------------------------------------------------------------ row statistics
+// ------------------------------------------------------------------ statistics jobs
 
 template <bool BF16, bool VEC>
-__device__ void stats_slot(const Params& p, int b, int slot) {
+__device__ void stats_job(const Params& p, int b, int slot, bool sampled_job) {
   constexpr int EPV = elems_per_vec(BF16);
   constexpr int CHUNK = stats_chunk(BF16);
-  const int J = 2 * p.max_k + 1;
+  constexpr int PAIR = 2 * EPV;  // elements folded per online step
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = slot % p.nc1;
   const int j = slot / p.nc1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   const Req r = load_req(p, b);
-  if (!r.slice_ok || !r.temp_ok) return;  // reported by the request's race workgroup 0
+  if (sampled_job ? !r.sampled() : !r.greedy_ok()) return;
   const void* base;
   int64_t row;
   if (j <= p.max_k) {
@@ -508,70 +353,71 @@ __device__ void stats_slot(const Params& p, int b, int slot) {
     row = static_cast<int64_t>(r.off0) + b + j;
   } else {
     const int t = j - p.max_k - 1;
-    if (r.greedy || t >= r.K) return;
+    if (t >= r.K) return;
     base = p.draft;
     row = static_cast<int64_t>(r.off0) + t;
   }
-
   const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
   const int64_t e_end = (e0 + CHUNK < p.V) ? e0 + CHUNK : p.V;
+  const int64_t rbase = row * static_cast<int64_t>(p.V);
 
-  // this thread's elements, in increasing index order
-  float x[kStatsVecs * EPV];
+  // issue every 16-byte load first; elements of vector u are
+  // e0 + (u * kThreads + tid) * EPV + [0, EPV), increasing in u
+  uint4 buf[kStatsVecs];
   if constexpr (VEC) {
-    const uint4* rowv = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(base) + row * static_cast<int64_t>(p.V) * (BF16 ? 2 : 4));
-    uint4 buf[kStatsVecs];
+    const uint4* rowv = reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
+                                                       rbase * (BF16 ? 2 : 4));
+    const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
     for (int u = 0; u < kStatsVecs; ++u) {
       const int64_t e = e0 + (static_cast<int64_t>(u) * kThreads + tid) * EPV;
-      if (e < e_end) {
-        buf[u] = rowv[e / EPV];
-      } else {
-        const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
-        buf[u] = make_uint4(ninf, ninf, ninf, ninf);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kStatsVecs; ++u) {
-      const uint32_t w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[u * 8 + 2 * k] = bf16_lo(w[k]);
-          x[u * 8 + 2 * k + 1] = bf16_hi(w[k]);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[u * 4 + k] = __uint_as_float(w[k]);
-      }
-    }
-  } else {
-    const int64_t rbase = row * static_cast<int64_t>(p.V);
-#pragma unroll
-    for (int u = 0; u < kStatsVecs; ++u) {
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        const int64_t e = e0 + (static_cast<int64_t>(u) * kThreads + tid) * EPV + k;
-        x[u * EPV + k] = (e < e_end) ? load_logit<BF16>(base, rbase + e) : -INFINITY;
-      }
+      buf[u] = (e < e_end) ? rowv[e / EPV] : make_uint4(ninf, ninf, ninf, ninf);
     }
   }
+  auto unpack_pair = [&](int pi, float* xs) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 v = buf[2 * pi + h];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (BF16) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            xs[h * 8 + 2 * k] = bf16_lo(w[k]);
+            xs[h * 8 + 2 * k + 1] = bf16_hi(w[k]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) xs[h * 4 + k] = __uint_as_float(w[k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const int64_t e = e0 + (static_cast<int64_t>(2 * pi + h) * kThreads + tid) * EPV + k;
+          xs[h * EPV + k] = (e < e_end) ? load_logit<BF16>(base, rbase + e) : -INFINITY;
+        }
+    }
+  };
 
   __shared__ float sh_a[kWaves];
   __shared__ float sh_b[kWaves];
-  float2 result;
+  uint64_t result = 0;
   if (r.greedy) {
     float best = -INFINITY;
     int idx = INT_MAX;
 #pragma unroll
-    for (int u = 0; u < kStatsVecs; ++u) {
+    for (int pi = 0; pi < kStatsVecs / 2; ++pi) {
+      float xs[PAIR];
+      unpack_pair(pi, xs);
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        const float v = x[u * EPV + k];
-        if (v > best) {
-          best = v;
-          idx = static_cast<int>(e0 + (static_cast<int64_t>(u) * kThreads + tid) * EPV + k);
+      for (int k = 0; k < PAIR; ++k) {
+        if (xs[k] > best) {
+          best = xs[k];
+          idx = static_cast<int>(e0 + (static_cast<int64_t>(2 * pi + k / EPV) * kThreads + tid) *
+                                          EPV + k % EPV);
         }
       }
     }
@@ -583,28 +429,32 @@ __device__ void stats_slot(const Params& p, int b, int slot) {
     __syncthreads();
     if (tid == 0) {
       for (int w = 1; w < kWaves; ++w) merge_argmax(best, idx, sh_a[w], __float_as_int(sh_b[w]));
-      result = make_float2(best, __int_as_float(idx));
+      result = pack_slot(best, static_cast<uint32_t>(idx));
     }
   } else {
+    // online over pairs of vectors: (m, s) with s relative to fl(m c)
     const float cf = kLog2e / r.T;
-    float m = -INFINITY;
+    float m = -INFINITY, s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kStatsVecs * EPV; ++i) m = fmaxf(m, x[i]);
-    // offset 0 when there is no finite max keeps a NaN visible in the sum
-    const float mc = (m == -INFINITY) ? 0.f : scaled_max(m, cf);
-    float acc[kStatsVecs];
+    for (int pi = 0; pi < kStatsVecs / 2; ++pi) {
+      float xs[PAIR];
+      unpack_pair(pi, xs);
+      float pm = xs[0];
 #pragma unroll
-    for (int u = 0; u < kStatsVecs; ++u) {
-      float sum = 0.f;
+      for (int k = 1; k < PAIR; ++k) pm = fmaxf(pm, xs[k]);
+      const float M = fmaxf(m, pm);
+      // offset 0 when there is no finite max keeps a NaN visible in the sum
+      const float Mc = (M == -INFINITY) ? 0.f : scaled_max(M, cf);
+      if (m != -INFINITY) s *= fast_exp2(scaled_max(m, cf) - Mc);
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) sum += fast_exp2(scaled_logit(x[u * EPV + k], cf, mc));
-      acc[u] = sum;
+      for (int k = 0; k < PAIR; k += 2) {
+        a0 += fast_exp2(scaled_logit(xs[k], cf, Mc));
+        a1 += fast_exp2(scaled_logit(xs[k + 1], cf, Mc));
+      }
+      s += a0 + a1;
+      m = M;
     }
-#pragma unroll
-    for (int h = kStatsVecs / 2; h >= 1; h >>= 1)
-#pragma unroll
-      for (int u = 0; u < h; ++u) acc[u] += acc[u + h];
-    float s = acc[0];
     wave_merge_stats(m, s, cf);
     if (lane == 0) {
       sh_a[wave] = m;
@@ -613,23 +463,179 @@ __device__ void stats_slot(const Params& p, int b, int slot) {
     __syncthreads();
     if (tid == 0) {
       for (int w = 1; w < kWaves; ++w) merge_stats(m, s, sh_a[w], sh_b[w], cf);
-      result = make_float2(m, s);
+      result = pack_slot(m, __float_as_uint(s));
     }
   }
-
-  __shared__ int sh_last;
-  if (tid == 0) {
-    store_coherent(p.part + (static_cast<int64_t>(b) * J + j) * p.nc1 + c, result);
-    drain_memory();
-    const uint32_t need = static_cast<uint32_t>((r.greedy ? r.K + 1 : 2 * r.K + 1) * p.nc1);
-    sh_last = (count_one(&counters(p, b).done) + 1 == need) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  finish_request<BF16>(p, b, r);
+  if (tid == 0) slot_store(part_slot(p, b, j, c), result);
 }
 
-// ------------------------------------------------------------------ race
+// ------------------------------------------------------------------ finishers
+
+// Waits for the partials of rows 0..nrows-1 (row r: slot j = r for r <= K,
+// j = max_k + r - K for the draft rows), folds them into sh_m / sh_ls and
+// zeroes the slots.  Greedy: sh_ls holds the argmax index bits.  Sets *bad on
+// a non-finite row, a NaN sum or an expired wait.
+template <bool GREEDY>
+__device__ void fold_partials(const Params& p, int b, int K, float cf, int nrows, float* sh_m,
+                              float* sh_ls, int* bad) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float a[kRowsPerWave], s[kRowsPerWave];
+  int ia[kRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    a[i] = -INFINITY;
+    s[i] = 0.f;
+    ia[i] = INT_MAX;
+  }
+  bool expired = false;
+  for (int c0 = 0; c0 < p.nc1; c0 += 64) {
+    const int c = c0 + lane;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int row = wave + i * kWaves;
+      if (row < nrows && c < p.nc1) {
+        const int j = (row <= K) ? row : p.max_k + row - K;
+        uint64_t* slot = part_slot(p, b, j, c);
+        const uint64_t v = slot_wait(slot);
+        if (v == 0u) {
+          expired = true;
+          continue;
+        }
+        slot_store(slot, 0u);
+        if (GREEDY) {
+          if (slot_f(v) > -INFINITY)
+            merge_argmax(a[i], ia[i], slot_f(v), static_cast<int>(slot_w(v)));
+        } else {
+          merge_stats(a[i], s[i], slot_f(v), __uint_as_float(slot_w(v)), cf);
+        }
+      }
+    }
+  }
+  if (expired) atomicOr(bad, 1);
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int row = wave + i * kWaves;
+    if (GREEDY)
+      wave_merge_argmax(a[i], ia[i]);
+    else
+      wave_merge_stats(a[i], s[i], cf);
+    if (lane == 0 && row < nrows) {
+      const bool finite_max = a[i] > -INFINITY && a[i] < INFINITY;
+      if (GREEDY) {
+        if (!finite_max) atomicOr(bad, 1);
+        sh_ls[row] = __int_as_float(ia[i]);
+      } else {
+        if (!finite_max || !(s[i] < INFINITY)) atomicOr(bad, 1);
+        sh_m[row] = a[i];
+        sh_ls[row] = fast_log2(s[i]);
+      }
+    }
+  }
+}
+
+template <bool BF16>
+__device__ void finish_sampled(const Params& p, int b) {
+  const Req r = load_req(p, b);
+  if (!r.sampled()) return;
+  const int tid = threadIdx.x;
+  const int K = r.K;
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  const int64_t drow0 = r.off0;
+  const float cf = kLog2e / r.T;
+
+  __shared__ int sh_bad;
+  __shared__ float sh_m[kRowsMax];
+  __shared__ float sh_ls[kRowsMax];
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  int32_t x = 0;
+  if (tid < K) {
+    x = p.tokens[r.off0 + tid];
+    if (x < 0 || x >= p.V) atomicOr(&sh_bad, 1);
+  }
+  fold_partials<false>(p, b, K, cf, 2 * K + 1, sh_m, sh_ls, &sh_bad);
+  __syncthreads();
+
+  uint64_t* pub = p.pub + 4 * static_cast<int64_t>(b);
+  if (sh_bad) {
+    write_fault(p, b, r);
+    if (tid == 0) slot_store(pub + 3, pack_slot(1.f, kStatusFault));
+    return;
+  }
+  // ratio test r_t * q_t(x_t) < p_t(x_t), left to right (wave 0 holds t < K <= 8)
+  bool reject = false;
+  if (tid < K) {
+    const float zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
+    const float zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
+    const float pp = fast_exp2(scaled_logit(zp, cf, scaled_max(sh_m[tid], cf)) - sh_ls[tid]);
+    const float qq =
+        fast_exp2(scaled_logit(zq, cf, scaled_max(sh_m[K + 1 + tid], cf)) - sh_ls[K + 1 + tid]);
+    const float u = uniform_open01(philox4x32_10(0u, tid, b, 1u, p.k0, p.k1).w[0]);
+    reject = !(u * qq < pp);
+    if (p.p_at) p.p_at[drow0 + tid] = pp;
+    if (p.q_at) p.q_at[drow0 + tid] = qq;
+  }
+  const uint64_t mask = __ballot(reject);
+  if (tid == 0) {
+    const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
+    const float mcq = n < K ? scaled_max(sh_m[K + 1 + n], cf) : 0.f;
+    const float lsq = n < K ? sh_ls[K + 1 + n] : 0.f;
+    slot_store(pub + 0, pack_slot(scaled_max(sh_m[n], cf), __float_as_uint(sh_ls[n])));
+    slot_store(pub + 1, pack_slot(mcq, __float_as_uint(lsq)));
+    slot_store(pub + 2, pack_slot(cf, static_cast<uint32_t>(n)));
+    drain_memory();
+    slot_store(pub + 3, pack_slot(1.f, kStatusOk));
+  }
+}
+
+__device__ void finish_greedy(const Params& p, int b) {
+  const Req r = load_req(p, b);
+  const int tid = threadIdx.x;
+  if (!r.slice_ok) {
+    if (tid == 0) p.accept_len[b] = -1;
+    return;
+  }
+  if (!r.temp_ok) {
+    write_fault(p, b, r);
+    return;
+  }
+  if (!r.greedy) return;
+  const int K = r.K;
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  __shared__ int sh_bad;
+  __shared__ float sh_ls[kRowsMax];
+  __shared__ int sh_n;
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  int32_t x = 0;
+  if (tid < K) {
+    x = p.tokens[r.off0 + tid];
+    if (x < 0 || x >= p.V) atomicOr(&sh_bad, 1);
+  }
+  fold_partials<true>(p, b, K, 0.f, K + 1, nullptr, sh_ls, &sh_bad);
+  __syncthreads();
+  if (sh_bad) {
+    write_fault(p, b, r);
+    return;
+  }
+  // first t < K whose draft differs from the argmax; the stop token is argmax row n
+  const bool mismatch = tid < K && __float_as_int(sh_ls[tid]) != x;
+  const uint64_t mask = __ballot(mismatch);
+  if (tid == 0) sh_n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
+  __syncthreads();
+  const int n = sh_n;
+  if (tid <= K) {
+    const int32_t y = __float_as_int(sh_ls[n]);
+    p.out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? y : -1);
+  }
+  if (tid < K) {
+    if (p.p_at) p.p_at[r.off0 + tid] = NAN;
+    if (p.q_at) p.q_at[r.off0 + tid] = NAN;
+  }
+  if (tid == 0) p.accept_len[b] = n;
+}
+
+// ------------------------------------------------------------------ race jobs
 
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend, float out[4]) {
@@ -653,22 +659,39 @@ __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend,
   }
 }
 
+struct RaceRow {
+  float mcp, lsp, mcq, lsq, cf;
+  int n;
+};
+
+__device__ __forceinline__ RaceRow read_published(const uint64_t* pub) {
+  RaceRow rr;
+  const uint64_t w0 = slot_load(pub + 0), w1 = slot_load(pub + 1), w2 = slot_load(pub + 2);
+  rr.mcp = slot_f(w0);
+  rr.lsp = __uint_as_float(slot_w(w0));
+  rr.mcq = slot_f(w1);
+  rr.lsq = __uint_as_float(slot_w(w1));
+  rr.cf = slot_f(w2);
+  rr.n = static_cast<int>(slot_w(w2));
+  return rr;
+}
+
 // Race candidates of tokens 4g..4g+3 folded into this thread's best
 // (bw / be, bidx); tokens arrive in increasing order, so a strict > keeps the
 // lowest index on ties.
 __device__ __forceinline__ void race_group(const float zp[4], const float zq[4], bool residual,
-                                           const Published& pub, int64_t g, int64_t v_end,
+                                           const RaceRow& rr, int64_t g, int64_t v_end,
                                            uint32_t b, uint32_t k0, uint32_t k1, float& bw,
                                            float& be, int& bidx) {
-  const Philox4 r = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(pub.n), b, 0u,
+  const Philox4 r = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(rr.n), b, 0u,
                                   k0, k1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t v = g * 4 + k;
     if (v >= v_end) break;
     const float e = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
-    float w = fast_exp2(scaled_logit(zp[k], pub.cf, pub.mcp) - pub.lsp);
-    if (residual) w -= fast_exp2(scaled_logit(zq[k], pub.cf, pub.mcq) - pub.lsq);
+    float w = fast_exp2(scaled_logit(zp[k], rr.cf, rr.mcp) - rr.lsp);
+    if (residual) w -= fast_exp2(scaled_logit(zq[k], rr.cf, rr.mcq) - rr.lsq);
     if (w * be > bw * e) {
       bw = w;
       be = e;
@@ -683,143 +706,142 @@ __device__ __forceinline__ float race_key(float bw, float be, int bidx) {
 }
 
 template <bool BF16, bool VEC>
-__device__ void race_slot(const Params& p, int b, int c) {
-  const int tid = threadIdx.x;
+__device__ void race_chunk(const Params& p, int b, int c) {
   const Req r = load_req(p, b);
-  if (!r.slice_ok) {
-    if (c == 0 && tid == 0) p.accept_len[b] = -1;
-    return;
-  }
-  if (!r.temp_ok) {
-    if (c == 0) write_fault(p, b, r);
-    return;
-  }
-  if (r.greedy) return;  // finished by its row-statistics finisher
-
-  Counters& cn = counters(p, b);
-  __shared__ int sh_flag;
-  if (tid == 0) {
-    unsigned it = 0;
-    while (load_coherent_u32(&cn.ready) == 0u) {
-      if (++it > kSpinLimit) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-    sh_flag = (it > kSpinLimit) ? 1 : 0;
-  }
+  if (!r.sampled()) return;
+  const int tid = threadIdx.x;
+  const uint64_t* pub = p.pub + 4 * static_cast<int64_t>(b);
+  __shared__ uint32_t sh_status;
+  if (tid == 0) sh_status = slot_w(slot_wait(pub + 3));  // 0 if the wait expired
   __syncthreads();
-  if (sh_flag) {
-    if (c == 0 && tid == 0) p.accept_len[b] = -1;
+  uint64_t* out = p.race_part + static_cast<int64_t>(b) * p.nc2 + c;
+  if (sh_status != kStatusOk) {
+    if (tid == 0) slot_store(out, pack_slot(-INFINITY, INT_MAX));
     return;
   }
-  const Published pub = read_published(p.pub + b);
-  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
-  const int64_t drow0 = r.off0;
+  const RaceRow rr = read_published(pub);
   const int64_t esz = BF16 ? 2 : 4;
-  const void* prow = static_cast<const char*>(p.target) + (trow0 + pub.n) * p.V * esz;
-  const bool residual = pub.n < r.K;
-  const void* qrow =
-      residual ? static_cast<const char*>(p.draft) + (drow0 + pub.n) * p.V * esz : nullptr;
-
+  const bool residual = rr.n < r.K;
+  const void* prow =
+      static_cast<const char*>(p.target) + (static_cast<int64_t>(r.off0) + b + rr.n) * p.V * esz;
+  const void* qrow = residual ? static_cast<const char*>(p.draft) +
+                                    (static_cast<int64_t>(r.off0) + rr.n) * p.V * esz
+                              : nullptr;
+  const int64_t v_begin = static_cast<int64_t>(c) * kRaceChunk;
+  const int64_t v_end = (v_begin + kRaceChunk < p.V) ? v_begin + kRaceChunk : p.V;
+  float zp[kRaceGroups][4], zq[kRaceGroups][4];
+#pragma unroll
+  for (int gi = 0; gi < kRaceGroups; ++gi) {  // issue every load before any math
+    const int64_t g = v_begin / 4 + gi * kThreads + tid;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) zq[gi][k] = 0.f;
+    if (g * 4 < v_end) {
+      load4<BF16, VEC>(prow, g * 4, v_end, zp[gi]);
+      if (residual) load4<BF16, VEC>(qrow, g * 4, v_end, zq[gi]);
+    }
+  }
+  float bw = 0.f, be = 1.f;  // any w > 0 beats the empty candidate
+  int idx = INT_MAX;
+#pragma unroll
+  for (int gi = 0; gi < kRaceGroups; ++gi) {
+    const int64_t g = v_begin / 4 + gi * kThreads + tid;
+    if (g * 4 < v_end)
+      race_group(zp[gi], zq[gi], residual, rr, g, v_end, b, p.k0, p.k1, bw, be, idx);
+  }
+  float key = race_key(bw, be, idx);
   __shared__ float sh_key[kWaves];
   __shared__ int sh_idx[kWaves];
+  block_argmax(key, idx, sh_key, sh_idx);
+  if (tid == 0) slot_store(out, pack_slot(key, static_cast<uint32_t>(idx)));
+}
+
+template <bool BF16, bool VEC>
+__device__ void race_finish(const Params& p, int b) {
+  const Req r = load_req(p, b);
+  if (!r.sampled()) return;
+  const int tid = threadIdx.x;
+  __shared__ float sh_key[kWaves];
+  __shared__ int sh_idx[kWaves];
+  __shared__ int sh_expired;
+  if (tid == 0) sh_expired = 0;
+  __syncthreads();
   float key = -INFINITY;
   int idx = INT_MAX;
-  if (pub.status == kStatusOk) {
-    float bw = 0.f, be = 1.f;  // any w > 0 beats the empty candidate
-    const int64_t v_begin = static_cast<int64_t>(c) * kRaceChunk;
-    const int64_t v_end = (v_begin + kRaceChunk < p.V) ? v_begin + kRaceChunk : p.V;
-    float zp[kRaceGroups][4], zq[kRaceGroups][4];
-#pragma unroll
-    for (int gi = 0; gi < kRaceGroups; ++gi) {  // issue every load before any math
-      const int64_t g = v_begin / 4 + gi * kThreads + tid;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) zq[gi][k] = 0.f;
-      if (g * 4 < v_end) {
-        load4<BF16, VEC>(prow, g * 4, v_end, zp[gi]);
-        if (residual) load4<BF16, VEC>(qrow, g * 4, v_end, zq[gi]);
-      }
+  for (int i = tid; i < p.nc2; i += kThreads) {
+    uint64_t* slot = p.race_part + static_cast<int64_t>(b) * p.nc2 + i;
+    const uint64_t v = slot_wait(slot);
+    if (v == 0u) {
+      atomicOr(&sh_expired, 1);
+      continue;
     }
-#pragma unroll
-    for (int gi = 0; gi < kRaceGroups; ++gi) {
-      const int64_t g = v_begin / 4 + gi * kThreads + tid;
-      if (g * 4 < v_end)
-        race_group(zp[gi], zq[gi], residual, pub, g, v_end, b, p.k0, p.k1, bw, be, idx);
+    slot_store(slot, 0u);
+    merge_argmax(key, idx, slot_f(v), static_cast<int>(slot_w(v)));
+  }
+  block_argmax(key, idx, sh_key, sh_idx);  // its barriers also publish sh_expired
+  uint64_t* pub = p.pub + 4 * static_cast<int64_t>(b);
+  const uint32_t status = slot_w(slot_load(pub + 3));
+  const RaceRow rr = read_published(pub);
+  __syncthreads();  // every thread has read the record before it is cleared
+  if (tid < 4) slot_store(pub + tid, 0u);
+  if (sh_expired || status == 0u) {
+    if (tid == 0) p.accept_len[b] = -1;
+    return;
+  }
+  if (status != kStatusOk) return;  // the finisher wrote the failure
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  if (idx == INT_MAX) {
+    // no token had p > q (rounding can only cause this when p == q): race on p_n
+    const int64_t esz = BF16 ? 2 : 4;
+    const void* prow = static_cast<const char*>(p.target) + (trow0 + rr.n) * p.V * esz;
+    float bw = 0.f, be = 1.f;
+    for (int64_t g = tid; g * 4 < p.V; g += kThreads) {
+      float zp[4];
+      const float zq[4] = {0.f, 0.f, 0.f, 0.f};
+      load4<BF16, VEC>(prow, g * 4, p.V, zp);
+      race_group(zp, zq, false, rr, g, p.V, b, p.k0, p.k1, bw, be, idx);
     }
     key = race_key(bw, be, idx);
     block_argmax(key, idx, sh_key, sh_idx);
   }
-
-  __shared__ int sh_last;
-  if (tid == 0) {
-    if (pub.status == kStatusOk) {
-      store_coherent(p.race_part + static_cast<int64_t>(b) * p.nc2 + c,
-                     make_float2(key, __int_as_float(idx)));
-      drain_memory();
-    }
-    sh_last = (count_one(&cn.race_done) + 1 == static_cast<uint32_t>(p.nc2)) ? 1 : 0;
+  const int n = rr.n;
+  if (tid <= r.K) {
+    const int32_t xt = (tid < n) ? p.tokens[r.off0 + tid] : 0;
+    p.out_tokens[trow0 + tid] = (tid < n) ? xt : (tid == n ? idx : -1);
   }
-  __syncthreads();
-  if (!sh_last) return;
-
-  if (pub.status == kStatusOk) {
-    key = -INFINITY;
-    idx = INT_MAX;
-    for (int i = tid; i < p.nc2; i += kThreads) {
-      const float2 w = load_coherent(p.race_part + static_cast<int64_t>(b) * p.nc2 + i);
-      merge_argmax(key, idx, w.x, __float_as_int(w.y));
-    }
-    block_argmax(key, idx, sh_key, sh_idx);
-    if (idx == INT_MAX) {
-      // no token had p > q (rounding can only cause this when p == q): race on p_n
-      float bw = 0.f, be = 1.f;
-      for (int64_t g = tid; g * 4 < p.V; g += kThreads) {
-        float zp[4];
-        const float zq[4] = {0.f, 0.f, 0.f, 0.f};
-        load4<BF16, VEC>(prow, g * 4, p.V, zp);
-        race_group(zp, zq, false, pub, g, p.V, b, p.k0, p.k1, bw, be, idx);
-      }
-      key = race_key(bw, be, idx);
-      block_argmax(key, idx, sh_key, sh_idx);
-    }
-    const int n = pub.n;
-    if (tid <= r.K) {
-      const int32_t xt = (tid < n) ? p.tokens[r.off0 + tid] : 0;
-      p.out_tokens[trow0 + tid] = (tid < n) ? xt : (tid == n ? idx : -1);
-    }
-    if (tid == 0) p.accept_len[b] = n;
-  }
-  if (tid == 0) {
-    store_coherent_u32(&cn.ready, 0u);
-    store_coherent_u32(&cn.race_done, 0u);
-  }
+  if (tid == 0) p.accept_len[b] = n;
 }
 
 // ------------------------------------------------------------------ kernel
 
-// Grid order (S statistics slots per request, nc2 race slots per request,
-// d = min(lag, B)):
-//   [stats 0] .. [stats d-1]
-//   [stats d][race 0] [stats d+1][race 1] .. [stats B-1][race B-1-d]
-//   [race B-d] .. [race B-1]
-// so every race slot comes after all statistics slots of its request.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
   const int64_t g = blockIdx.x;
-  const int64_t d = p.lag < p.B ? p.lag : p.B;
-  const int64_t head = d * p.S;
-  const int64_t seg = p.S + p.nc2;
-  const int64_t body = head + (p.B - d) * seg;
-  if (g < head) {
-    stats_slot<BF16, VEC>(p, static_cast<int>(g / p.S), static_cast<int>(g % p.S));
-  } else if (g < body) {
-    const int64_t k = (g - head) / seg, o = (g - head) % seg;
-    if (o < p.S)
-      stats_slot<BF16, VEC>(p, static_cast<int>(d + k), static_cast<int>(o));
-    else
-      race_slot<BF16, VEC>(p, static_cast<int>(k), static_cast<int>(o - p.S));
-  } else {
-    const int64_t h = g - body;
-    race_slot<BF16, VEC>(p, static_cast<int>(p.B - d + h / p.nc2), static_cast<int>(h % p.nc2));
+  int ri = 0;
+  while (ri + 1 < p.n_regions && g >= p.reg[ri + 1].g0) ++ri;
+  const Region& R = p.reg[ri];
+  const int64_t rel = g - R.g0;
+  const int k = R.k0 + static_cast<int>(rel / R.seg);
+  int o = static_cast<int>(rel % R.seg);
+  for (int job = 0; job < kJobs; ++job) {
+    if (!(R.mask & (1 << job))) continue;
+    if (o >= p.job_len[job]) {
+      o -= p.job_len[job];
+      continue;
+    }
+    const int b = k - p.job_off[job];
+    switch (job) {
+      case kSA: stats_job<BF16, VEC>(p, b, o, true); break;
+      case kFA: finish_sampled<BF16>(p, b); break;
+      case kR:
+        if (o < p.nc2)
+          race_chunk<BF16, VEC>(p, b, o);
+        else
+          race_finish<BF16, VEC>(p, b);
+        break;
+      case kSB: stats_job<BF16, VEC>(p, b, o, false); break;
+      default: finish_greedy(p, b); break;
+    }
+    return;
   }
 }
 
@@ -830,6 +852,58 @@ bool shape_ok(int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Lays the jobs out in time steps (see the schedule at the top); returns the
+// grid size, or -1 if it does not fit the region table.
+int64_t build_schedule(Params& prm, int B, bool all_greedy) {
+  const int J = 2 * prm.max_k + 1;
+  const int len[kJobs] = {all_greedy ? 0 : J * prm.nc1, all_greedy ? 0 : 1,
+                          all_greedy ? 0 : prm.nc2 + 1, (prm.max_k + 1) * prm.nc1, 1};
+  const int seg_a = len[kSA] + len[kFA] + len[kR];
+  const int seg_b = len[kSB] + len[kFB];
+  const int d1 = all_greedy ? 0
+                            : static_cast<int>(std::min<int64_t>(
+                                  B, ceil_div(SV_FINISH_LAG_SLOTS, std::max(seg_a, 1))));
+  const int d2 = all_greedy ? 0
+                            : static_cast<int>(std::min<int64_t>(
+                                  B, ceil_div(SV_RACE_LAG_SLOTS, std::max(seg_a, 1))));
+  const int gb = all_greedy ? 0 : B;  // greedy statistics start after the sampled ones
+  const int db = static_cast<int>(
+      std::min<int64_t>(B, ceil_div(SV_FINISH_LAG_SLOTS, std::max(seg_b, 1))));
+  const int off[kJobs] = {0, d1, std::max(d2, d1), gb, gb + db};
+  int bounds[2 * kJobs];
+  int nb = 0;
+  for (int j = 0; j < kJobs; ++j) {
+    prm.job_len[j] = len[j];
+    prm.job_off[j] = off[j];
+    if (len[j] == 0) continue;
+    bounds[nb++] = off[j];
+    bounds[nb++] = off[j] + B;
+  }
+  std::sort(bounds, bounds + nb);
+  nb = static_cast<int>(std::unique(bounds, bounds + nb) - bounds);
+  int64_t g = 0;
+  prm.n_regions = 0;
+  for (int i = 0; i + 1 < nb; ++i) {
+    const int ka = bounds[i], kb = bounds[i + 1];
+    int mask = 0, seg = 0;
+    for (int j = 0; j < kJobs; ++j)
+      if (len[j] > 0 && off[j] <= ka && ka < off[j] + B) {
+        mask |= 1 << j;
+        seg += len[j];
+      }
+    if (seg == 0) continue;
+    if (prm.n_regions == kMaxRegions) return -1;
+    Region& R = prm.reg[prm.n_regions++];
+    R.g0 = g;
+    R.k0 = ka;
+    R.seg = seg;
+    R.mask = mask;
+    R.pad = 0;
+    g += static_cast<int64_t>(kb - ka) * seg;
+  }
+  return g;
+}
 
 template <bool BF16, bool VEC>
 int launch(const Params& prm, int64_t grid, hipStream_t stream, void* ev0, void* ev1) {
@@ -871,21 +945,16 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.max_k = max_k;
   prm.n_draft_rows = n_draft_rows;
   prm.nc1 = L.nc1;
-  prm.nc2 = all_greedy ? 0 : L.nc2;
-  prm.S = static_cast<int64_t>(L.J) * L.nc1;
-  prm.lag = all_greedy ? B : ceil_div(SV_RACE_LAG_SLOTS, prm.S);
-  prm.part = reinterpret_cast<float2*>(ws + L.stats_off);
-  prm.race_part = reinterpret_cast<float2*>(ws + L.race_off);
-  prm.pub = reinterpret_cast<Published*>(ws + L.pub_off);
-  const uintptr_t end = (reinterpret_cast<uintptr_t>(ws) + workspace_bytes) & ~uintptr_t{15};
-  prm.cnt_end = reinterpret_cast<Counters*>(end);
-  if (reinterpret_cast<char*>(prm.cnt_end - B) < ws + L.data_end) return SV_ERR_WORKSPACE;
+  prm.nc2 = L.nc2;
+  prm.part = reinterpret_cast<uint64_t*>(ws + L.stats_off);
+  prm.race_part = reinterpret_cast<uint64_t*>(ws + L.race_off);
+  prm.pub = reinterpret_cast<uint64_t*>(ws + L.pub_off);
   prm.accept_len = accept_len;
   prm.out_tokens = out_tokens;
   prm.p_at = p_at;
   prm.q_at = q_at;
-  const int64_t grid = static_cast<int64_t>(B) * (prm.S + prm.nc2);
-  if (grid > INT32_MAX) return SV_ERR_SHAPE;
+  const int64_t grid = build_schedule(prm, B, all_greedy);
+  if (grid <= 0 || grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 && aligned16(target) && (!draft || aligned16(draft));
   hipStream_t s = static_cast<hipStream_t>(stream);
