@@ -2,47 +2,54 @@
 //
 // What is computed is stated in include/spec_verify.h (the accept / residual /
 // bonus rule of "Decodificación Especulativa y EAGLE", section "La Regla de
-// Exactitud", and its greedy case).  How it runs on MI355X: one launch whose
-// workgroups each take one job from a fixed schedule.
+// Exactitud", and its greedy case).  How it runs on MI355X: one launch of
+// persistent workgroups that take work items from per-list ticket counters.
 //
-// Jobs of request b:
-//   SA  statistics of a sampled request: one job per (row, 64 KiB V-chunk) of
+// Work items of request b:
+//   SA  statistics of a sampled request: one item per (row, 64 KiB V-chunk) of
 //       its K+1 target and K draft rows.  Streams the chunk with 16-byte
 //       loads and reduces it to one 8-byte partial (max, sum of
-//       2^(z c - fl(max c))), c = log2(e) / T, then stores it and exits.
-//   FA  finisher of a sampled request: collects the partials, folds them into
-//       per-row (max, log2 sum), gathers p_t(x_t) and q_t(x_t), draws r_t,
-//       finds the first rejection n with a wave ballot, and publishes n with
-//       the statistics of row n.
-//   R   race of a sampled request: one job per 4096-token chunk of row n, the
-//       exponential race over the residual (p_n - q_n)+ after a rejection or
-//       over p_K otherwise, plus one job that folds the chunk winners and
-//       writes the outputs.
-//   SB  statistics of a greedy request: (max, lowest argmax index) per chunk
+//       2^(z c - fl(max c))), c = log2(e) / T.
+//   SG  statistics of a greedy request: (max, lowest argmax index) per chunk
 //       of its K+1 target rows (draft rows are never read).
-//   FB  finisher of a greedy request: first draft that differs from the row
-//       argmax; writes the outputs.  Also reports requests with a bad slice
-//       or temperature.
-// A job that does not apply to request b (e.g. SA of a greedy request) exits
-// at once.
+//   FA  finisher of a sampled request: folds the partials into per-row
+//       (max, log2 sum), gathers p_t(x_t) and q_t(x_t), draws r_t, finds the
+//       first rejection n with a wave ballot, and publishes n with the
+//       statistics of row n.
+//   R   race of a sampled request: one item per 4096-token chunk of row n, the
+//       exponential race over the residual (p_n - q_n)+ after a rejection or
+//       over p_K otherwise, plus one item that folds the chunk winners and
+//       writes the outputs.
+//   FG  finisher of a greedy request: first draft that differs from the row
+//       argmax; writes the outputs.  Also reports a request whose slice or
+//       temperature is invalid.
 //
-// Schedule: request b's SA jobs sit at "time" b, FA at b + d1, R at b + d2,
-// SB at B + b and FB at B + b + d1; the grid lists times in order and, inside
-// a time, the jobs in the order SA, FA, R, SB, FB.  So every job comes after
-// the jobs it depends on, sampled requests stream first, and their finishing
-// and races overlap the streaming of greedy requests and of later sampled
-// requests.
+// Work lists: request b belongs to list b mod 8, served by the workgroups with
+// blockIdx mod 8 equal to the list (on MI355X those sit on one XCD, so a
+// request's hand-offs stay in one L2, though nothing relies on that).  Every
+// workgroup of a list builds the same plan in LDS from the requests' offsets
+// and temperatures: the list's items laid out by "time step" -- SA of the
+// list's i-th request at step i, SG at step nloc + i (after every sampled
+// request), FA at i + d1, R at i + d1 + d2, FG at the SG step + d3, and inside
+// a step the order SA, SG, FA, R, FG.  The lags (about two generations of the
+// list's workgroups) put consumers well after their producers, so finishing
+// and races overlap the streaming of other rows.  A workgroup draws tickets
+// from the list's counter and processes item ticket by ticket.
+//
+// Forward progress needs no assumption about dispatch or residency: an item
+// only waits for items of the same list with smaller tickets, and a ticket is
+// only handed out to a running workgroup, so by induction on the ticket every
+// wait ends.  Waits are also bounded (kSpinLimit polls); an expired wait
+// reports accept_len = -1.
 //
 // Hand-offs between workgroups use 8-byte slots in the workspace that are
 // all-zero until written (a written slot never has all-zero bits: +0.0 is
-// stored as -0.0).  Producers store with a device-coherent (sc1) store and
-// exit; consumers poll with device-coherent loads, then write the slot back
-// to zero, so the workspace is all-zero again after every call.  No
-// agent-scope release/acquire fence is used (on gfx950 those write back or
-// invalidate the XCD's whole L2).  A consumer only waits for jobs that come
-// earlier in the grid; the earliest waiting job waits only for jobs that
-// never wait, so with in-order dispatch every wait ends.  Waits are also
-// bounded (kSpinLimit polls); an expired wait reports accept_len = -1.
+// stored as -0.0).  Producers store with a device-coherent (sc1) store;
+// consumers poll with device-coherent loads, then write the slot back to
+// zero.  No agent-scope release/acquire fence is used (on gfx950 those write
+// back or invalidate the XCD's whole L2).  The last workgroup of a list to
+// exit resets the list's counters, so the workspace is all-zero again after
+// every call.
 //
 // Race keys: the winner maximises ln w_v - ln E_v, i.e. w_v / E_v.  Inside a
 // thread candidates are compared by cross-multiplication (w_a e_b > w_b e_a)
@@ -71,12 +78,10 @@ constexpr int kRowsMax = 2 * SV_KMAX + 1;               // row slots per request
 constexpr int kRowsPerWave = (kRowsMax + kWaves - 1) / kWaves;
 constexpr unsigned kSpinLimit = 1u << 16;
 constexpr float kLog2e = 1.4426950408889634f;
-#ifndef SV_FINISH_LAG_SLOTS
-#define SV_FINISH_LAG_SLOTS 1024  // grid slots between a request's statistics and its finisher
-#endif
-#ifndef SV_RACE_LAG_SLOTS
-#define SV_RACE_LAG_SLOTS 2048  // grid slots between a request's statistics and its race
-#endif
+constexpr int kLists = 8;                       // work lists (one per XCD on MI355X)
+constexpr int kMaxLocal = 512;                  // requests per list and launch
+constexpr int kMaxSteps = 4 * kMaxLocal;        // time steps a list's plan can span
+constexpr int kCounterStride = 16;              // 64-byte lines between counters
 
 __host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
 __host__ __device__ constexpr int stats_chunk(bool bf16) {
@@ -84,6 +89,15 @@ __host__ __device__ constexpr int stats_chunk(bool bf16) {
 }
 
 // ------------------------------------------------------------------ helpers
+
+// threadIdx.x behind an empty asm: work items run in a loop, and without this
+// the compiler hoists every per-thread address offset of every item kind out
+// of the loop, where they stay live and triple the register footprint.
+__device__ __forceinline__ int item_tid() {
+  int t = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -179,7 +193,7 @@ __device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
 // All threads end with the workgroup's (key, idx) winner.
 __device__ __forceinline__ void block_argmax(float& key, int& idx, float* sh_k, int* sh_i) {
   wave_merge_argmax(key, idx);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   __syncthreads();
   if (lane == 0) {
     sh_k[wave] = key;
@@ -238,7 +252,7 @@ struct Layout {
   int J;    // row slots per request: target 0..max_k, then draft 0..max_k-1
   int nc1;  // statistics chunks per row
   int nc2;  // race chunks per row
-  size_t stats_off, race_off, pub_off, total;
+  size_t count_off, stats_off, race_off, pub_off, total;
 };
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -250,28 +264,16 @@ Layout make_layout(int32_t B, int32_t V, int32_t max_k, bool bf16) {
   L.J = 2 * max_k + 1;
   L.nc1 = static_cast<int>(ceil_div(V, stats_chunk(bf16)));
   L.nc2 = static_cast<int>(ceil_div(V, kRaceChunk));
-  L.stats_off = 0;
+  L.count_off = 0;  // tickets [kLists] then exits [kLists], one 64-byte line each
+  L.stats_off = round256(2 * kLists * kCounterStride * sizeof(uint32_t));
   // sized with the float32 chunk (the smaller one) so either dtype fits
   const size_t stats_bytes =
       static_cast<size_t>(B) * L.J * ceil_div(V, stats_chunk(false)) * sizeof(uint64_t);
-  L.race_off = round256(stats_bytes);
+  L.race_off = L.stats_off + round256(stats_bytes);
   L.pub_off = L.race_off + round256(static_cast<size_t>(B) * L.nc2 * sizeof(uint64_t));
   L.total = L.pub_off + round256(static_cast<size_t>(B) * 4 * sizeof(uint64_t));
   return L;
 }
-
-// Jobs in schedule order inside one time step.
-enum Job : int { kSA = 0, kFA = 1, kR = 2, kSB = 3, kFB = 4, kJobs = 5 };
-
-// A run of time steps with the same set of jobs present.
-struct Region {
-  int64_t g0;    // first grid slot
-  int32_t k0;    // first time step
-  int32_t seg;   // slots per time step
-  int32_t mask;  // jobs present (bit per Job)
-  int32_t pad;
-};
-constexpr int kMaxRegions = 12;
 
 struct Params {
   const void* target;
@@ -280,22 +282,20 @@ struct Params {
   const int32_t* tokens;
   const float* temperature;  // NULL: every request greedy
   uint32_t k0, k1;           // Philox key
-  int32_t B, V, max_k, n_draft_rows, nc1, nc2;
-  uint64_t* part;       // [B][J][nc1] statistics partials
-  uint64_t* race_part;  // [B][nc2] race chunk winners
-  uint64_t* pub;        // [B][4] published record: (fl(m c), log2 sum) of target row n,
-                        // the same of draft row n, (c, n), (1, status) -- last written
+  int32_t b_begin, b_end;    // requests of this launch
+  int32_t V, max_k, n_draft_rows, nc1, nc2, grid;
+  uint32_t* counters;        // tickets [kLists], exits [kLists] (stride kCounterStride)
+  uint64_t* part;            // [B][J][nc1] statistics partials
+  uint64_t* race_part;       // [B][nc2] race chunk winners
+  uint64_t* pub;             // [B][4] published record: (fl(m c), log2 sum) of target row n,
+                             // the same of draft row n, (c, n), (1, status) -- last written
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_at;
   float* q_at;
-  int32_t job_len[kJobs];  // slots each job kind takes per request
-  int32_t job_off[kJobs];  // time step of request 0's job
-  int32_t n_regions;
-  Region reg[kMaxRegions];
 };
 
-// Per-request checks every job can make from the request's scalars.
+// A request as the plan records it.
 struct Req {
   int32_t off0, K;
   float T;
@@ -304,21 +304,9 @@ struct Req {
   __device__ bool greedy_ok() const { return slice_ok && temp_ok && greedy; }
 };
 
-__device__ __forceinline__ Req load_req(const Params& p, int b) {
-  Req r;
-  r.off0 = p.offsets[b];
-  const int32_t off1 = p.offsets[b + 1];
-  r.K = off1 - r.off0;
-  r.slice_ok = r.off0 >= 0 && off1 <= p.n_draft_rows && r.K >= 0 && r.K <= p.max_k;
-  r.T = p.temperature ? p.temperature[b] : 0.f;
-  r.greedy = r.T == 0.f;
-  r.temp_ok = (r.T >= 0.f) && (r.T < INFINITY) && (r.greedy || r.K == 0 || p.draft != nullptr);
-  return r;
-}
-
 // Outputs of a failed request (its slice is valid).
 __device__ void write_fault(const Params& p, int b, const Req& r) {
-  const int tid = threadIdx.x;
+  const int tid = item_tid();
   const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
   if (tid <= r.K) p.out_tokens[trow0 + tid] = -1;
   if (tid < r.K) {
@@ -328,34 +316,224 @@ __device__ void write_fault(const Params& p, int b, const Req& r) {
   if (tid == 0) p.accept_len[b] = -1;
 }
 
+// Row r of a request (target rows 0..K, then draft rows 0..K-1) to its slot.
+__device__ __forceinline__ int row_slot(int max_k, int K, int r) {
+  return r <= K ? r : max_k + r - K;
+}
+
 __device__ __forceinline__ uint64_t* part_slot(const Params& p, int b, int j, int c) {
   return p.part + (static_cast<int64_t>(b) * (2 * p.max_k + 1) + j) * p.nc1 + c;
 }
 
-// ------------------------------------------------------------------ statistics jobs
+// ------------------------------------------------------------------ plan
 
-template <bool BF16, bool VEC>
-__device__ void stats_job(const Params& p, int b, int slot, bool sampled_job) {
+enum Kind : int { kSA = 0, kSG = 1, kFA = 2, kR = 3, kFG = 4, kKinds = 5 };
+
+struct Plan {
+  int32_t nloc;              // requests in this list
+  int32_t steps;             // time steps
+  int32_t total;             // items
+  int32_t off[kKinds];       // time step of the list's first request, per kind
+  int32_t off0[kMaxLocal];   // draft_offsets[b]
+  int32_t info[kMaxLocal];   // K | slice_ok << 8 | temp_ok << 9 | greedy << 10
+  float temp[kMaxLocal];
+  int32_t P[kMaxSteps + 1];  // items before each time step
+};
+
+__device__ __forceinline__ Req make_req(int32_t info, int32_t off0, float T) {
+  Req r;
+  r.off0 = off0;
+  r.K = info & 0xff;
+  r.slice_ok = (info >> 8) & 1;
+  r.temp_ok = (info >> 9) & 1;
+  r.greedy = (info >> 10) & 1;
+  r.T = T;
+  return r;
+}
+
+// Request i of the plan, read by one thread.
+__device__ __forceinline__ Req plan_req(const Plan& pl, int i) {
+  return make_req(pl.info[i], pl.off0[i], pl.temp[i]);
+}
+
+// A value every lane of the wave holds, moved to a scalar register.  Plan
+// entries read at a workgroup-uniform index are uniform, but the compiler
+// cannot prove it for LDS loads; without this the item dispatch would be
+// compiled as divergent control flow.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Request i of the plan, i uniform across the workgroup.
+__device__ __forceinline__ Req plan_req_uniform(const Plan& pl, int i) {
+  return make_req(uni(pl.info[i]), uni(pl.off0[i]), uni_f(pl.temp[i]));
+}
+
+__device__ __forceinline__ int kind_len(const Params& p, int kind, const Req& r) {
+  switch (kind) {
+    case kSA: return r.sampled() ? (2 * r.K + 1) * p.nc1 : 0;
+    case kSG: return r.greedy_ok() ? (r.K + 1) * p.nc1 : 0;
+    case kFA: return r.sampled() ? 1 : 0;
+    case kR: return r.sampled() ? p.nc2 + 1 : 0;
+    default: return r.sampled() ? 0 : 1;
+  }
+}
+
+__device__ __forceinline__ int list_workgroups(const Params& p, int list) {
+  return list < p.grid ? (p.grid - list + kLists - 1) / kLists : 0;
+}
+
+// Items of time step k (the request of kind j at step k is k - off[j]).
+__device__ __forceinline__ int step_items(const Params& p, const Plan& pl, int k) {
+  int n = 0;
+  for (int j = 0; j < kKinds; ++j) {
+    const int i = k - pl.off[j];
+    if (i >= 0 && i < pl.nloc) n += kind_len(p, j, plan_req(pl, i));
+  }
+  return n;
+}
+
+// Every workgroup of a list computes the same plan.
+__device__ void build_plan(const Params& p, int list, Plan& pl) {
+  const int tid = threadIdx.x;
+  const int first = p.b_begin + list;
+  const int nloc = first < p.b_end ? (p.b_end - first + kLists - 1) / kLists : 0;
+  int n_s = 0, n_g = 0, sum_s = 0, sum_g = 0;
+  for (int i = tid; i < nloc; i += kThreads) {
+    const int b = first + i * kLists;
+    const int32_t o0 = p.offsets[b], o1 = p.offsets[b + 1];
+    const int64_t K64 = static_cast<int64_t>(o1) - o0;
+    const bool slice_ok = o0 >= 0 && o1 <= p.n_draft_rows && K64 >= 0 && K64 <= p.max_k;
+    const int32_t K = slice_ok ? static_cast<int32_t>(K64) : 0;
+    const float T = p.temperature ? p.temperature[b] : 0.f;
+    const bool greedy = T == 0.f;
+    const bool temp_ok = (T >= 0.f) && (T < INFINITY) && (greedy || K == 0 || p.draft != nullptr);
+    const int Ks = K;
+    pl.off0[i] = o0;
+    pl.info[i] = Ks | (slice_ok << 8) | (temp_ok << 9) | (greedy << 10);
+    pl.temp[i] = T;
+    if (slice_ok && temp_ok) {
+      if (greedy) {
+        ++n_g;
+        sum_g += (Ks + 1) * p.nc1;
+      } else {
+        ++n_s;
+        sum_s += (2 * Ks + 1) * p.nc1;
+      }
+    }
+  }
+  // list totals
+  __shared__ int sh_red[4][kWaves];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    n_s += __shfl_xor(n_s, o, 64);
+    n_g += __shfl_xor(n_g, o, 64);
+    sum_s += __shfl_xor(sum_s, o, 64);
+    sum_g += __shfl_xor(sum_g, o, 64);
+  }
+  if ((tid & 63) == 0) {
+    sh_red[0][tid >> 6] = n_s;
+    sh_red[1][tid >> 6] = n_g;
+    sh_red[2][tid >> 6] = sum_s;
+    sh_red[3][tid >> 6] = sum_g;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int t[4] = {0, 0, 0, 0};
+    for (int q = 0; q < 4; ++q)
+      for (int w = 0; w < kWaves; ++w) t[q] += sh_red[q][w];
+    const int64_t gen = list_workgroups(p, list);  // one generation of this list's workgroups
+    const int64_t avg_s = std::max<int64_t>(1, t[2] / std::max(1, t[0]));
+    const int64_t avg_g = std::max<int64_t>(1, t[3] / std::max(1, t[1]));
+    const int64_t cap = 2 * static_cast<int64_t>(nloc);
+    const int d1 = static_cast<int>(std::max<int64_t>(1, std::min(cap, ceil_div(2 * gen, avg_s))));
+    const int d2 = static_cast<int>(
+        std::max<int64_t>(1, std::min<int64_t>(nloc, ceil_div(gen, avg_s + p.nc2 + 1))));
+    const int d3 = static_cast<int>(std::max<int64_t>(1, std::min(cap, ceil_div(2 * gen, avg_g))));
+    pl.nloc = nloc;
+    pl.off[kSA] = 0;
+    pl.off[kSG] = t[0] > 0 ? nloc : 0;  // greedy statistics after the sampled ones
+    pl.off[kFA] = d1;
+    pl.off[kR] = d1 + d2;
+    pl.off[kFG] = pl.off[kSG] + d3;
+    int steps = 0;
+    for (int j = 0; j < kKinds; ++j) steps = std::max(steps, pl.off[j] + nloc);
+    pl.steps = nloc > 0 ? steps : 0;
+  }
+  __syncthreads();
+  // P[k] = items before step k: per-thread runs of steps, then a block scan
+  const int steps = pl.steps;
+  const int per = (steps + kThreads - 1) / kThreads;
+  const int k0 = tid * per, k1 = std::min(steps, k0 + per);
+  int run = 0;
+  for (int k = k0; k < k1; ++k) run += step_items(p, pl, k);
+  int incl = run;  // inclusive scan of run across the workgroup
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if ((tid & 63) >= o) incl += v;
+  }
+  __shared__ int sh_wave[kWaves];
+  if ((tid & 63) == 63) sh_wave[tid >> 6] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int w = 0; w < (tid >> 6); ++w) base += sh_wave[w];
+  for (int k = k0; k < k1; ++k) {
+    pl.P[k] = base;
+    base += step_items(p, pl, k);
+  }
+  if (tid == kThreads - 1) {
+    pl.P[steps] = base;
+    pl.total = base;
+  }
+  __syncthreads();
+}
+
+// Ticket -> (kind, local request, index inside the request's items of that
+// kind); t is uniform across the workgroup and so are the results.
+__device__ void decode_ticket(const Params& p, const Plan& pl, int t, int& kind, int& i, int& o) {
+  int lo = 0, hi = uni(pl.steps);  // largest k with P[k] <= t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uni(pl.P[mid]) <= t)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  o = t - uni(pl.P[lo]);
+  const int nloc = uni(pl.nloc);
+  for (int j = 0; j < kKinds; ++j) {
+    const int ii = lo - uni(pl.off[j]);
+    if (ii < 0 || ii >= nloc) continue;
+    const int len = kind_len(p, j, plan_req_uniform(pl, ii));
+    if (o < len) {
+      kind = j;
+      i = ii;
+      return;
+    }
+    o -= len;
+  }
+  kind = -1;  // unreachable for t < total
+  i = 0;
+}
+
+// ------------------------------------------------------------------ statistics items
+
+template <bool BF16, bool VEC, bool GREEDY>
+__device__ void stats_item(const Params& p, int b, const Req& r, int row_r, int c) {
   constexpr int EPV = elems_per_vec(BF16);
   constexpr int CHUNK = stats_chunk(BF16);
   constexpr int PAIR = 2 * EPV;  // elements folded per online step
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = slot % p.nc1;
-  const int j = slot / p.nc1;
-
-  const Req r = load_req(p, b);
-  if (sampled_job ? !r.sampled() : !r.greedy_ok()) return;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   const void* base;
   int64_t row;
-  if (j <= p.max_k) {
-    if (j > r.K) return;
+  if (row_r <= r.K) {
     base = p.target;
-    row = static_cast<int64_t>(r.off0) + b + j;
+    row = static_cast<int64_t>(r.off0) + b + row_r;
   } else {
-    const int t = j - p.max_k - 1;
-    if (t >= r.K) return;
     base = p.draft;
-    row = static_cast<int64_t>(r.off0) + t;
+    row = static_cast<int64_t>(r.off0) + row_r - r.K - 1;
   }
   const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
   const int64_t e_end = (e0 + CHUNK < p.V) ? e0 + CHUNK : p.V;
@@ -405,7 +583,7 @@ __device__ void stats_job(const Params& p, int b, int slot, bool sampled_job) {
   __shared__ float sh_a[kWaves];
   __shared__ float sh_b[kWaves];
   uint64_t result = 0;
-  if (r.greedy) {
+  if constexpr (GREEDY) {
     float best = -INFINITY;
     int idx = INT_MAX;
 #pragma unroll
@@ -466,19 +644,18 @@ __device__ void stats_job(const Params& p, int b, int slot, bool sampled_job) {
       result = pack_slot(m, __float_as_uint(s));
     }
   }
-  if (tid == 0) slot_store(part_slot(p, b, j, c), result);
+  if (tid == 0) slot_store(part_slot(p, b, row_slot(p.max_k, r.K, row_r), c), result);
 }
 
 // ------------------------------------------------------------------ finishers
 
-// Waits for the partials of rows 0..nrows-1 (row r: slot j = r for r <= K,
-// j = max_k + r - K for the draft rows), folds them into sh_m / sh_ls and
+// Waits for the partials of rows 0..nrows-1, folds them into sh_m / sh_ls and
 // zeroes the slots.  Greedy: sh_ls holds the argmax index bits.  Sets *bad on
 // a non-finite row, a NaN sum or an expired wait.
 template <bool GREEDY>
 __device__ void fold_partials(const Params& p, int b, int K, float cf, int nrows, float* sh_m,
                               float* sh_ls, int* bad) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   float a[kRowsPerWave], s[kRowsPerWave];
   int ia[kRowsPerWave];
 #pragma unroll
@@ -490,23 +667,31 @@ __device__ void fold_partials(const Params& p, int b, int K, float cf, int nrows
   bool expired = false;
   for (int c0 = 0; c0 < p.nc1; c0 += 64) {
     const int c = c0 + lane;
+    // issue every slot load before waiting on any of them
+    uint64_t v[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int row = wave + i * kWaves;
+      v[i] = (row < nrows && c < p.nc1)
+                 ? slot_load(part_slot(p, b, row_slot(p.max_k, K, row), c))
+                 : 1u;
+    }
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int row = wave + i * kWaves;
       if (row < nrows && c < p.nc1) {
-        const int j = (row <= K) ? row : p.max_k + row - K;
-        uint64_t* slot = part_slot(p, b, j, c);
-        const uint64_t v = slot_wait(slot);
-        if (v == 0u) {
+        uint64_t* slot = part_slot(p, b, row_slot(p.max_k, K, row), c);
+        if (v[i] == 0u) v[i] = slot_wait(slot);
+        if (v[i] == 0u) {
           expired = true;
           continue;
         }
         slot_store(slot, 0u);
         if (GREEDY) {
-          if (slot_f(v) > -INFINITY)
-            merge_argmax(a[i], ia[i], slot_f(v), static_cast<int>(slot_w(v)));
+          if (slot_f(v[i]) > -INFINITY)
+            merge_argmax(a[i], ia[i], slot_f(v[i]), static_cast<int>(slot_w(v[i])));
         } else {
-          merge_stats(a[i], s[i], slot_f(v), __uint_as_float(slot_w(v)), cf);
+          merge_stats(a[i], s[i], slot_f(v[i]), __uint_as_float(slot_w(v[i])), cf);
         }
       }
     }
@@ -534,10 +719,8 @@ __device__ void fold_partials(const Params& p, int b, int K, float cf, int nrows
 }
 
 template <bool BF16>
-__device__ void finish_sampled(const Params& p, int b) {
-  const Req r = load_req(p, b);
-  if (!r.sampled()) return;
-  const int tid = threadIdx.x;
+__device__ void finish_sampled(const Params& p, int b, const Req& r) {
+  const int tid = item_tid();
   const int K = r.K;
   const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
   const int64_t drow0 = r.off0;
@@ -549,9 +732,15 @@ __device__ void finish_sampled(const Params& p, int b) {
   if (tid == 0) sh_bad = 0;
   __syncthreads();
   int32_t x = 0;
+  float zp = 0.f, zq = 0.f;
   if (tid < K) {
     x = p.tokens[r.off0 + tid];
-    if (x < 0 || x >= p.V) atomicOr(&sh_bad, 1);
+    if (x < 0 || x >= p.V) {
+      atomicOr(&sh_bad, 1);
+    } else {  // gathered now, so the loads overlap the wait for the partials
+      zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
+      zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
+    }
   }
   fold_partials<false>(p, b, K, cf, 2 * K + 1, sh_m, sh_ls, &sh_bad);
   __syncthreads();
@@ -565,8 +754,6 @@ __device__ void finish_sampled(const Params& p, int b) {
   // ratio test r_t * q_t(x_t) < p_t(x_t), left to right (wave 0 holds t < K <= 8)
   bool reject = false;
   if (tid < K) {
-    const float zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
-    const float zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
     const float pp = fast_exp2(scaled_logit(zp, cf, scaled_max(sh_m[tid], cf)) - sh_ls[tid]);
     const float qq =
         fast_exp2(scaled_logit(zq, cf, scaled_max(sh_m[K + 1 + tid], cf)) - sh_ls[K + 1 + tid]);
@@ -588,9 +775,9 @@ __device__ void finish_sampled(const Params& p, int b) {
   }
 }
 
-__device__ void finish_greedy(const Params& p, int b) {
-  const Req r = load_req(p, b);
-  const int tid = threadIdx.x;
+// Greedy requests, and requests whose slice or temperature is invalid.
+__device__ void finish_greedy(const Params& p, int b, const Req& r) {
+  const int tid = item_tid();
   if (!r.slice_ok) {
     if (tid == 0) p.accept_len[b] = -1;
     return;
@@ -599,7 +786,6 @@ __device__ void finish_greedy(const Params& p, int b) {
     write_fault(p, b, r);
     return;
   }
-  if (!r.greedy) return;
   const int K = r.K;
   const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
   __shared__ int sh_bad;
@@ -635,7 +821,7 @@ __device__ void finish_greedy(const Params& p, int b) {
   if (tid == 0) p.accept_len[b] = n;
 }
 
-// ------------------------------------------------------------------ race jobs
+// ------------------------------------------------------------------ race items
 
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend, float out[4]) {
@@ -706,10 +892,8 @@ __device__ __forceinline__ float race_key(float bw, float be, int bidx) {
 }
 
 template <bool BF16, bool VEC>
-__device__ void race_chunk(const Params& p, int b, int c) {
-  const Req r = load_req(p, b);
-  if (!r.sampled()) return;
-  const int tid = threadIdx.x;
+__device__ void race_chunk(const Params& p, int b, const Req& r, int c) {
+  const int tid = item_tid();
   const uint64_t* pub = p.pub + 4 * static_cast<int64_t>(b);
   __shared__ uint32_t sh_status;
   if (tid == 0) sh_status = slot_w(slot_wait(pub + 3));  // 0 if the wait expired
@@ -756,10 +940,8 @@ __device__ void race_chunk(const Params& p, int b, int c) {
 }
 
 template <bool BF16, bool VEC>
-__device__ void race_finish(const Params& p, int b) {
-  const Req r = load_req(p, b);
-  if (!r.sampled()) return;
-  const int tid = threadIdx.x;
+__device__ void race_finish(const Params& p, int b, const Req& r) {
+  const int tid = item_tid();
   __shared__ float sh_key[kWaves];
   __shared__ int sh_idx[kWaves];
   __shared__ int sh_expired;
@@ -814,34 +996,53 @@ __device__ void race_finish(const Params& p, int b) {
 // ------------------------------------------------------------------ kernel
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
-  const int64_t g = blockIdx.x;
-  int ri = 0;
-  while (ri + 1 < p.n_regions && g >= p.reg[ri + 1].g0) ++ri;
-  const Region& R = p.reg[ri];
-  const int64_t rel = g - R.g0;
-  const int k = R.k0 + static_cast<int>(rel / R.seg);
-  int o = static_cast<int>(rel % R.seg);
-  for (int job = 0; job < kJobs; ++job) {
-    if (!(R.mask & (1 << job))) continue;
-    if (o >= p.job_len[job]) {
-      o -= p.job_len[job];
-      continue;
-    }
-    const int b = k - p.job_off[job];
-    switch (job) {
-      case kSA: stats_job<BF16, VEC>(p, b, o, true); break;
-      case kFA: finish_sampled<BF16>(p, b); break;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void sv_verify(Params p) {
+  const int tid = threadIdx.x;
+  const int list = blockIdx.x % kLists;
+  uint32_t* ticket = p.counters + list * kCounterStride;
+  uint32_t* exits = p.counters + (kLists + list) * kCounterStride;
+  __shared__ Plan pl;
+  __shared__ uint32_t sh_t;
+  uint32_t next = 0;
+  if (tid == 0) next = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  build_plan(p, list, pl);  // overlaps the first ticket's round trip
+  if (tid == 0) sh_t = next;
+  __syncthreads();
+  const uint32_t total = static_cast<uint32_t>(uni(pl.total));
+  uint32_t t = static_cast<uint32_t>(uni(static_cast<int>(sh_t)));
+  while (t < total) {
+    // take the next ticket now; it is only read after this item
+    if (tid == 0)
+      next = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int kind, i, o;
+    decode_ticket(p, pl, static_cast<int>(t), kind, i, o);
+    const int b = p.b_begin + list + i * kLists;
+    const Req r = plan_req_uniform(pl, i);
+    switch (kind) {
+      case kSA: stats_item<BF16, VEC, false>(p, b, r, o / p.nc1, o % p.nc1); break;
+      case kSG: stats_item<BF16, VEC, true>(p, b, r, o / p.nc1, o % p.nc1); break;
+      case kFA: finish_sampled<BF16>(p, b, r); break;
       case kR:
         if (o < p.nc2)
-          race_chunk<BF16, VEC>(p, b, o);
+          race_chunk<BF16, VEC>(p, b, r, o);
         else
-          race_finish<BF16, VEC>(p, b);
+          race_finish<BF16, VEC>(p, b, r);
         break;
-      case kSB: stats_job<BF16, VEC>(p, b, o, false); break;
-      default: finish_greedy(p, b); break;
+      case kFG: finish_greedy(p, b, r); break;
+      default: break;
     }
-    return;
+    __syncthreads();
+    if (tid == 0) sh_t = next;
+    __syncthreads();
+    t = static_cast<uint32_t>(uni(static_cast<int>(sh_t)));
+  }
+  // the list's last workgroup to leave resets its counters for the next call
+  if (tid == 0) {
+    const uint32_t left = __hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left + 1 == static_cast<uint32_t>(list_workgroups(p, list))) {
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -853,65 +1054,44 @@ bool shape_ok(int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Lays the jobs out in time steps (see the schedule at the top); returns the
-// grid size, or -1 if it does not fit the region table.
-int64_t build_schedule(Params& prm, int B, bool all_greedy) {
-  const int J = 2 * prm.max_k + 1;
-  const int len[kJobs] = {all_greedy ? 0 : J * prm.nc1, all_greedy ? 0 : 1,
-                          all_greedy ? 0 : prm.nc2 + 1, (prm.max_k + 1) * prm.nc1, 1};
-  const int seg_a = len[kSA] + len[kFA] + len[kR];
-  const int seg_b = len[kSB] + len[kFB];
-  const int d1 = all_greedy ? 0
-                            : static_cast<int>(std::min<int64_t>(
-                                  B, ceil_div(SV_FINISH_LAG_SLOTS, std::max(seg_a, 1))));
-  const int d2 = all_greedy ? 0
-                            : static_cast<int>(std::min<int64_t>(
-                                  B, ceil_div(SV_RACE_LAG_SLOTS, std::max(seg_a, 1))));
-  const int gb = all_greedy ? 0 : B;  // greedy statistics start after the sampled ones
-  const int db = static_cast<int>(
-      std::min<int64_t>(B, ceil_div(SV_FINISH_LAG_SLOTS, std::max(seg_b, 1))));
-  const int off[kJobs] = {0, d1, std::max(d2, d1), gb, gb + db};
-  int bounds[2 * kJobs];
-  int nb = 0;
-  for (int j = 0; j < kJobs; ++j) {
-    prm.job_len[j] = len[j];
-    prm.job_off[j] = off[j];
-    if (len[j] == 0) continue;
-    bounds[nb++] = off[j];
-    bounds[nb++] = off[j] + B;
+// Workgroups that fit on the device at once (cached per device and kernel;
+// a property of the device, not of any call).
+template <bool BF16, bool VEC>
+int resident_workgroups() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sv_verify<BF16, VEC>, kThreads, 0) !=
+        hipSuccess)
+      return 0;
+    cache[dev] = std::max(1, cus * per_cu);
   }
-  std::sort(bounds, bounds + nb);
-  nb = static_cast<int>(std::unique(bounds, bounds + nb) - bounds);
-  int64_t g = 0;
-  prm.n_regions = 0;
-  for (int i = 0; i + 1 < nb; ++i) {
-    const int ka = bounds[i], kb = bounds[i + 1];
-    int mask = 0, seg = 0;
-    for (int j = 0; j < kJobs; ++j)
-      if (len[j] > 0 && off[j] <= ka && ka < off[j] + B) {
-        mask |= 1 << j;
-        seg += len[j];
-      }
-    if (seg == 0) continue;
-    if (prm.n_regions == kMaxRegions) return -1;
-    Region& R = prm.reg[prm.n_regions++];
-    R.g0 = g;
-    R.k0 = ka;
-    R.seg = seg;
-    R.mask = mask;
-    R.pad = 0;
-    g += static_cast<int64_t>(kb - ka) * seg;
-  }
-  return g;
+  return cache[dev];
 }
 
 template <bool BF16, bool VEC>
-int launch(const Params& prm, int64_t grid, hipStream_t stream, void* ev0, void* ev1) {
+int launch(Params prm, int32_t B, hipStream_t stream, void* ev0, void* ev1) {
+  const int resident = resident_workgroups<BF16, VEC>();
+  if (resident <= 0) return SV_ERR_LAUNCH;
   if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), stream) != hipSuccess)
     return SV_ERR_LAUNCH;
-  hipLaunchKernelGGL((sv_verify<BF16, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
-                     0, stream, prm);
-  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  // requests go in launches of at most kLists * kMaxLocal
+  for (int32_t b0 = 0; b0 < B; b0 += kLists * kMaxLocal) {
+    prm.b_begin = b0;
+    prm.b_end = std::min<int32_t>(B, b0 + kLists * kMaxLocal);
+    const int64_t nreq = prm.b_end - prm.b_begin;
+    const int64_t items = nreq * ((2 * prm.max_k + 1) * prm.nc1 + prm.nc2 + 3);
+    int64_t grid = std::min<int64_t>(resident, items);
+    grid = std::max<int64_t>(kLists, (grid + kLists - 1) / kLists * kLists);
+    prm.grid = static_cast<int32_t>(grid);
+    hipLaunchKernelGGL((sv_verify<BF16, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
+                       0, stream, prm);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  }
   if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), stream) != hipSuccess)
     return SV_ERR_LAUNCH;
   return SV_OK;
@@ -940,12 +1120,15 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.temperature = all_greedy ? nullptr : temperature;
   prm.k0 = static_cast<uint32_t>(seed);
   prm.k1 = static_cast<uint32_t>(seed >> 32);
-  prm.B = B;
+  prm.b_begin = 0;
+  prm.b_end = B;
   prm.V = V;
   prm.max_k = max_k;
   prm.n_draft_rows = n_draft_rows;
   prm.nc1 = L.nc1;
   prm.nc2 = L.nc2;
+  prm.grid = 0;
+  prm.counters = reinterpret_cast<uint32_t*>(ws + L.count_off);
   prm.part = reinterpret_cast<uint64_t*>(ws + L.stats_off);
   prm.race_part = reinterpret_cast<uint64_t*>(ws + L.race_off);
   prm.pub = reinterpret_cast<uint64_t*>(ws + L.pub_off);
@@ -953,16 +1136,12 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.out_tokens = out_tokens;
   prm.p_at = p_at;
   prm.q_at = q_at;
-  const int64_t grid = build_schedule(prm, B, all_greedy);
-  if (grid <= 0 || grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 && aligned16(target) && (!draft || aligned16(draft));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (bf16)
-    return vec ? launch<true, true>(prm, grid, s, ev0, ev1)
-               : launch<true, false>(prm, grid, s, ev0, ev1);
-  return vec ? launch<false, true>(prm, grid, s, ev0, ev1)
-             : launch<false, false>(prm, grid, s, ev0, ev1);
+    return vec ? launch<true, true>(prm, B, s, ev0, ev1) : launch<true, false>(prm, B, s, ev0, ev1);
+  return vec ? launch<false, true>(prm, B, s, ev0, ev1) : launch<false, false>(prm, B, s, ev0, ev1);
 }
 
 }  // namespace
