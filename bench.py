@@ -10,9 +10,10 @@ Infinity Cache.  Prints one JSON line.
 
 Reported:
   value          verified draft positions per second (sum of K_b per step / time)
-  roofline       the single verify kernel: algorithmic bytes per launch / its
-                 mean duration from HIP events recorded on the launch stream,
-                 against 8 TB/s
+  roofline       the statistics kernel (sv_stats, the pass that streams every
+                 needed logit once; the dominant, HBM-bound kernel): algorithmic
+                 bytes per launch / its mean duration from HIP events recorded on
+                 the launch stream, against 8 TB/s
   cpu_baseline   the float64 oracle on a bounded sample of the same batch
 """
 from __future__ import annotations
@@ -87,7 +88,7 @@ class Hip:
 def traffic_record(workload: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_sv_verify_workload{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_sv_stats_workload{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -171,7 +172,7 @@ def main():
     print(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / args.steps * 1e6:.2f} us/step)",
           file=sys.stderr, flush=True)
 
-    # ---- kernel duration from events the library records around its launch
+    # ---- statistics-kernel duration from events the library records around it
     n_t = min(args.steps, 200)
     evs = [(hip.event(), hip.event()) for _ in range(n_t)]
     timed = lib.spec_verify_sample_timed
@@ -182,7 +183,7 @@ def main():
     torch.cuda.synchronize()
     k_us = 1e3 * sum(hip.elapsed_ms(a, b) for a, b in evs) / n_t
     achieved = alg / (k_us * 1e-6) / 1e9
-    print(f"[bench] sv_verify kernel {k_us:.2f} us (events)", file=sys.stderr, flush=True)
+    print(f"[bench] sv_stats kernel {k_us:.2f} us (events)", file=sys.stderr, flush=True)
 
     # ---- correctness spot check of this exact launch configuration
     call(*argsets[0])
@@ -211,10 +212,10 @@ def main():
         "hbm_frac_step": alg / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg,
         "bytes_per_verified_position": alg / positions,
-        "kernel_us": {"sv_verify": k_us},
+        "kernel_us": {"sv_stats": k_us, "step": ms_per_step * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(args.workload),
-                     "kernel": "sv_verify"},
+                     "kernel": "sv_stats"},
     }
 
     if not args.no_cpu_baseline:
