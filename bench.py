@@ -10,10 +10,9 @@ Infinity Cache.  Prints one JSON line.
 
 Reported:
   value          verified draft positions per second (sum of K_b per step / time)
-  roofline       the statistics kernel (sv_stats, the pass that streams every
-                 needed logit once; the dominant, HBM-bound kernel): algorithmic
-                 bytes per launch / its mean duration from HIP events recorded on
-                 the launch stream, against 8 TB/s
+  roofline       the single verify kernel: algorithmic bytes per launch / its
+                 mean duration from HIP events recorded on the launch stream,
+                 against 8 TB/s
   cpu_baseline   the float64 oracle on a bounded sample of the same batch
 """
 from __future__ import annotations
@@ -45,6 +44,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
+                    help="for hardware-counter runs: after the warmup, run --steps verify "
+                         "calls, then 5 device copies of MIB MiB (the counters' reference "
+                         "kernel of known size), and exit without timing")
     return ap.parse_args()
 
 
@@ -88,7 +91,7 @@ class Hip:
 def traffic_record(workload: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_sv_stats_workload{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_sv_verify_workload{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -104,7 +107,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)",
+              "(the verify step is per request, so several GPUs would each run it on "
+              "their own requests; no multi-GPU layer is part of this library)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -156,6 +160,19 @@ def main():
             raise SystemExit(f"spec_verify_sample returned {rc}")
     torch.cuda.synchronize()
 
+    if args.traffic_probe:
+        for i in range(args.steps):
+            call(*argsets[i % copies])
+        src = torch.ones(args.traffic_probe << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] traffic probe: {args.steps} verify calls, 5 copies of "
+              f"{args.traffic_probe} MiB", file=sys.stderr, flush=True)
+        return
+
     # ---- timed region: exactly `steps` steps, synchronised on both sides
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -172,7 +189,7 @@ def main():
     print(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / args.steps * 1e6:.2f} us/step)",
           file=sys.stderr, flush=True)
 
-    # ---- statistics-kernel duration from events the library records around it
+    # ---- kernel duration from events the library records around its launch
     n_t = min(args.steps, 200)
     evs = [(hip.event(), hip.event()) for _ in range(n_t)]
     timed = lib.spec_verify_sample_timed
@@ -183,7 +200,7 @@ def main():
     torch.cuda.synchronize()
     k_us = 1e3 * sum(hip.elapsed_ms(a, b) for a, b in evs) / n_t
     achieved = alg / (k_us * 1e-6) / 1e9
-    print(f"[bench] sv_stats kernel {k_us:.2f} us (events)", file=sys.stderr, flush=True)
+    print(f"[bench] sv_verify kernel {k_us:.2f} us (events)", file=sys.stderr, flush=True)
 
     # ---- correctness spot check of this exact launch configuration
     call(*argsets[0])
@@ -212,10 +229,10 @@ def main():
         "hbm_frac_step": alg / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg,
         "bytes_per_verified_position": alg / positions,
-        "kernel_us": {"sv_stats": k_us, "step": ms_per_step * 1e3},
+        "kernel_us": {"sv_verify": k_us},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(args.workload),
-                     "kernel": "sv_stats"},
+                     "kernel": "sv_verify"},
     }
 
     if not args.no_cpu_baseline:

@@ -42,20 +42,13 @@
  *
  * Ownership: the caller owns every buffer, the workspace included.  The library
  * allocates nothing, keeps no host state between calls, never synchronises, and
- * only enqueues two kernels on `stream` (a hipStream_t; NULL is the default
- * stream): a statistics pass over the logits and a finishing pass.  Outputs
- * are valid once the stream reaches the end of the call's work.  The
- * workspace carries per-chunk statistics and race winners from one pass to
- * the next: it must be zero-filled once before its first use (hipMemset), and
- * every call leaves it zero-filled again when it completes, so it can be
+ * only enqueues one kernel on `stream` (a hipStream_t; NULL is the default
+ * stream).  Outputs are valid once the stream reaches the end of the call's
+ * work.  The workspace carries per-request counters between the kernel's
+ * workgroups: it must be zero-filled once before its first use (hipMemset),
+ * and every call leaves it zero-filled again when it completes, so it can be
  * reused by later calls of any size up to the one it was sized for.  Two
  * calls that may run concurrently need separate workspaces.
- *
- * draft_offsets should be non-decreasing.  Target and draft rows are assigned
- * to requests by searching the offsets; a request with an invalid slice fails
- * alone when the offsets are non-decreasing, but with decreasing offsets the
- * requests whose rows cannot be assigned unambiguously fail as well
- * (accept_len = -1).  Out-of-range offsets never cause out-of-bounds reads.
  *
  * Errors: a negative return value means nothing was enqueued (except
  * SV_ERR_LAUNCH, which reports a launch failure).  accept_len[b] = -1 with
@@ -130,10 +123,9 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, int3
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* spec_verify_sample, plus two HIP events (hipEvent_t handles created by the
- * caller) recorded on `stream` immediately before and after the statistics
- * kernel (the pass that streams every logit the call needs, and the one
- * bounded by HBM bandwidth), so a caller can time that kernel on the stream it
- * runs on.  Both events must be valid.  Same results as spec_verify_sample. */
+ * caller) recorded on `stream` immediately before and after the library's
+ * kernel, so a caller can time the kernel on the stream it runs on.  Both
+ * events must be valid.  Same results as spec_verify_sample. */
 int spec_verify_sample_timed(const void* target_logits, const void* draft_logits, int32_t dtype,
                              int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows,
                              const int32_t* draft_offsets, const int32_t* draft_tokens,
