@@ -44,7 +44,7 @@
  * allocates nothing, keeps no host state between calls, never synchronises, and
  * only enqueues one kernel on `stream` (a hipStream_t; NULL is the default
  * stream).  Outputs are valid once the stream reaches the end of the call's
- * work.  The workspace carries per-request counters between the kernel's
+ * work.  The workspace carries hand-off slots between the kernel's
  * workgroups: it must be zero-filled once before its first use (hipMemset),
  * and every call leaves it zero-filled again when it completes, so it can be
  * reused by later calls of any size up to the one it was sized for.  Two

@@ -2,56 +2,54 @@
 //
 // What is computed is stated in include/spec_verify.h (the accept / residual /
 // bonus rule of "Decodificación Especulativa y EAGLE", section "La Regla de
-// Exactitud", and its greedy case).  How it runs on MI355X: one launch whose
-// workgroups each take one job from a fixed schedule.
+// Exactitud", and its greedy case).  How it runs on MI355X: one launch.
 //
-// Jobs of request b:
-//   SA  statistics of a sampled request: one job per (row, 64 KiB V-chunk) of
-//       its K+1 target and K draft rows.  Streams the chunk with 16-byte
-//       loads and reduces it to one 8-byte partial (max, sum of
-//       2^(z c - fl(max c))), c = log2(e) / T, then stores it and exits.
-//   FA  finisher of a sampled request: collects the partials, folds them into
-//       per-row (max, log2 sum), gathers p_t(x_t) and q_t(x_t), draws r_t,
-//       finds the first rejection n with a wave ballot, and publishes n with
-//       the statistics of row n.
-//   R   race of a sampled request: one job per 4096-token chunk of row n, the
-//       exponential race over the residual (p_n - q_n)+ after a rejection or
-//       over p_K otherwise, plus one job that folds the chunk winners and
-//       writes the outputs.
-//   SB  statistics of a greedy request: (max, lowest argmax index) per chunk
-//       of its K+1 target rows (draft rows are never read).
-//   FB  finisher of a greedy request: first draft that differs from the row
-//       argmax; writes the outputs.  Also reports requests with a bad slice
-//       or temperature.
-// A job that does not apply to request b (e.g. SA of a greedy request) exits
-// at once.
-//
-// Schedule: request b's SA jobs sit at "time" b, SB at B + b, FA at b + d1,
-// R at b + d1 + d2 and FB at B + b + d3; the grid lists times in order and,
-// inside a time, the jobs in the order SA, SB, FA, R, FB.  The lags are
-// about two generations of resident workgroups, so every job comes well
-// after the jobs it depends on, sampled requests stream first, and their
-// finishing and races overlap the streaming of greedy requests and of later
-// sampled requests.
+// Vocabulary chunks.  Every row is cut into chunks of 8 KiB (4096 bf16 or
+// 2048 float32 logits).  Workgroup g serves chunk group cg = g mod ng (m
+// consecutive chunks) of two requests, b1 = g / ng and b2 = b1 - lag:
+//   1. statistics of request b1: each wave streams whole row-chunks (8
+//      16-byte loads per lane, two row-chunks in flight) of every row the
+//      request reads -- K+1 target and K draft rows when it is sampled, the
+//      K+1 target rows when it is greedy -- and reduces each row-chunk to one
+//      8-byte partial: (max, sum of 2^(z c - fl(max c))), c = log2(e) / T, or
+//      (max, lowest argmax index) for greedy rows;
+//   2. race of request b2 (sampled requests only): fold the partials of all
+//      rows of b2 (every workgroup of b2 does the same fold in the same order,
+//      so all of them find the same values), gather p_t(x_t) and q_t(x_t),
+//      draw r_t, find the first rejection n with a wave ballot, then run the
+//      exponential race over this workgroup's chunks of row n -- the residual
+//      (p_n - q_n)+ after a rejection, p_K otherwise.
+// The last workgroup of a request in grid order finishes it: the last
+// statistics workgroup of a greedy request folds its argmaxes and writes the
+// outputs; the last race workgroup of a sampled request folds the chunk
+// winners and writes the outputs.  Each polls the slots of its siblings,
+// which sit earlier in the grid.  The lag puts a request's races a few
+// hundred workgroups after its statistics, so they usually find the partials
+// ready, and the race arithmetic of one request overlaps the streaming of
+// later ones.  No workgroup is empty except the race-only tail for greedy
+// requests at the end of the grid.
 //
 // Hand-offs between workgroups use 8-byte slots in the workspace that are
 // all-zero until written (a written slot never has all-zero bits: +0.0 is
-// stored as -0.0).  Producers store with a device-coherent (sc1) store and
-// exit; consumers poll with device-coherent loads, then write the slot back
-// to zero, so the workspace is all-zero again after every call.  No
-// agent-scope release/acquire fence is used (on gfx950 those write back or
-// invalidate the XCD's whole L2).  A consumer only waits for jobs that come
-// earlier in the grid; the earliest waiting job waits only for jobs that
-// never wait, so with in-order dispatch every wait ends.  Waits are also
-// bounded (kSpinLimit polls); an expired wait reports accept_len = -1.
+// stored as -0.0).  Producers store with device-coherent (sc1) stores;
+// consumers poll with device-coherent loads.  The finishing workgroup of a
+// request writes every slot of that request back to zero, so the workspace
+// is all-zero again after every call.  No agent-
+// scope release/acquire fence is used (on gfx950 those write back or
+// invalidate the XCD's whole L2).  A workgroup waits only for partials of
+// workgroups earlier in the grid, and those store their partials before they
+// wait for anything, so with in-order dispatch every wait ends.  Waits are
+// also bounded (kSpinLimit polls); an expired wait reports accept_len = -1.
 //
 // Race keys: the winner maximises ln w_v - ln E_v, i.e. w_v / E_v.  Inside a
-// thread candidates are compared by cross-multiplication (w_a e_b > w_b e_a)
-// with e = -log2 U = E / ln 2 (a common factor); a thread's best becomes the
-// float key w / e for the merges across threads, waves and chunks.  Weights
-// are 2^(z c - fl(m c)) with fl(m c) the rounded product for the row maximum
-// m; the same rounded offset is used when the row's sum is formed, so it
-// cancels exactly from p = w / sum.
+// thread and chunk, candidates are compared by cross-multiplication
+// (w_a e_b > w_b e_a) with e = -log2 U = E / ln 2 (a common factor); a
+// thread's best in a chunk becomes the float key w / e, and keys merge
+// across threads, chunks and workgroups by (larger key, then lower index),
+// an order-independent rule, so the winner does not depend on how chunks are
+// grouped.  Weights are 2^(z c - fl(m c)) with fl(m c) the rounded product
+// for the row maximum m; the same rounded offset is used when the row's sum
+// is formed, so it cancels exactly from p = w / sum.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -65,28 +63,28 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kStatsVecs = 16;  // 16-byte loads per thread per statistics chunk
-constexpr int kRaceGroups = 4;  // 4-token Philox groups per thread per race chunk
-constexpr int kRaceChunk = kThreads * kRaceGroups * 4;  // tokens per race chunk
-constexpr int kRowsMax = 2 * SV_KMAX + 1;               // row slots per request
-constexpr int kRowsPerWave = (kRowsMax + kWaves - 1) / kWaves;
+constexpr int kItemVecs = 8;                      // 16-byte loads per lane per row-chunk
+constexpr int kItemsInFlight = 2;                 // row-chunks a wave loads before reducing
+constexpr int kChunkBytes = 64 * kItemVecs * 16;  // one row-chunk: 8 KiB
+constexpr int kRowsMax = 2 * SV_KMAX + 1;         // row slots per request
+constexpr int kFoldBlock = 16;                    // partials a lane holds while folding
 constexpr unsigned kSpinLimit = 1u << 16;
+constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
 constexpr float kLog2e = 1.4426950408889634f;
-// Consumers sit this many grid slots after their producers: about two
-// generations of resident workgroups (5 per CU here), so a consumer is
-// dispatched once its producers have finished rather than spinning beside
-// them.
-#ifndef SV_FINISH_LAG_SLOTS
-#define SV_FINISH_LAG_SLOTS 4096  // statistics -> finisher
-#endif
+// The race of request b runs in the workgroups of request b + lag, with lag
+// chosen so that about this many workgroups separate them.
 #ifndef SV_RACE_LAG_SLOTS
-#define SV_RACE_LAG_SLOTS 2048  // finisher -> race
+#define SV_RACE_LAG_SLOTS 1024
+#endif
+// Race chunks per race workgroup (at least the statistics grouping): more
+// chunks spread the fold and the memory round trips of a race over more
+// tokens; fewer give each race more parallelism.
+#ifndef SV_RACE_CHUNKS
+#define SV_RACE_CHUNKS 2
 #endif
 
 __host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
-__host__ __device__ constexpr int stats_chunk(bool bf16) {
-  return kThreads * kStatsVecs * elems_per_vec(bf16);
-}
+__host__ __device__ constexpr int chunk_tokens(bool bf16) { return kChunkBytes / (bf16 ? 2 : 4); }
 
 // ------------------------------------------------------------------ helpers
 
@@ -111,27 +109,71 @@ struct Philox4 {
   uint32_t w[4];
 };
 
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t a = static_cast<uint64_t>(0xD2511F53u) * c0;
-    const uint64_t d = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+    const uint64_t a = static_cast<uint64_t>(kPhiloxM0) * c0;
+    const uint64_t d = static_cast<uint64_t>(kPhiloxM1) * c2;
     const uint32_t n0 = static_cast<uint32_t>(d >> 32) ^ c1 ^ k0;
     const uint32_t n2 = static_cast<uint32_t>(a >> 32) ^ c3 ^ k1;
     c1 = static_cast<uint32_t>(d);
     c3 = static_cast<uint32_t>(a);
     c0 = n0;
     c2 = n2;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
   }
   return Philox4{{c0, c1, c2, c3}};
 }
 
-// (2 * (x >> 9) + 1) * 2^-24, exact in float32, strictly inside (0, 1).
+// a ^ b ^ k in one instruction (gfx950's three-input bit operation; 0x96 is
+// the truth table of three-way exclusive or).  k is wave-uniform.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+// The same generator for race counters (c0, c1, c2, 0) with c1, c2 and the key
+// wave-uniform.  Rounds 1-3 still mix uniform words (the compiler keeps those
+// on the scalar unit); from round 4 on every word varies per lane and each
+// output word takes one three-input xor.
+__device__ __forceinline__ Philox4 philox_race(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t k0, uint32_t k1) {
+  uint32_t c3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t a = static_cast<uint64_t>(kPhiloxM0) * c0;
+    const uint64_t d = static_cast<uint64_t>(kPhiloxM1) * c2;
+    uint32_t n0, n2;
+    if (r < 3) {
+      n0 = static_cast<uint32_t>(d >> 32) ^ c1 ^ k0;
+      n2 = static_cast<uint32_t>(a >> 32) ^ c3 ^ k1;
+    } else {
+      n0 = xor3(static_cast<uint32_t>(d >> 32), c1, k0);
+      n2 = xor3(static_cast<uint32_t>(a >> 32), c3, k1);
+    }
+    c1 = static_cast<uint32_t>(d);
+    c3 = static_cast<uint32_t>(a);
+    c0 = n0;
+    c2 = n2;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+
+// (2 * (x >> 9) + 1) * 2^-24, exact in float32, strictly inside (0, 1): the
+// float 1 + (x >> 9) 2^-23 (one funnel shift puts x >> 9 under the exponent
+// bits of 1.0) minus (1 - 2^-24); both lie in [0.5, 2], so the difference is
+// exact (Sterbenz).
 __device__ __forceinline__ float uniform_open01(uint32_t x) {
-  return __fmaf_rn(static_cast<float>(x >> 9), 0x1p-23f, 0x1p-24f);
+  const uint32_t one_plus = __builtin_amdgcn_alignbit(0x7Fu, x, 9u);  // 0x3F800000 | x >> 9
+  return __uint_as_float(one_plus) - 0x1.fffffep-1f;
 }
 
 // fl(m * c): the row-maximum offset, rounded once (the build disables
@@ -143,15 +185,17 @@ __device__ __forceinline__ float scaled_logit(float z, float cf, float mc) {
   return __fmaf_rn(z, cf, -mc);
 }
 
-// (max, sum) pairs; a sum s is relative to fl(max * c).  Larger max wins and
-// the other sum is rescaled by 2^(fl(m c) - fl(M c)).  A side with max == -inf
-// contributes 0 * s, which keeps a NaN sum NaN.
+// 2^(fl(m c) - Mc) for a partial with maximum m merging under offset Mc;
+// 0 for a partial with no finite maximum (0 * s keeps a NaN sum NaN).
+__device__ __forceinline__ float rescale(float m, float cf, float Mc) {
+  return (m == -INFINITY) ? 0.f : fast_exp2(scaled_max(m, cf) - Mc);
+}
+
+// (max, sum) pairs; a sum s is relative to fl(max * c).
 __device__ __forceinline__ void merge_stats(float& m, float& s, float m2, float s2, float cf) {
   const float M = fmaxf(m, m2);
   const float Mc = scaled_max(M, cf);
-  const float f1 = (m == -INFINITY) ? 0.f : fast_exp2(scaled_max(m, cf) - Mc);
-  const float f2 = (m2 == -INFINITY) ? 0.f : fast_exp2(scaled_max(m2, cf) - Mc);
-  s = s * f1 + s2 * f2;
+  s = s * rescale(m, cf, Mc) + s2 * rescale(m2, cf, Mc);
   m = M;
 }
 
@@ -163,13 +207,16 @@ __device__ __forceinline__ void merge_argmax(float& v, int& i, float v2, int i2)
   }
 }
 
-__device__ __forceinline__ void wave_merge_stats(float& m, float& s, float cf) {
+__device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64);
-    const float s2 = __shfl_xor(s, o, 64);
-    merge_stats(m, s, m2, s2, cf);
-  }
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
 }
 
 __device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
@@ -194,6 +241,16 @@ __device__ __forceinline__ void block_argmax(float& key, int& idx, float* sh_k, 
   key = sh_k[0];
   idx = sh_i[0];
   for (int w = 1; w < kWaves; ++w) merge_argmax(key, idx, sh_k[w], sh_i[w]);
+}
+
+// This wave's index in the workgroup, known to the compiler as wave-uniform
+// (so per-wave decisions become scalar branches, not exec-masked ones).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// A value every lane holds equally, moved to a scalar register.
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform_float(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
 // ------------------------------------------------------------------ hand-off slots
@@ -227,56 +284,15 @@ __device__ uint64_t slot_wait(const uint64_t* p) {
 }
 
 // Drain this thread's outstanding memory operations, so device-coherent
-// stores made so far are visible before the next one.  The signal fences keep
-// the compiler from moving memory accesses across the wait.
+// stores made so far are acknowledged before the next access.  The signal
+// fences keep the compiler from moving memory accesses across the wait.
 __device__ __forceinline__ void drain_memory() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// ------------------------------------------------------------------ workspace
-
-enum : uint32_t { kStatusOk = 1, kStatusFault = 2 };
-
-struct Layout {
-  int J;    // row slots per request: target 0..max_k, then draft 0..max_k-1
-  int nc1;  // statistics chunks per row
-  int nc2;  // race chunks per row
-  size_t stats_off, race_off, pub_off, total;
-};
-
-__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-
-Layout make_layout(int32_t B, int32_t V, int32_t max_k, bool bf16) {
-  Layout L;
-  L.J = 2 * max_k + 1;
-  L.nc1 = static_cast<int>(ceil_div(V, stats_chunk(bf16)));
-  L.nc2 = static_cast<int>(ceil_div(V, kRaceChunk));
-  L.stats_off = 0;
-  // sized with the float32 chunk (the smaller one) so either dtype fits
-  const size_t stats_bytes =
-      static_cast<size_t>(B) * L.J * ceil_div(V, stats_chunk(false)) * sizeof(uint64_t);
-  L.race_off = round256(stats_bytes);
-  L.pub_off = L.race_off + round256(static_cast<size_t>(B) * L.nc2 * sizeof(uint64_t));
-  L.total = L.pub_off + round256(static_cast<size_t>(B) * 4 * sizeof(uint64_t));
-  return L;
-}
-
-// Jobs in schedule order inside one time step.
-enum Job : int { kSA = 0, kSB = 1, kFA = 2, kR = 3, kFB = 4, kJobs = 5 };
-
-// A run of time steps with the same set of jobs present.
-struct Region {
-  int64_t g0;    // first grid slot
-  int32_t k0;    // first time step
-  int32_t seg;   // slots per time step
-  int32_t mask;  // jobs present (bit per Job)
-  int32_t pad;
-};
-constexpr int kMaxRegions = 12;
+// ------------------------------------------------------------------ parameters
 
 struct Params {
   const void* target;
@@ -285,28 +301,28 @@ struct Params {
   const int32_t* tokens;
   const float* temperature;  // NULL: every request greedy
   uint32_t k0, k1;           // Philox key
-  int32_t B, V, max_k, n_draft_rows, nc1, nc2;
-  uint64_t* part;       // [B][J][nc1] statistics partials
-  uint64_t* race_part;  // [B][nc2] race chunk winners
-  uint64_t* pub;        // [B][4] published record: (fl(m c), log2 sum) of target row n,
-                        // the same of draft row n, (c, n), (1, status) -- last written
+  int32_t B, V, max_k, n_draft_rows;
+  int32_t nc;   // row-chunks per row
+  int32_t m;    // chunks per workgroup
+  int32_t ng;   // workgroups per request, ceil(nc / m)
+  int32_t mr;   // race chunks per race workgroup (a multiple of m)
+  int32_t ngr;  // race workgroups per request, ceil(nc / mr) <= ng
+  int32_t lag;  // request b's race runs in the first ngr workgroups of request b + lag
+  uint64_t* part;    // [B][2 max_k + 1][nc] row-chunk partials
+  uint64_t* race;    // [B][ngr] race winner of each race workgroup
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_at;
   float* q_at;
-  int32_t job_len[kJobs];  // slots each job kind takes per request
-  int32_t job_off[kJobs];  // time step of request 0's job
-  int32_t n_regions;
-  Region reg[kMaxRegions];
 };
 
-// Per-request checks every job can make from the request's scalars.
+// Per-request checks every workgroup can make from the request's scalars.
 struct Req {
   int32_t off0, K;
   float T;
   bool slice_ok, temp_ok, greedy;
+  __device__ bool valid() const { return slice_ok && temp_ok; }
   __device__ bool sampled() const { return slice_ok && temp_ok && !greedy; }
-  __device__ bool greedy_ok() const { return slice_ok && temp_ok && greedy; }
 };
 
 __device__ __forceinline__ Req load_req(const Params& p, int b) {
@@ -322,7 +338,7 @@ __device__ __forceinline__ Req load_req(const Params& p, int b) {
   return r;
 }
 
-// Outputs of a failed request (its slice is valid).
+// Outputs of a failed request whose slice is valid.
 __device__ void write_fault(const Params& p, int b, const Req& r) {
   const int tid = threadIdx.x;
   const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
@@ -334,316 +350,364 @@ __device__ void write_fault(const Params& p, int b, const Req& r) {
   if (tid == 0) p.accept_len[b] = -1;
 }
 
-__device__ __forceinline__ uint64_t* part_slot(const Params& p, int b, int j, int c) {
-  return p.part + (static_cast<int64_t>(b) * (2 * p.max_k + 1) + j) * p.nc1 + c;
+// Row r of a request (r <= K target row r, else draft row r - K - 1) keeps its
+// partials in row slot j.
+__device__ __forceinline__ int row_slot(const Params& p, int K, int r) {
+  return r <= K ? r : p.max_k + r - K;
 }
 
-// ------------------------------------------------------------------ statistics jobs
+__device__ __forceinline__ uint64_t* part_slot(const Params& p, int b, int j, int c) {
+  return p.part + (static_cast<int64_t>(b) * (2 * p.max_k + 1) + j) * p.nc + c;
+}
 
-template <bool BF16, bool VEC>
-__device__ void stats_job(const Params& p, int b, int slot, bool sampled_job) {
-  constexpr int EPV = elems_per_vec(BF16);
-  constexpr int CHUNK = stats_chunk(BF16);
-  constexpr int PAIR = 2 * EPV;  // elements folded per online step
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = slot % p.nc1;
-  const int j = slot / p.nc1;
-
-  const Req r = load_req(p, b);
-  if (sampled_job ? !r.sampled() : !r.greedy_ok()) return;
-  const void* base;
-  int64_t row;
-  if (j <= p.max_k) {
-    if (j > r.K) return;
-    base = p.target;
-    row = static_cast<int64_t>(r.off0) + b + j;
-  } else {
-    const int t = j - p.max_k - 1;
-    if (t >= r.K) return;
-    base = p.draft;
-    row = static_cast<int64_t>(r.off0) + t;
+// Zeroes the row-chunk partials of rows 0..nrows-1 of request b (the
+// finishing workgroup, once every reader of them is done).
+__device__ void clear_request(const Params& p, int b, int K, int nrows) {
+  const int n = nrows * p.nc;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int r = i / p.nc;
+    slot_store(part_slot(p, b, row_slot(p, K, r), i - r * p.nc), 0u);
   }
-  const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
-  const int64_t e_end = (e0 + CHUNK < p.V) ? e0 + CHUNK : p.V;
-  const int64_t rbase = row * static_cast<int64_t>(p.V);
+}
 
-  // issue every 16-byte load first; elements of vector u are
-  // e0 + (u * kThreads + tid) * EPV + [0, EPV), increasing in u
-  uint4 buf[kStatsVecs];
+// ------------------------------------------------------------------ statistics
+
+// One wave's share of a row-chunk: lane elements e0 + (u * 64 + lane) * EPV +
+// [0, EPV), u = 0..kItemVecs-1.  The vector path loads every vector from an
+// in-row address (indices clamped to the row's last vector) on one code path,
+// so the loads of several row-chunks stay in flight together; mask_tail then
+// replaces the vectors past the row end with -inf.  The scalar path reads -inf
+// past V itself.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load_item(const void* base, int64_t row, int V, int64_t e0,
+                                          uint4* out) {
+  constexpr int EPV = elems_per_vec(BF16);
+  const int lane = threadIdx.x & 63;
   if constexpr (VEC) {
     const uint4* rowv = reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
-                                                       rbase * (BF16 ? 2 : 4));
-    const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
+                                                       row * V * (BF16 ? 2 : 4));
+    const int last = V / EPV - 1;
+    const int i0 = static_cast<int>(e0 / EPV) + lane;
 #pragma unroll
-    for (int u = 0; u < kStatsVecs; ++u) {
-      const int64_t e = e0 + (static_cast<int64_t>(u) * kThreads + tid) * EPV;
-      buf[u] = (e < e_end) ? rowv[e / EPV] : make_uint4(ninf, ninf, ninf, ninf);
-    }
-  }
-  auto unpack_pair = [&](int pi, float* xs) {
-    if constexpr (VEC) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint4 v = buf[2 * pi + h];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (BF16) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            xs[h * 8 + 2 * k] = bf16_lo(w[k]);
-            xs[h * 8 + 2 * k + 1] = bf16_hi(w[k]);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) xs[h * 4 + k] = __uint_as_float(w[k]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-          const int64_t e = e0 + (static_cast<int64_t>(2 * pi + h) * kThreads + tid) * EPV + k;
-          xs[h * EPV + k] = (e < e_end) ? load_logit<BF16>(base, rbase + e) : -INFINITY;
-        }
-    }
-  };
-
-  __shared__ float sh_a[kWaves];
-  __shared__ float sh_b[kWaves];
-  uint64_t result = 0;
-  if (r.greedy) {
-    float best = -INFINITY;
-    int idx = INT_MAX;
-#pragma unroll
-    for (int pi = 0; pi < kStatsVecs / 2; ++pi) {
-      float xs[PAIR];
-      unpack_pair(pi, xs);
-#pragma unroll
-      for (int k = 0; k < PAIR; ++k) {
-        if (xs[k] > best) {
-          best = xs[k];
-          idx = static_cast<int>(e0 + (static_cast<int64_t>(2 * pi + k / EPV) * kThreads + tid) *
-                                          EPV + k % EPV);
-        }
-      }
-    }
-    wave_merge_argmax(best, idx);
-    if (lane == 0) {
-      sh_a[wave] = best;
-      sh_b[wave] = __int_as_float(idx);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < kWaves; ++w) merge_argmax(best, idx, sh_a[w], __float_as_int(sh_b[w]));
-      result = pack_slot(best, static_cast<uint32_t>(idx));
-    }
+    for (int u = 0; u < kItemVecs; ++u) out[u] = rowv[min(i0 + u * 64, last)];
   } else {
-    // online over pairs of vectors: (m, s) with s relative to fl(m c)
-    const float cf = kLog2e / r.T;
-    float m = -INFINITY, s = 0.f;
+    const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
+    const int64_t rb = row * V;
 #pragma unroll
-    for (int pi = 0; pi < kStatsVecs / 2; ++pi) {
-      float xs[PAIR];
-      unpack_pair(pi, xs);
-      float pm = xs[0];
+    for (int u = 0; u < kItemVecs; ++u) {
+      const int64_t e = e0 + static_cast<int64_t>(u * 64 + lane) * EPV;
+      uint32_t w[4];
 #pragma unroll
-      for (int k = 1; k < PAIR; ++k) pm = fmaxf(pm, xs[k]);
-      const float M = fmaxf(m, pm);
-      // offset 0 when there is no finite max keeps a NaN visible in the sum
-      const float Mc = (M == -INFINITY) ? 0.f : scaled_max(M, cf);
-      if (m != -INFINITY) s *= fast_exp2(scaled_max(m, cf) - Mc);
-      float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int k = 0; k < PAIR; k += 2) {
-        a0 += fast_exp2(scaled_logit(xs[k], cf, Mc));
-        a1 += fast_exp2(scaled_logit(xs[k + 1], cf, Mc));
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (BF16) {
+          const uint16_t* b16 = static_cast<const uint16_t*>(base);
+          const uint32_t lo = (e + 2 * k < V) ? b16[rb + e + 2 * k] : 0xff80u;
+          const uint32_t hi = (e + 2 * k + 1 < V) ? b16[rb + e + 2 * k + 1] : 0xff80u;
+          w[k] = lo | (hi << 16);
+        } else {
+          w[k] = (e + k < V) ? __float_as_uint(static_cast<const float*>(base)[rb + e + k])
+                             : ninf;
+        }
       }
-      s += a0 + a1;
-      m = M;
-    }
-    wave_merge_stats(m, s, cf);
-    if (lane == 0) {
-      sh_a[wave] = m;
-      sh_b[wave] = s;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < kWaves; ++w) merge_stats(m, s, sh_a[w], sh_b[w], cf);
-      result = pack_slot(m, __float_as_uint(s));
+      out[u] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
-  if (tid == 0) slot_store(part_slot(p, b, j, c), result);
 }
 
-// ------------------------------------------------------------------ finishers
-
-// Waits for the partials of rows 0..nrows-1 (row r: slot j = r for r <= K,
-// j = max_k + r - K for the draft rows), folds them into sh_m / sh_ls and
-// zeroes the slots.  Greedy: sh_ls holds the argmax index bits.  Sets *bad on
-// a non-finite row, a NaN sum or an expired wait.
-template <bool GREEDY>
-__device__ void fold_partials(const Params& p, int b, int K, float cf, int nrows, float* sh_m,
-                              float* sh_ls, int* bad) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float a[kRowsPerWave], s[kRowsPerWave];
-  int ia[kRowsPerWave];
+// Vector path, row-chunk reaching past the row end: vectors past it become -inf.
+template <bool BF16>
+__device__ __forceinline__ void mask_tail(uint4* buf, int V, int64_t e0) {
+  constexpr int EPV = elems_per_vec(BF16);
+  const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
+  const int last = V / EPV - 1;
+  const int i0 = static_cast<int>(e0 / EPV) + (threadIdx.x & 63);
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    a[i] = -INFINITY;
-    s[i] = 0.f;
-    ia[i] = INT_MAX;
-  }
-  bool expired = false;
-  for (int c0 = 0; c0 < p.nc1; c0 += 64) {
-    const int c = c0 + lane;
-    // issue every slot load before waiting on any of them
-    uint64_t v[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int row = wave + i * kWaves;
-      const int j = (row <= K) ? row : p.max_k + row - K;
-      v[i] = (row < nrows && c < p.nc1) ? slot_load(part_slot(p, b, j, c)) : 1u;
-    }
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int row = wave + i * kWaves;
-      if (row < nrows && c < p.nc1) {
-        const int j = (row <= K) ? row : p.max_k + row - K;
-        uint64_t* slot = part_slot(p, b, j, c);
-        if (v[i] == 0u) v[i] = slot_wait(slot);
-        if (v[i] == 0u) {
-          expired = true;
-          continue;
-        }
-        slot_store(slot, 0u);
-        if (GREEDY) {
-          if (slot_f(v[i]) > -INFINITY)
-            merge_argmax(a[i], ia[i], slot_f(v[i]), static_cast<int>(slot_w(v[i])));
-        } else {
-          merge_stats(a[i], s[i], slot_f(v[i]), __uint_as_float(slot_w(v[i])), cf);
-        }
-      }
-    }
-  }
-  if (expired) atomicOr(bad, 1);
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int row = wave + i * kWaves;
-    if (GREEDY)
-      wave_merge_argmax(a[i], ia[i]);
-    else
-      wave_merge_stats(a[i], s[i], cf);
-    if (lane == 0 && row < nrows) {
-      const bool finite_max = a[i] > -INFINITY && a[i] < INFINITY;
-      if (GREEDY) {
-        if (!finite_max) atomicOr(bad, 1);
-        sh_ls[row] = __int_as_float(ia[i]);
-      } else {
-        if (!finite_max || !(s[i] < INFINITY)) atomicOr(bad, 1);
-        sh_m[row] = a[i];
-        sh_ls[row] = fast_log2(s[i]);
-      }
-    }
-  }
+  for (int u = 0; u < kItemVecs; ++u)
+    if (i0 + u * 64 > last) buf[u] = make_uint4(ninf, ninf, ninf, ninf);
 }
 
 template <bool BF16>
-__device__ void finish_sampled(const Params& p, int b) {
-  const Req r = load_req(p, b);
-  if (!r.sampled()) return;
-  const int tid = threadIdx.x;
-  const int K = r.K;
-  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
-  const int64_t drow0 = r.off0;
-  const float cf = kLog2e / r.T;
-
-  __shared__ int sh_bad;
-  __shared__ float sh_m[kRowsMax];
-  __shared__ float sh_ls[kRowsMax];
-  if (tid == 0) sh_bad = 0;
-  __syncthreads();
-  int32_t x = 0;
-  float zp = 0.f, zq = 0.f;
-  if (tid < K) {
-    x = p.tokens[r.off0 + tid];
-    if (x < 0 || x >= p.V) {
-      atomicOr(&sh_bad, 1);
-    } else {  // gathered now, so the loads overlap the wait for the partials
-      zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
-      zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
+__device__ __forceinline__ void unpack(const uint4& v, float* xs) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      xs[2 * k] = bf16_lo(w[k]);
+      xs[2 * k + 1] = bf16_hi(w[k]);
     }
-  }
-  fold_partials<false>(p, b, K, cf, 2 * K + 1, sh_m, sh_ls, &sh_bad);
-  __syncthreads();
-
-  uint64_t* pub = p.pub + 4 * static_cast<int64_t>(b);
-  if (sh_bad) {
-    write_fault(p, b, r);
-    if (tid == 0) slot_store(pub + 3, pack_slot(1.f, kStatusFault));
-    return;
-  }
-  // ratio test r_t * q_t(x_t) < p_t(x_t), left to right (wave 0 holds t < K <= 8)
-  bool reject = false;
-  if (tid < K) {
-    const float pp = fast_exp2(scaled_logit(zp, cf, scaled_max(sh_m[tid], cf)) - sh_ls[tid]);
-    const float qq =
-        fast_exp2(scaled_logit(zq, cf, scaled_max(sh_m[K + 1 + tid], cf)) - sh_ls[K + 1 + tid]);
-    const float u = uniform_open01(philox4x32_10(0u, tid, b, 1u, p.k0, p.k1).w[0]);
-    reject = !(u * qq < pp);
-    if (p.p_at) p.p_at[drow0 + tid] = pp;
-    if (p.q_at) p.q_at[drow0 + tid] = qq;
-  }
-  const uint64_t mask = __ballot(reject);
-  if (tid == 0) {
-    const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
-    const float mcq = n < K ? scaled_max(sh_m[K + 1 + n], cf) : 0.f;
-    const float lsq = n < K ? sh_ls[K + 1 + n] : 0.f;
-    slot_store(pub + 0, pack_slot(scaled_max(sh_m[n], cf), __float_as_uint(sh_ls[n])));
-    slot_store(pub + 1, pack_slot(mcq, __float_as_uint(lsq)));
-    slot_store(pub + 2, pack_slot(cf, static_cast<uint32_t>(n)));
-    drain_memory();
-    slot_store(pub + 3, pack_slot(1.f, kStatusOk));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xs[k] = __uint_as_float(w[k]);
   }
 }
 
-__device__ void finish_greedy(const Params& p, int b) {
+// Partial of one row-chunk held by the wave: (max, sum of 2^(z c - fl(max c))).
+// One pass: each vector's sum is formed relative to the vector's own maximum,
+// then rescaled to the wave maximum.
+template <bool BF16>
+__device__ __forceinline__ uint64_t item_stats(const uint4* buf, float cf) {
+  constexpr int EPV = elems_per_vec(BF16);
+  float vm[kItemVecs], vs[kItemVecs];
+#pragma unroll
+  for (int u = 0; u < kItemVecs; ++u) {
+    float xs[EPV];
+    unpack<BF16>(buf[u], xs);
+    float m = xs[0];
+#pragma unroll
+    for (int k = 1; k < EPV; ++k) m = fmaxf(m, xs[k]);
+    // offset 0 when there is no finite max keeps a NaN visible in the sum
+    const float mc = (m == -INFINITY) ? 0.f : scaled_max(m, cf);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < EPV; k += 2) {
+      s0 += fast_exp2(scaled_logit(xs[k], cf, mc));
+      s1 += fast_exp2(scaled_logit(xs[k + 1], cf, mc));
+    }
+    vm[u] = m;
+    vs[u] = s0 + s1;
+  }
+  float mx = vm[0];
+#pragma unroll
+  for (int u = 1; u < kItemVecs; ++u) mx = fmaxf(mx, vm[u]);
+  mx = wave_max(mx);
+  const float Mc = (mx == -INFINITY) ? 0.f : scaled_max(mx, cf);
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kItemVecs; ++u) s += vs[u] * rescale(vm[u], cf, Mc);
+  s = wave_sum(s);
+  return pack_slot(mx, __float_as_uint(s));
+}
+
+// Partial of one row-chunk for a greedy row: (max, lowest index attaining it).
+// The wave maximum from per-vector maxima; then each lane takes the first of
+// its vectors holding it (a backward scan keeps the last match, the lowest)
+// and the first element of that vector equal to it.  NaN never matches.
+template <bool BF16>
+__device__ __forceinline__ uint64_t item_argmax(const uint4* buf, int64_t e0) {
+  constexpr int EPV = elems_per_vec(BF16);
+  const int lane = threadIdx.x & 63;
+  float vm[kItemVecs];
+#pragma unroll
+  for (int u = 0; u < kItemVecs; ++u) {
+    float xs[EPV];
+    unpack<BF16>(buf[u], xs);
+    vm[u] = xs[0];
+#pragma unroll
+    for (int k = 1; k < EPV; ++k) vm[u] = fmaxf(vm[u], xs[k]);
+  }
+  float mx = vm[0];
+#pragma unroll
+  for (int u = 1; u < kItemVecs; ++u) mx = fmaxf(mx, vm[u]);
+  mx = wave_max(mx);
+  int us = -1;
+  uint4 sel = buf[0];
+#pragma unroll
+  for (int u = kItemVecs - 1; u >= 0; --u) {
+    if (vm[u] == mx) {
+      us = u;
+      sel = buf[u];
+    }
+  }
+  int idx = INT_MAX;
+  if (us >= 0) {
+    float xs[EPV];
+    unpack<BF16>(sel, xs);
+    int ks = 0;
+#pragma unroll
+    for (int k = EPV - 1; k >= 0; --k)
+      if (xs[k] == mx) ks = k;
+    idx = static_cast<int>(e0) + (us * 64 + lane) * EPV + ks;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) idx = min(idx, __shfl_xor(idx, o, 64));
+  return pack_slot(mx, static_cast<uint32_t>(idx));
+}
+
+__device__ void finish_greedy(const Params& p, int b, const Req& r);
+
+// One wave's row-chunks of request b in group cg, reduced to (max, sum)
+// partials for a sampled request or (max, argmax) for a greedy one.
+template <bool BF16, bool VEC, bool GREEDY>
+__device__ void stats_items(const Params& p, int b, const Req& r, int cg, float cf) {
+  constexpr int CHUNK = chunk_tokens(BF16);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int K = r.K;
+  const int nrows = GREEDY ? K + 1 : 2 * K + 1;
+  const int c_first = cg * p.m;
+  const int mg = min(p.m, p.nc - c_first);
+  const int n_items = nrows * mg;
+  // (the scalar-load path holds one row-chunk at a time: its loads are
+  // 2-byte or 4-byte, so a row-chunk already takes many registers in flight)
+  constexpr int IN_FLIGHT = VEC ? kItemsInFlight : 1;
+  // wave w takes items 2w, 2w+1, then 8 further on; item i is row i / mg,
+  // chunk c_first + i % mg
+  for (int i0 = wave * IN_FLIGHT; i0 < n_items; i0 += kWaves * IN_FLIGHT) {
+    uint4 buf[IN_FLIGHT][kItemVecs];
+#pragma unroll
+    for (int k = 0; k < IN_FLIGHT; ++k) {
+      // issue every load before any math, on one code path: past the last
+      // item the wave loads the last item again (the second load of the same
+      // lines is served by the cache) and skips it below
+      const int i = min(i0 + k, n_items - 1);
+      const int row = i / mg;
+      const int c = c_first + i - row * mg;
+      const bool tgt = row <= K;
+      const int64_t prow = tgt ? static_cast<int64_t>(r.off0) + b + row
+                               : static_cast<int64_t>(r.off0) + row - K - 1;
+      load_item<BF16, VEC>(tgt ? p.target : p.draft, prow, p.V, static_cast<int64_t>(c) * CHUNK,
+                           buf[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < IN_FLIGHT; ++k) {
+      const int i = i0 + k;
+      if (i < n_items) {
+        const int row = i / mg;
+        const int c = c_first + i - row * mg;
+        if (VEC && static_cast<int64_t>(c + 1) * CHUNK > p.V)
+          mask_tail<BF16>(buf[k], p.V, static_cast<int64_t>(c) * CHUNK);
+        const uint64_t v = GREEDY ? item_argmax<BF16>(buf[k], static_cast<int64_t>(c) * CHUNK)
+                                  : item_stats<BF16>(buf[k], cf);
+        if (lane == 0) slot_store(part_slot(p, b, row_slot(p, K, row), c), v);
+      }
+    }
+  }
+}
+
+// Statistics of request b over the chunks of group cg.
+template <bool BF16, bool VEC>
+__device__ void stats_part(const Params& p, int b, int cg) {
   const Req r = load_req(p, b);
   const int tid = threadIdx.x;
-  if (!r.slice_ok) {
+  if (!r.valid()) {
+    if (cg == 0) {
+      if (r.slice_ok)
+        write_fault(p, b, r);
+      else if (tid == 0)
+        p.accept_len[b] = -1;
+    }
+    return;
+  }
+  if (r.greedy) {
+    stats_items<BF16, VEC, true>(p, b, r, cg, 0.f);
+    if (cg == p.ng - 1) finish_greedy(p, b, r);  // the request's last workgroup
+  } else {
+    stats_items<BF16, VEC, false>(p, b, r, cg, kLog2e / r.T);
+  }
+}
+
+// ------------------------------------------------------------------ folding
+
+struct FoldShared {
+  float m[kWaves][kRowsMax];
+  float s[kWaves][kRowsMax];  // greedy: argmax index bits
+  float row_m[kRowsMax];      // folded row maximum
+  float row_ls[kRowsMax];     // sampled: log2 of the row sum; greedy: argmax index bits
+  int bad;                    // 1: a row is not finite, 2: a wait expired
+};
+
+// Folds the partials of rows 0..nrows-1 of request b: lane = row, each wave
+// takes a quarter of the chunks (in order), then wave 0 merges the waves in
+// order.  Every workgroup that folds the same request gets the same floats.
+template <bool GREEDY>
+__device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, FoldShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  if (tid == 0) sh.bad = 0;
+  const int cpw = (p.nc + kWaves - 1) / kWaves;
+  const int cb = wave * cpw;
+  const int ce = min(cb + cpw, p.nc);
+  const bool active = lane < nrows;
+  const int j = active ? row_slot(p, K, lane) : 0;
+  float M = -INFINITY, S = 0.f;
+  int I = INT_MAX;
+  bool expired = false;
+  for (int c0 = cb; c0 < ce; c0 += kFoldBlock) {
+    uint64_t v[kFoldBlock];
+#pragma unroll
+    for (int i = 0; i < kFoldBlock; ++i)  // issue every load before waiting on any
+      v[i] = (active && c0 + i < ce) ? slot_load(part_slot(p, b, j, c0 + i)) : 0u;
+#pragma unroll
+    for (int i = 0; i < kFoldBlock; ++i) {
+      if (active && c0 + i < ce && v[i] == 0u) {
+        v[i] = slot_wait(part_slot(p, b, j, c0 + i));
+        if (v[i] == 0u) expired = true;
+      }
+    }
+    if (!active) continue;
+    if constexpr (GREEDY) {
+#pragma unroll
+      for (int i = 0; i < kFoldBlock; ++i)
+        if (c0 + i < ce && v[i] != 0u)
+          merge_argmax(M, I, slot_f(v[i]), static_cast<int>(slot_w(v[i])));
+    } else {
+      float bm = M;
+#pragma unroll
+      for (int i = 0; i < kFoldBlock; ++i)
+        if (c0 + i < ce && v[i] != 0u) bm = fmaxf(bm, slot_f(v[i]));
+      const float bmc = (bm == -INFINITY) ? 0.f : scaled_max(bm, cf);
+      S *= rescale(M, cf, bmc);
+#pragma unroll
+      for (int i = 0; i < kFoldBlock; ++i)
+        if (c0 + i < ce && v[i] != 0u)
+          S += __uint_as_float(slot_w(v[i])) * rescale(slot_f(v[i]), cf, bmc);
+      M = bm;
+    }
+  }
+  __syncthreads();  // sh.bad initialised
+  if (expired) atomicOr(&sh.bad, 2);
+  if (active) {
+    sh.m[wave][lane] = M;
+    sh.s[wave][lane] = GREEDY ? __int_as_float(I) : S;
+  }
+  __syncthreads();
+  if (wave == 0 && active) {
+    for (int w = 1; w < kWaves; ++w) {
+      if constexpr (GREEDY)
+        merge_argmax(M, I, sh.m[w][lane], __float_as_int(sh.s[w][lane]));
+      else
+        merge_stats(M, S, sh.m[w][lane], sh.s[w][lane], cf);
+    }
+    const bool finite_max = M > -INFINITY && M < INFINITY;
+    if (!finite_max || (!GREEDY && !(S < INFINITY))) atomicOr(&sh.bad, 1);
+    sh.row_m[lane] = M;
+    sh.row_ls[lane] = GREEDY ? __int_as_float(I) : fast_log2(S);
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ greedy finish
+
+__device__ void finish_greedy(const Params& p, int b, const Req& r) {
+  __shared__ FoldShared sh;
+  __shared__ int sh_n;
+  const int tid = threadIdx.x;
+  __syncthreads();  // this workgroup's own partials are stored
+  const int K = r.K;
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  int32_t x = 0;
+  bool bad_token = false;
+  if (tid < K) {
+    x = p.tokens[r.off0 + tid];
+    bad_token = x < 0 || x >= p.V;
+  }
+  fold_rows<true>(p, b, K, K + 1, 0.f, sh);
+  const bool any_bad_token = __syncthreads_or(bad_token);
+  clear_request(p, b, K, K + 1);
+  if (sh.bad & 2) {
     if (tid == 0) p.accept_len[b] = -1;
     return;
   }
-  if (!r.temp_ok) {
-    write_fault(p, b, r);
-    return;
-  }
-  if (!r.greedy) return;
-  const int K = r.K;
-  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
-  __shared__ int sh_bad;
-  __shared__ float sh_ls[kRowsMax];
-  __shared__ int sh_n;
-  if (tid == 0) sh_bad = 0;
-  __syncthreads();
-  int32_t x = 0;
-  if (tid < K) {
-    x = p.tokens[r.off0 + tid];
-    if (x < 0 || x >= p.V) atomicOr(&sh_bad, 1);
-  }
-  fold_partials<true>(p, b, K, 0.f, K + 1, nullptr, sh_ls, &sh_bad);
-  __syncthreads();
-  if (sh_bad) {
+  if (sh.bad || any_bad_token) {
     write_fault(p, b, r);
     return;
   }
   // first t < K whose draft differs from the argmax; the stop token is argmax row n
-  const bool mismatch = tid < K && __float_as_int(sh_ls[tid]) != x;
+  const bool mismatch = tid < K && __float_as_int(sh.row_ls[tid]) != x;
   const uint64_t mask = __ballot(mismatch);
   if (tid == 0) sh_n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
   __syncthreads();
   const int n = sh_n;
   if (tid <= K) {
-    const int32_t y = __float_as_int(sh_ls[n]);
+    const int32_t y = __float_as_int(sh.row_ls[n]);
     p.out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? y : -1);
   }
   if (tid < K) {
@@ -653,7 +717,12 @@ __device__ void finish_greedy(const Params& p, int b) {
   if (tid == 0) p.accept_len[b] = n;
 }
 
-// ------------------------------------------------------------------ race jobs
+// ------------------------------------------------------------------ race
+
+struct RaceRow {
+  float mcp, lsp, mcq, lsq, cf;
+  int n;
+};
 
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend, float out[4]) {
@@ -677,43 +746,31 @@ __device__ __forceinline__ void load4(const void* rowp, int64_t v, int64_t vend,
   }
 }
 
-struct RaceRow {
-  float mcp, lsp, mcq, lsq, cf;
-  int n;
-};
-
-__device__ __forceinline__ RaceRow read_published(const uint64_t* pub) {
-  RaceRow rr;
-  const uint64_t w0 = slot_load(pub + 0), w1 = slot_load(pub + 1), w2 = slot_load(pub + 2);
-  rr.mcp = slot_f(w0);
-  rr.lsp = __uint_as_float(slot_w(w0));
-  rr.mcq = slot_f(w1);
-  rr.lsq = __uint_as_float(slot_w(w1));
-  rr.cf = slot_f(w2);
-  rr.n = static_cast<int>(slot_w(w2));
-  return rr;
-}
-
 // Race candidates of tokens 4g..4g+3 folded into this thread's best
 // (bw / be, bidx); tokens arrive in increasing order, so a strict > keeps the
-// lowest index on ties.
-__device__ __forceinline__ void race_group(const float zp[4], const float zq[4], bool residual,
+// lowest index on ties.  Bonus weights drop the row's common factor 2^-lsp.
+template <bool RESIDUAL, bool FULL>
+__device__ __forceinline__ void race_group(const float zp[4], const float zq[4],
                                            const RaceRow& rr, int64_t g, int64_t v_end,
                                            uint32_t b, uint32_t k0, uint32_t k1, float& bw,
                                            float& be, int& bidx) {
-  const Philox4 r = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(rr.n), b, 0u,
-                                  k0, k1);
+  const Philox4 r = philox_race(static_cast<uint32_t>(g), static_cast<uint32_t>(rr.n), b, k0, k1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t v = g * 4 + k;
-    if (v >= v_end) break;
+    const int v = static_cast<int>(g) * 4 + k;
+    if (!FULL && v >= v_end) break;
     const float e = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
-    float w = fast_exp2(scaled_logit(zp[k], rr.cf, rr.mcp) - rr.lsp);
-    if (residual) w -= fast_exp2(scaled_logit(zq[k], rr.cf, rr.mcq) - rr.lsq);
+    float w;
+    if constexpr (RESIDUAL) {
+      w = fast_exp2(scaled_logit(zp[k], rr.cf, rr.mcp) - rr.lsp) -
+          fast_exp2(scaled_logit(zq[k], rr.cf, rr.mcq) - rr.lsq);
+    } else {
+      w = fast_exp2(scaled_logit(zp[k], rr.cf, rr.mcp));
+    }
     if (w * be > bw * e) {
       bw = w;
       be = e;
-      bidx = static_cast<int>(v);
+      bidx = v;
     }
   }
 }
@@ -723,102 +780,206 @@ __device__ __forceinline__ float race_key(float bw, float be, int bidx) {
   return bidx == INT_MAX ? -INFINITY : bw / be;
 }
 
-template <bool BF16, bool VEC>
-__device__ void race_chunk(const Params& p, int b, int c) {
-  const Req r = load_req(p, b);
-  if (!r.sampled()) return;
-  const int tid = threadIdx.x;
-  const uint64_t* pub = p.pub + 4 * static_cast<int64_t>(b);
-  __shared__ uint32_t sh_status;
-  if (tid == 0) sh_status = slot_w(slot_wait(pub + 3));  // 0 if the wait expired
-  __syncthreads();
-  uint64_t* out = p.race_part + static_cast<int64_t>(b) * p.nc2 + c;
-  if (sh_status != kStatusOk) {
-    if (tid == 0) slot_store(out, pack_slot(-INFINITY, INT_MAX));
-    return;
+// 4 logits at v (a multiple of 4) with one vector load (vector path only).
+template <bool BF16>
+__device__ __forceinline__ void load4v(const void* rowp, int64_t v, float out[4]) {
+  if constexpr (BF16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(rowp) + v);
+    out[0] = bf16_lo(w.x);
+    out[1] = bf16_hi(w.x);
+    out[2] = bf16_lo(w.y);
+    out[3] = bf16_hi(w.y);
+  } else {
+    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(rowp) + v);
+    out[0] = w.x;
+    out[1] = w.y;
+    out[2] = w.z;
+    out[3] = w.w;
   }
-  const RaceRow rr = read_published(pub);
-  const int64_t esz = BF16 ? 2 : 4;
-  const bool residual = rr.n < r.K;
-  const void* prow =
-      static_cast<const char*>(p.target) + (static_cast<int64_t>(r.off0) + b + rr.n) * p.V * esz;
-  const void* qrow = residual ? static_cast<const char*>(p.draft) +
-                                    (static_cast<int64_t>(r.off0) + rr.n) * p.V * esz
-                              : nullptr;
-  const int64_t v_begin = static_cast<int64_t>(c) * kRaceChunk;
-  const int64_t v_end = (v_begin + kRaceChunk < p.V) ? v_begin + kRaceChunk : p.V;
-  float zp[kRaceGroups][4], zq[kRaceGroups][4];
+}
+
+// Race over chunk c of row n: this thread's (key, index) merged into (key, idx).
+// A chunk wholly inside the row (vector path) takes unconditional loads and no
+// per-token bounds; the last chunk of a row checks every group and token.
+template <bool BF16, bool VEC, bool RESIDUAL>
+__device__ __forceinline__ void race_chunk(const Params& p, int b, int c, const void* prow,
+                                           const void* qrow, const RaceRow& rr, float& key,
+                                           int& idx) {
+  constexpr int CHUNK = chunk_tokens(BF16);
+  constexpr int G = CHUNK / (4 * kThreads);  // 4-token groups per thread
+  const int tid = threadIdx.x;
+  const int64_t v_end = min(static_cast<int64_t>(c + 1) * CHUNK, static_cast<int64_t>(p.V));
+  const int64_t g0 = static_cast<int64_t>(c) * (CHUNK / 4);
+  float zp[G][4], zq[G][4];
+  float bw = 0.f, be = 1.f;  // any w > 0 beats the empty candidate
+  int bi = INT_MAX;
+  if (VEC && static_cast<int64_t>(c + 1) * CHUNK <= p.V) {
 #pragma unroll
-  for (int gi = 0; gi < kRaceGroups; ++gi) {  // issue every load before any math
-    const int64_t g = v_begin / 4 + gi * kThreads + tid;
+    for (int gi = 0; gi < G; ++gi) {  // issue every load before any math
+      const int64_t g = g0 + gi * kThreads + tid;
+      load4v<BF16>(prow, g * 4, zp[gi]);
+      if (RESIDUAL) load4v<BF16>(qrow, g * 4, zq[gi]);
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) zq[gi][k] = 0.f;
-    if (g * 4 < v_end) {
-      load4<BF16, VEC>(prow, g * 4, v_end, zp[gi]);
-      if (residual) load4<BF16, VEC>(qrow, g * 4, v_end, zq[gi]);
+    for (int gi = 0; gi < G; ++gi)
+      race_group<RESIDUAL, true>(zp[gi], zq[gi], rr, g0 + gi * kThreads + tid, v_end,
+                                 static_cast<uint32_t>(b), p.k0, p.k1, bw, be, bi);
+  } else {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int64_t g = g0 + gi * kThreads + tid;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) zq[gi][k] = 0.f;
+      if (g * 4 < v_end) {
+        load4<BF16, VEC>(prow, g * 4, v_end, zp[gi]);
+        if (RESIDUAL) load4<BF16, VEC>(qrow, g * 4, v_end, zq[gi]);
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int64_t g = g0 + gi * kThreads + tid;
+      if (g * 4 < v_end)
+        race_group<RESIDUAL, false>(zp[gi], zq[gi], rr, g, v_end, static_cast<uint32_t>(b), p.k0,
+                                    p.k1, bw, be, bi);
     }
   }
-  float bw = 0.f, be = 1.f;  // any w > 0 beats the empty candidate
-  int idx = INT_MAX;
-#pragma unroll
-  for (int gi = 0; gi < kRaceGroups; ++gi) {
-    const int64_t g = v_begin / 4 + gi * kThreads + tid;
-    if (g * 4 < v_end)
-      race_group(zp[gi], zq[gi], residual, rr, g, v_end, b, p.k0, p.k1, bw, be, idx);
-  }
-  float key = race_key(bw, be, idx);
-  __shared__ float sh_key[kWaves];
-  __shared__ int sh_idx[kWaves];
-  block_argmax(key, idx, sh_key, sh_idx);
-  if (tid == 0) slot_store(out, pack_slot(key, static_cast<uint32_t>(idx)));
+  merge_argmax(key, idx, race_key(bw, be, bi), bi);
 }
 
 template <bool BF16, bool VEC>
-__device__ void race_finish(const Params& p, int b) {
-  const Req r = load_req(p, b);
-  if (!r.sampled()) return;
+__device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceRow& rr,
+                               bool bad, bool fold_expired);
+
+// Race of sampled request b over the chunks of group cg.  x holds draft token
+// t = threadIdx.x of request b for t < K (loaded at the start of the workgroup).
+template <bool BF16, bool VEC>
+__device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t x) {
+  __shared__ FoldShared sh;
+  __shared__ int sh_n;
+  __shared__ float sh_key[kWaves];
+  __shared__ int sh_idx[kWaves];
   const int tid = threadIdx.x;
+  const int K = r.K;
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  const int64_t drow0 = r.off0;
+  const int64_t esz = BF16 ? 2 : 4;
+  const float cf = kLog2e / r.T;
+
+  // gather z at x_t now, so the loads overlap the wait for the partials
+  float zp = 0.f, zq = 0.f;
+  bool bad_token = false;
+  if (tid < K) {
+    if (x < 0 || x >= p.V) {
+      bad_token = true;
+    } else {
+      zp = load_logit<BF16>(p.target, (trow0 + tid) * p.V + x);
+      zq = load_logit<BF16>(p.draft, (drow0 + tid) * p.V + x);
+    }
+  }
+  fold_rows<false>(p, b, K, 2 * K + 1, cf, sh);
+  const bool any_bad_token = __syncthreads_or(bad_token) != 0;
+  const bool bad = (sh.bad & 1) || any_bad_token;
+  const bool expired = (sh.bad & 2) != 0;
+
+  RaceRow rr{};
+  rr.cf = cf;
+  float key = -INFINITY;
+  int idx = INT_MAX;
+  if (!bad && !expired) {
+    // ratio test r_t * q_t(x_t) < p_t(x_t), left to right (wave 0 holds t < K <= 8)
+    bool reject = false;
+    if (tid < K) {
+      const float pp =
+          fast_exp2(scaled_logit(zp, cf, scaled_max(sh.row_m[tid], cf)) - sh.row_ls[tid]);
+      const float qq = fast_exp2(scaled_logit(zq, cf, scaled_max(sh.row_m[K + 1 + tid], cf)) -
+                                 sh.row_ls[K + 1 + tid]);
+      const float u = uniform_open01(philox4x32_10(0u, tid, b, 1u, p.k0, p.k1).w[0]);
+      reject = !(u * qq < pp);
+      if (cg == 0) {
+        if (p.p_at) p.p_at[drow0 + tid] = pp;
+        if (p.q_at) p.q_at[drow0 + tid] = qq;
+      }
+    }
+    const uint64_t mask = __ballot(reject);
+    if (tid == 0) sh_n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : K;
+    __syncthreads();
+    // workgroup-uniform values read from LDS: keep them in scalar registers
+    rr.n = uniform_int(sh_n);
+    rr.mcp = uniform_float(scaled_max(sh.row_m[rr.n], cf));
+    rr.lsp = uniform_float(sh.row_ls[rr.n]);
+    if (rr.n < K) {
+      rr.mcq = uniform_float(scaled_max(sh.row_m[K + 1 + rr.n], cf));
+      rr.lsq = uniform_float(sh.row_ls[K + 1 + rr.n]);
+    }
+    const void* prow = static_cast<const char*>(p.target) + (trow0 + rr.n) * p.V * esz;
+    const int c_first = cg * p.mr;
+    const int c_end = min(c_first + p.mr, p.nc);
+    if (rr.n < K) {
+      const void* qrow = static_cast<const char*>(p.draft) + (drow0 + rr.n) * p.V * esz;
+      for (int c = c_first; c < c_end; ++c)
+        race_chunk<BF16, VEC, true>(p, b, c, prow, qrow, rr, key, idx);
+    } else {
+      for (int c = c_first; c < c_end; ++c)
+        race_chunk<BF16, VEC, false>(p, b, c, prow, nullptr, rr, key, idx);
+    }
+  }
+  block_argmax(key, idx, sh_key, sh_idx);
+  if (tid == 0)
+    slot_store(p.race + static_cast<int64_t>(b) * p.ngr + cg,
+               pack_slot(key, expired ? kExpiredIdx : static_cast<uint32_t>(idx)));
+  // the request's last race workgroup finishes it
+  if (cg == p.ngr - 1) finish_sampled<BF16, VEC>(p, b, r, rr, bad, expired);
+}
+
+// The last race workgroup of request b: folds the workgroup winners, writes
+// the outputs and clears the request's slots.
+template <bool BF16, bool VEC>
+__device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceRow& rr,
+                               bool bad, bool fold_expired) {
   __shared__ float sh_key[kWaves];
   __shared__ int sh_idx[kWaves];
   __shared__ int sh_expired;
-  if (tid == 0) sh_expired = 0;
+  const int tid = threadIdx.x;
+  if (tid == 0) sh_expired = fold_expired ? 1 : 0;
   __syncthreads();
   float key = -INFINITY;
   int idx = INT_MAX;
-  for (int i = tid; i < p.nc2; i += kThreads) {
-    uint64_t* slot = p.race_part + static_cast<int64_t>(b) * p.nc2 + i;
+  for (int i = tid; i < p.ngr; i += kThreads) {
+    uint64_t* slot = p.race + static_cast<int64_t>(b) * p.ngr + i;
     const uint64_t v = slot_wait(slot);
-    if (v == 0u) {
+    slot_store(slot, 0u);
+    if (v == 0u || slot_w(v) == kExpiredIdx) {
       atomicOr(&sh_expired, 1);
       continue;
     }
-    slot_store(slot, 0u);
     merge_argmax(key, idx, slot_f(v), static_cast<int>(slot_w(v)));
   }
   block_argmax(key, idx, sh_key, sh_idx);  // its barriers also publish sh_expired
-  uint64_t* pub = p.pub + 4 * static_cast<int64_t>(b);
-  const uint32_t status = slot_w(slot_load(pub + 3));
-  const RaceRow rr = read_published(pub);
-  __syncthreads();  // every thread has read the record before it is cleared
-  if (tid < 4) slot_store(pub + tid, 0u);
-  if (sh_expired || status == 0u) {
+  clear_request(p, b, r.K, 2 * r.K + 1);
+  if (sh_expired) {
     if (tid == 0) p.accept_len[b] = -1;
     return;
   }
-  if (status != kStatusOk) return;  // the finisher wrote the failure
+  if (bad) {
+    write_fault(p, b, r);
+    return;
+  }
   const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
   if (idx == INT_MAX) {
     // no token had p > q (rounding can only cause this when p == q): race on p_n
     const int64_t esz = BF16 ? 2 : 4;
     const void* prow = static_cast<const char*>(p.target) + (trow0 + rr.n) * p.V * esz;
     float bw = 0.f, be = 1.f;
+    int bi = INT_MAX;
     for (int64_t g = tid; g * 4 < p.V; g += kThreads) {
       float zp[4];
       const float zq[4] = {0.f, 0.f, 0.f, 0.f};
       load4<BF16, VEC>(prow, g * 4, p.V, zp);
-      race_group(zp, zq, false, rr, g, p.V, b, p.k0, p.k1, bw, be, idx);
+      race_group<false, false>(zp, zq, rr, g, p.V, static_cast<uint32_t>(b), p.k0, p.k1, bw, be,
+                               bi);
     }
-    key = race_key(bw, be, idx);
+    key = race_key(bw, be, bi);
+    idx = bi;
     block_argmax(key, idx, sh_key, sh_idx);
   }
   const int n = rr.n;
@@ -833,34 +994,21 @@ __device__ void race_finish(const Params& p, int b) {
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
-  const int64_t g = blockIdx.x;
-  int ri = 0;
-  while (ri + 1 < p.n_regions && g >= p.reg[ri + 1].g0) ++ri;
-  const Region& R = p.reg[ri];
-  const int64_t rel = g - R.g0;
-  const int k = R.k0 + static_cast<int>(rel / R.seg);
-  int o = static_cast<int>(rel % R.seg);
-  for (int job = 0; job < kJobs; ++job) {
-    if (!(R.mask & (1 << job))) continue;
-    if (o >= p.job_len[job]) {
-      o -= p.job_len[job];
-      continue;
-    }
-    const int b = k - p.job_off[job];
-    switch (job) {
-      case kSA: stats_job<BF16, VEC>(p, b, o, true); break;
-      case kFA: finish_sampled<BF16>(p, b); break;
-      case kR:
-        if (o < p.nc2)
-          race_chunk<BF16, VEC>(p, b, o);
-        else
-          race_finish<BF16, VEC>(p, b);
-        break;
-      case kSB: stats_job<BF16, VEC>(p, b, o, false); break;
-      default: finish_greedy(p, b); break;
-    }
-    return;
+  const int g = blockIdx.x;
+  const int b1 = g / p.ng;
+  const int cg = g - b1 * p.ng;
+  const int b2 = b1 - p.lag;
+  // the race request's draft tokens, loaded before the statistics stream
+  Req r2{};
+  bool race = false;
+  int32_t x = 0;
+  if (b2 >= 0 && b2 < p.B) {
+    r2 = load_req(p, b2);
+    race = r2.sampled() && cg < p.ngr;
+    if (race && static_cast<int>(threadIdx.x) < r2.K) x = p.tokens[r2.off0 + threadIdx.x];
   }
+  if (b1 < p.B) stats_part<BF16, VEC>(p, b1, cg);
+  if (race) race_part<BF16, VEC>(p, b2, cg, r2, x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -871,59 +1019,31 @@ bool shape_ok(int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Lays the jobs out in time steps (see the schedule at the top); returns the
-// grid size, or -1 if it does not fit the region table.
-int64_t build_schedule(Params& prm, int B, bool all_greedy) {
-  const int J = 2 * prm.max_k + 1;
-  int len[kJobs];
-  len[kSA] = all_greedy ? 0 : J * prm.nc1;
-  len[kSB] = (prm.max_k + 1) * prm.nc1;
-  len[kFA] = all_greedy ? 0 : 1;
-  len[kR] = all_greedy ? 0 : prm.nc2 + 1;
-  len[kFB] = 1;
-  const int gb = all_greedy ? 0 : B;  // greedy statistics start after the sampled ones
-  const int64_t d1 = ceil_div(SV_FINISH_LAG_SLOTS, std::max(len[kSA], 1));
-  const int64_t d2 = ceil_div(SV_RACE_LAG_SLOTS, std::max(len[kSA] + len[kSB], 1));
-  const int64_t d3 = ceil_div(SV_FINISH_LAG_SLOTS, len[kSB]);
-  const int64_t cap = 4 * static_cast<int64_t>(B);  // keeps every offset small
-  int off[kJobs];
-  off[kSA] = 0;
-  off[kSB] = gb;
-  off[kFA] = static_cast<int>(std::min(d1, cap));
-  off[kR] = static_cast<int>(std::min(d1 + d2, cap));
-  off[kFB] = static_cast<int>(gb + std::min(d3, cap));
-  int bounds[2 * kJobs];
-  int nb = 0;
-  for (int j = 0; j < kJobs; ++j) {
-    prm.job_len[j] = len[j];
-    prm.job_off[j] = off[j];
-    if (len[j] == 0) continue;
-    bounds[nb++] = off[j];
-    bounds[nb++] = off[j] + B;
-  }
-  std::sort(bounds, bounds + nb);
-  nb = static_cast<int>(std::unique(bounds, bounds + nb) - bounds);
-  int64_t g = 0;
-  prm.n_regions = 0;
-  for (int i = 0; i + 1 < nb; ++i) {
-    const int ka = bounds[i], kb = bounds[i + 1];
-    int mask = 0, seg = 0;
-    for (int j = 0; j < kJobs; ++j)
-      if (len[j] > 0 && off[j] <= ka && ka < off[j] + B) {
-        mask |= 1 << j;
-        seg += len[j];
-      }
-    if (seg == 0) continue;
-    if (prm.n_regions == kMaxRegions) return -1;
-    Region& R = prm.reg[prm.n_regions++];
-    R.g0 = g;
-    R.k0 = ka;
-    R.seg = seg;
-    R.mask = mask;
-    R.pad = 0;
-    g += static_cast<int64_t>(kb - ka) * seg;
-  }
-  return g;
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct Layout {
+  size_t part_off, race_off, total;
+};
+
+// Sized with the float32 chunk (the smaller one, so more chunks) so that
+// either dtype fits.
+Layout make_layout(int32_t B, int32_t V, int32_t max_k) {
+  const size_t nc = static_cast<size_t>(ceil_div(V, chunk_tokens(false)));
+  Layout L;
+  L.part_off = 0;
+  L.race_off = round256(static_cast<size_t>(B) * (2 * max_k + 1) * nc * sizeof(uint64_t));
+  L.total = L.race_off + round256(static_cast<size_t>(B) * nc * sizeof(uint64_t));
+  return L;
+}
+
+// Chunks per workgroup: enough rows x chunks that a workgroup streams about
+// 64 KiB (8 row-chunks) when the request reads all its rows.
+int chunks_per_workgroup(int rows, int nc) {
+  int m = 1;
+  while (m < 8 && rows * m < 8) m *= 2;
+  return std::max(1, std::min(m, nc));
 }
 
 template <bool BF16, bool VEC>
@@ -951,7 +1071,7 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   if (workspace_bytes < spec_verify_workspace_bytes(B, V, max_k) || !aligned16(workspace))
     return SV_ERR_WORKSPACE;
   const bool bf16 = dtype == SV_BF16;
-  const Layout L = make_layout(B, V, max_k, bf16);
+  const Layout L = make_layout(B, V, max_k);
   char* ws = static_cast<char*>(workspace);
   Params prm;
   prm.target = target;
@@ -965,16 +1085,21 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.V = V;
   prm.max_k = max_k;
   prm.n_draft_rows = n_draft_rows;
-  prm.nc1 = L.nc1;
-  prm.nc2 = L.nc2;
-  prm.part = reinterpret_cast<uint64_t*>(ws + L.stats_off);
-  prm.race_part = reinterpret_cast<uint64_t*>(ws + L.race_off);
-  prm.pub = reinterpret_cast<uint64_t*>(ws + L.pub_off);
+  prm.nc = static_cast<int32_t>(ceil_div(V, chunk_tokens(bf16)));
+  prm.m = chunks_per_workgroup(all_greedy ? max_k + 1 : 2 * max_k + 1, prm.nc);
+  prm.ng = static_cast<int32_t>(ceil_div(prm.nc, prm.m));
+  prm.mr = std::min(prm.nc, prm.m * std::max(1, SV_RACE_CHUNKS / prm.m));
+  prm.ngr = static_cast<int32_t>(ceil_div(prm.nc, prm.mr));
+  prm.lag = static_cast<int32_t>(
+      std::min<int64_t>(B, std::max<int64_t>(1, ceil_div(SV_RACE_LAG_SLOTS, prm.ng))));
+  prm.part = reinterpret_cast<uint64_t*>(ws + L.part_off);
+  prm.race = reinterpret_cast<uint64_t*>(ws + L.race_off);
   prm.accept_len = accept_len;
   prm.out_tokens = out_tokens;
   prm.p_at = p_at;
   prm.q_at = q_at;
-  const int64_t grid = build_schedule(prm, B, all_greedy);
+  // all-greedy calls have no races, so no race-only tail
+  const int64_t grid = (static_cast<int64_t>(B) + (all_greedy ? 0 : prm.lag)) * prm.ng;
   if (grid <= 0 || grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 && aligned16(target) && (!draft || aligned16(draft));
@@ -992,7 +1117,7 @@ extern "C" {
 
 size_t spec_verify_workspace_bytes(int32_t B, int32_t V, int32_t max_k) {
   if (!shape_ok(B, V, max_k, 0)) return 0;
-  return make_layout(B, V, max_k, false).total;
+  return make_layout(B, V, max_k).total;
 }
 
 int spec_verify_greedy(const void* target_logits, int32_t dtype, int32_t B, int32_t V,
