@@ -26,8 +26,8 @@
 // which sit earlier in the grid.  The lag puts a request's races a few
 // hundred workgroups after its statistics, so they usually find the partials
 // ready, and the race arithmetic of one request overlaps the streaming of
-// later ones.  No workgroup is empty except the race-only tail for greedy
-// requests at the end of the grid.
+// later ones.  After the B x ng workgroups with statistics comes a tail of
+// lag x ngr race-only workgroups (empty for greedy requests).
 //
 // Hand-offs between workgroups use 8-byte slots in the workspace that are
 // all-zero until written (a written slot never has all-zero bits: +0.0 is
@@ -54,6 +54,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 #include <cmath>
 #include <cstdint>
 
@@ -79,6 +80,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Race chunks per race workgroup (at least the statistics grouping): more
 // chunks spread the fold and the memory round trips of a race over more
 // tokens; fewer give each race more parallelism.
+// s_sleep units (64 clocks each) between polling rounds of a fold
+#ifndef SV_FOLD_SLEEP
+#define SV_FOLD_SLEEP 1
+#endif
 #ifndef SV_RACE_CHUNKS
 #define SV_RACE_CHUNKS 2
 #endif
@@ -625,13 +630,21 @@ __device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, Fo
 #pragma unroll
     for (int i = 0; i < kFoldBlock; ++i)  // issue every load before waiting on any
       v[i] = (active && c0 + i < ce) ? slot_load(part_slot(p, b, j, c0 + i)) : 0u;
+    // re-poll every slot still missing together, one round trip per round
+    uint32_t missing = 0u;
 #pragma unroll
-    for (int i = 0; i < kFoldBlock; ++i) {
-      if (active && c0 + i < ce && v[i] == 0u) {
-        v[i] = slot_wait(part_slot(p, b, j, c0 + i));
-        if (v[i] == 0u) expired = true;
-      }
+    for (int i = 0; i < kFoldBlock; ++i)
+      if (active && c0 + i < ce && v[i] == 0u) missing |= 1u << i;
+    for (unsigned it = 0; missing != 0u && it < kSpinLimit; ++it) {
+      __builtin_amdgcn_s_sleep(SV_FOLD_SLEEP);
+#pragma unroll
+      for (int i = 0; i < kFoldBlock; ++i)
+        if (missing & (1u << i)) v[i] = slot_load(part_slot(p, b, j, c0 + i));
+#pragma unroll
+      for (int i = 0; i < kFoldBlock; ++i)
+        if ((missing & (1u << i)) && v[i] != 0u) missing &= ~(1u << i);
     }
+    if (missing != 0u) expired = true;
     if (!active) continue;
     if constexpr (GREEDY) {
 #pragma unroll
@@ -846,6 +859,67 @@ __device__ __forceinline__ void race_chunk(const Params& p, int b, int c, const 
   merge_argmax(key, idx, race_key(bw, be, bi), bi);
 }
 
+// Race over two whole chunks c, c + 1 inside the row (vector path): every
+// load of both is issued first, kept packed (4 logits per 8 bytes for bf16),
+// so the second chunk's loads do not wait behind the first chunk's math.
+// Each chunk still reduces to its own per-thread key, as in race_chunk.
+template <bool BF16, bool RESIDUAL>
+__device__ __forceinline__ void race_pair(const Params& p, int b, int c, const void* prow,
+                                          const void* qrow, const RaceRow& rr, float& key,
+                                          int& idx) {
+  constexpr int CHUNK = chunk_tokens(BF16);
+  constexpr int G = CHUNK / (4 * kThreads);
+  using Raw = typename std::conditional<BF16, uint2, uint4>::type;
+  const int tid = threadIdx.x;
+  const Raw* pr = static_cast<const Raw*>(prow);
+  const Raw* qr = static_cast<const Raw*>(qrow);
+  Raw rp[2][G], rq[2][G];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int64_t g = static_cast<int64_t>(c + h) * (CHUNK / 4) + gi * kThreads + tid;
+      rp[h][gi] = pr[g];
+      if (RESIDUAL) rq[h][gi] = qr[g];
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float bw = 0.f, be = 1.f;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int64_t g = static_cast<int64_t>(c + h) * (CHUNK / 4) + gi * kThreads + tid;
+      float zp[4], zq[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
+        zp[0] = bf16_lo(rp[h][gi].x);
+        zp[1] = bf16_hi(rp[h][gi].x);
+        zp[2] = bf16_lo(rp[h][gi].y);
+        zp[3] = bf16_hi(rp[h][gi].y);
+        if (RESIDUAL) {
+          zq[0] = bf16_lo(rq[h][gi].x);
+          zq[1] = bf16_hi(rq[h][gi].x);
+          zq[2] = bf16_lo(rq[h][gi].y);
+          zq[3] = bf16_hi(rq[h][gi].y);
+        }
+      } else {
+        zp[0] = __uint_as_float(rp[h][gi].x);
+        zp[1] = __uint_as_float(rp[h][gi].y);
+        zp[2] = __uint_as_float(rp[h][gi].z);
+        zp[3] = __uint_as_float(rp[h][gi].w);
+        if (RESIDUAL) {
+          zq[0] = __uint_as_float(rq[h][gi].x);
+          zq[1] = __uint_as_float(rq[h][gi].y);
+          zq[2] = __uint_as_float(rq[h][gi].z);
+          zq[3] = __uint_as_float(rq[h][gi].w);
+        }
+      }
+      race_group<RESIDUAL, true>(zp, zq, rr, g, static_cast<int64_t>(p.V),
+                                 static_cast<uint32_t>(b), p.k0, p.k1, bw, be, bi);
+    }
+    merge_argmax(key, idx, race_key(bw, be, bi), bi);
+  }
+}
+
 template <bool BF16, bool VEC>
 __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceRow& rr,
                                bool bad, bool fold_expired);
@@ -914,13 +988,19 @@ __device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t 
     const void* prow = static_cast<const char*>(p.target) + (trow0 + rr.n) * p.V * esz;
     const int c_first = cg * p.mr;
     const int c_end = min(c_first + p.mr, p.nc);
+    constexpr int CHUNK = chunk_tokens(BF16);
+    int c = c_first;
     if (rr.n < K) {
       const void* qrow = static_cast<const char*>(p.draft) + (drow0 + rr.n) * p.V * esz;
-      for (int c = c_first; c < c_end; ++c)
-        race_chunk<BF16, VEC, true>(p, b, c, prow, qrow, rr, key, idx);
+      if (VEC)
+        for (; c + 1 < c_end && static_cast<int64_t>(c + 2) * CHUNK <= p.V; c += 2)
+          race_pair<BF16, true>(p, b, c, prow, qrow, rr, key, idx);
+      for (; c < c_end; ++c) race_chunk<BF16, VEC, true>(p, b, c, prow, qrow, rr, key, idx);
     } else {
-      for (int c = c_first; c < c_end; ++c)
-        race_chunk<BF16, VEC, false>(p, b, c, prow, nullptr, rr, key, idx);
+      if (VEC)
+        for (; c + 1 < c_end && static_cast<int64_t>(c + 2) * CHUNK <= p.V; c += 2)
+          race_pair<BF16, false>(p, b, c, prow, nullptr, rr, key, idx);
+      for (; c < c_end; ++c) race_chunk<BF16, VEC, false>(p, b, c, prow, nullptr, rr, key, idx);
     }
   }
   block_argmax(key, idx, sh_key, sh_idx);
@@ -994,9 +1074,18 @@ __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceR
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
+  // B x ng workgroups with statistics, then a tail of lag x ngr race-only ones
   const int g = blockIdx.x;
-  const int b1 = g / p.ng;
-  const int cg = g - b1 * p.ng;
+  const int main_wgs = p.B * p.ng;
+  int b1, cg;
+  if (g < main_wgs) {
+    b1 = g / p.ng;
+    cg = g - b1 * p.ng;
+  } else {
+    const int t = g - main_wgs;
+    b1 = p.B + t / p.ngr;
+    cg = t - (b1 - p.B) * p.ngr;
+  }
   const int b2 = b1 - p.lag;
   // the race request's draft tokens, loaded before the statistics stream
   Req r2{};
@@ -1090,8 +1179,10 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.ng = static_cast<int32_t>(ceil_div(prm.nc, prm.m));
   prm.mr = std::min(prm.nc, prm.m * std::max(1, SV_RACE_CHUNKS / prm.m));
   prm.ngr = static_cast<int32_t>(ceil_div(prm.nc, prm.mr));
-  prm.lag = static_cast<int32_t>(
-      std::min<int64_t>(B, std::max<int64_t>(1, ceil_div(SV_RACE_LAG_SLOTS, prm.ng))));
+  prm.lag = SV_RACE_LAG_SLOTS == 0
+                ? 0
+                : static_cast<int32_t>(std::min<int64_t>(
+                      B, std::max<int64_t>(1, ceil_div(SV_RACE_LAG_SLOTS, prm.ng))));
   prm.part = reinterpret_cast<uint64_t*>(ws + L.part_off);
   prm.race = reinterpret_cast<uint64_t*>(ws + L.race_off);
   prm.accept_len = accept_len;
@@ -1099,7 +1190,8 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.p_at = p_at;
   prm.q_at = q_at;
   // all-greedy calls have no races, so no race-only tail
-  const int64_t grid = (static_cast<int64_t>(B) + (all_greedy ? 0 : prm.lag)) * prm.ng;
+  const int64_t grid = static_cast<int64_t>(B) * prm.ng +
+                       (all_greedy ? 0 : static_cast<int64_t>(prm.lag) * prm.ngr);
   if (grid <= 0 || grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 && aligned16(target) && (!draft || aligned16(draft));
