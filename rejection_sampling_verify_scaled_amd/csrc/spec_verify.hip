@@ -53,6 +53,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <type_traits>
 #include <cmath>
@@ -66,27 +67,20 @@ constexpr int kThreads = 256;  // 4 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kItemVecs = 8;                      // 16-byte loads per lane per row-chunk
 constexpr int kItemsInFlight = 2;                 // row-chunks a wave loads before reducing
+constexpr int kGroupItems = kWaves * kItemsInFlight;  // flat grouping: row-chunks per workgroup
 constexpr int kChunkBytes = 64 * kItemVecs * 16;  // one row-chunk: 8 KiB
 constexpr int kRowsMax = 2 * SV_KMAX + 1;         // row slots per request
 constexpr int kFoldBlock = 16;                    // partials a lane holds while folding
 constexpr unsigned kSpinLimit = 1u << 16;
 constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
 constexpr float kLog2e = 1.4426950408889634f;
-// The race of request b runs in the workgroups of request b + lag, with lag
-// chosen so that about this many workgroups separate them.
-#ifndef SV_RACE_LAG_SLOTS
-#define SV_RACE_LAG_SLOTS 1024
-#endif
-// Race chunks per race workgroup (at least the statistics grouping): more
-// chunks spread the fold and the memory round trips of a race over more
-// tokens; fewer give each race more parallelism.
 // s_sleep units (64 clocks each) between polling rounds of a fold
 #ifndef SV_FOLD_SLEEP
 #define SV_FOLD_SLEEP 1
 #endif
-#ifndef SV_RACE_CHUNKS
-#define SV_RACE_CHUNKS 2
-#endif
+// Workgroups of this kernel one CU holds at once (96 VGPRs per lane: five
+// waves per SIMD, so five 4-wave workgroups per CU).
+constexpr int kWorkgroupsPerCu = 5;
 
 __host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
 __host__ __device__ constexpr int chunk_tokens(bool bf16) { return kChunkBytes / (bf16 ? 2 : 4); }
@@ -291,12 +285,6 @@ __device__ uint64_t slot_wait(const uint64_t* p) {
 // Drain this thread's outstanding memory operations, so device-coherent
 // stores made so far are acknowledged before the next access.  The signal
 // fences keep the compiler from moving memory accesses across the wait.
-__device__ __forceinline__ void drain_memory() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // ------------------------------------------------------------------ parameters
 
 struct Params {
@@ -308,9 +296,10 @@ struct Params {
   uint32_t k0, k1;           // Philox key
   int32_t B, V, max_k, n_draft_rows;
   int32_t nc;   // row-chunks per row
-  int32_t m;    // chunks per workgroup
-  int32_t ng;   // workgroups per request, ceil(nc / m)
-  int32_t mr;   // race chunks per race workgroup (a multiple of m)
+  int32_t flat; // 1: flat item grouping (8 items per workgroup), 0: column grouping
+  int32_t m;    // column grouping: chunks per workgroup
+  int32_t ng;   // workgroups per request: ceil(nc / m), or ceil(rows nc / 8) when flat
+  int32_t mr;   // race chunks per race workgroup
   int32_t ngr;  // race workgroups per request, ceil(nc / mr) <= ng
   int32_t lag;  // request b's race runs in the first ngr workgroups of request b + lag
   uint64_t* part;    // [B][2 max_k + 1][nc] row-chunk partials
@@ -538,24 +527,37 @@ __device__ void stats_items(const Params& p, int b, const Req& r, int cg, float 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int K = r.K;
   const int nrows = GREEDY ? K + 1 : 2 * K + 1;
-  const int c_first = cg * p.m;
-  const int mg = min(p.m, p.nc - c_first);
-  const int n_items = nrows * mg;
+  // The request's (row, chunk) items are numbered row-major over the chunks
+  // a group covers; item i is row i / span, chunk c0 + i % span.  Flat
+  // grouping: every group covers all nc chunks and takes the 8 items
+  // [8 cg, 8 cg + 8).  Column grouping: group cg covers m chunks from cg m and
+  // takes all its rows x m items.
+  int span, c0, i_lo, i_hi;
+  if (p.flat) {
+    span = p.nc;
+    c0 = 0;
+    i_lo = cg * kGroupItems;
+    i_hi = min(i_lo + kGroupItems, nrows * p.nc);
+  } else {
+    c0 = cg * p.m;
+    span = min(p.m, p.nc - c0);
+    i_lo = 0;
+    i_hi = nrows * span;
+  }
   // (the scalar-load path holds one row-chunk at a time: its loads are
   // 2-byte or 4-byte, so a row-chunk already takes many registers in flight)
   constexpr int IN_FLIGHT = VEC ? kItemsInFlight : 1;
-  // wave w takes items 2w, 2w+1, then 8 further on; item i is row i / mg,
-  // chunk c_first + i % mg
-  for (int i0 = wave * IN_FLIGHT; i0 < n_items; i0 += kWaves * IN_FLIGHT) {
+  // wave w takes items 2w, 2w+1 of the group, then 8 further on
+  for (int i0 = i_lo + wave * IN_FLIGHT; i0 < i_hi; i0 += kWaves * IN_FLIGHT) {
     uint4 buf[IN_FLIGHT][kItemVecs];
 #pragma unroll
     for (int k = 0; k < IN_FLIGHT; ++k) {
       // issue every load before any math, on one code path: past the last
       // item the wave loads the last item again (the second load of the same
       // lines is served by the cache) and skips it below
-      const int i = min(i0 + k, n_items - 1);
-      const int row = i / mg;
-      const int c = c_first + i - row * mg;
+      const int i = min(i0 + k, i_hi - 1);
+      const int row = i / span;
+      const int c = c0 + i - row * span;
       const bool tgt = row <= K;
       const int64_t prow = tgt ? static_cast<int64_t>(r.off0) + b + row
                                : static_cast<int64_t>(r.off0) + row - K - 1;
@@ -565,9 +567,9 @@ __device__ void stats_items(const Params& p, int b, const Req& r, int cg, float 
 #pragma unroll
     for (int k = 0; k < IN_FLIGHT; ++k) {
       const int i = i0 + k;
-      if (i < n_items) {
-        const int row = i / mg;
-        const int c = c_first + i - row * mg;
+      if (i < i_hi) {
+        const int row = i / span;
+        const int c = c0 + i - row * span;
         if (VEC && static_cast<int64_t>(c + 1) * CHUNK > p.V)
           mask_tail<BF16>(buf[k], p.V, static_cast<int64_t>(c) * CHUNK);
         const uint64_t v = GREEDY ? item_argmax<BF16>(buf[k], static_cast<int64_t>(c) * CHUNK)
@@ -1110,6 +1112,22 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute units of the current device, looked up once per device.
+int64_t compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Layout {
@@ -1175,14 +1193,36 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.max_k = max_k;
   prm.n_draft_rows = n_draft_rows;
   prm.nc = static_cast<int32_t>(ceil_div(V, chunk_tokens(bf16)));
-  prm.m = chunks_per_workgroup(all_greedy ? max_k + 1 : 2 * max_k + 1, prm.nc);
-  prm.ng = static_cast<int32_t>(ceil_div(prm.nc, prm.m));
-  prm.mr = std::min(prm.nc, prm.m * std::max(1, SV_RACE_CHUNKS / prm.m));
+  // Flat grouping when every request has max_k drafts: each workgroup then
+  // streams one full round of row-chunks.  With ragged draft lengths it would
+  // leave the shorter requests' surplus workgroups empty, so column grouping
+  // (one chunk column of every row per workgroup) is used instead.
+  const int rows = all_greedy ? max_k + 1 : 2 * max_k + 1;
+  prm.flat = static_cast<int64_t>(n_draft_rows) == static_cast<int64_t>(B) * max_k;
+  if (prm.flat) {
+    prm.m = 1;
+    prm.ng = static_cast<int32_t>(ceil_div(static_cast<int64_t>(rows) * prm.nc, kGroupItems));
+    // two chunks per race workgroup, or more when a request has fewer
+    // statistics workgroups than that leaves race workgroups
+    prm.mr = static_cast<int32_t>(
+        std::min<int64_t>(prm.nc, std::max<int64_t>(2, ceil_div(prm.nc, prm.ng))));
+  } else {
+    prm.m = chunks_per_workgroup(rows, prm.nc);
+    prm.ng = static_cast<int32_t>(ceil_div(prm.nc, prm.m));
+    prm.mr = std::min(prm.nc, prm.m * std::max(1, 4 / prm.m));
+  }
   prm.ngr = static_cast<int32_t>(ceil_div(prm.nc, prm.mr));
-  prm.lag = SV_RACE_LAG_SLOTS == 0
-                ? 0
-                : static_cast<int32_t>(std::min<int64_t>(
-                      B, std::max<int64_t>(1, ceil_div(SV_RACE_LAG_SLOTS, prm.ng))));
+  // Race placement.  A race workgroup polls, holding its slot, until its
+  // request's statistics are in, so it is placed about when they complete:
+  // four fifths of a resident generation of workgroups after them.  When
+  // the whole statistics grid is at most two generations, every race goes
+  // after all statistics workgroups instead (lag = B).
+  const int64_t resident = kWorkgroupsPerCu * compute_units();
+  const int64_t stats_wgs = static_cast<int64_t>(B) * prm.ng;
+  prm.lag = static_cast<int32_t>(
+      stats_wgs <= 2 * resident
+          ? B
+          : std::min<int64_t>(B, std::max<int64_t>(1, ceil_div(4 * resident / 5, prm.ng))));
   prm.part = reinterpret_cast<uint64_t*>(ws + L.part_off);
   prm.race = reinterpret_cast<uint64_t*>(ws + L.race_off);
   prm.accept_len = accept_len;

@@ -103,6 +103,21 @@ def test_ragged_vocab_and_k(dtype, V):
     compare(b, gg, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
 
 
+@pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
+@pytest.mark.parametrize("V,K", [(1, 2), (37, 8), (4099, 1), (40001, 4), (70000, 8), (128256, 3)])
+def test_uniform_k_vocab(dtype, V, K):
+    """Every request with K = max_k drafts (flat row-chunk grouping), ragged vocabulary tails."""
+    rng = np.random.default_rng(V * 11 + K * 3 + dtype)
+    B = 24
+    temps = rng.choice([0.0, 0.5, 1.0, 1.7], size=B)
+    b = W.make_custom_batch(rng, dtype, V, [K] * B, temps, seed=V + K, max_k=K)
+    say(f"uniform V={V} K={K} dtype={dtype}")
+    gpu = run_gpu(b, "sample")
+    compare(b, gpu, oracle.verify_batch(b))
+    gg = run_gpu(b, "greedy")
+    compare(b, gg, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
+
+
 def test_plain_sampling_k0():
     """max_k = 0: every request is plain sampling from softmax(z / T)."""
     rng = np.random.default_rng(3)
