@@ -82,6 +82,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // waves per SIMD, so five 4-wave workgroups per CU).
 constexpr int kWorkgroupsPerCu = 5;
 
+__device__ __forceinline__ int ceil_div_dev(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
 __host__ __device__ constexpr int chunk_tokens(bool bf16) { return kChunkBytes / (bf16 ? 2 : 4); }
 
@@ -596,7 +597,11 @@ __device__ void stats_part(const Params& p, int b, int cg) {
   }
   if (r.greedy) {
     stats_items<BF16, VEC, true>(p, b, r, cg, 0.f);
-    if (cg == p.ng - 1) finish_greedy(p, b, r);  // the request's last workgroup
+    // the request's last workgroup with items finishes it (flat grouping
+    // leaves the groups past a greedy request's (K+1) nc items empty)
+    const int last = p.flat ? static_cast<int>(ceil_div_dev((r.K + 1) * p.nc, kGroupItems)) - 1
+                            : p.ng - 1;
+    if (cg == last) finish_greedy(p, b, r);
   } else {
     stats_items<BF16, VEC, false>(p, b, r, cg, kLog2e / r.T);
   }
