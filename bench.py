@@ -208,6 +208,23 @@ def main():
     print(f"[bench] sv_verify kernel {k_us:.2f} us per launch over the timed region, "
           f"{ev_us:.2f} us with events around each launch", file=sys.stderr, flush=True)
 
+    # ---- the achievable line: a plain 1 GiB device-to-device copy (torch's copy
+    # kernel) on the same stream, counted as bytes read plus bytes written
+    cp_src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    for _ in range(3):
+        cp_dst.copy_(cp_src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    n_cp = 10
+    c0.record(stream)
+    for _ in range(n_cp):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * cp_src.numel() * n_cp / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cp_src, cp_dst
+
     # ---- correctness spot check of this exact launch configuration
     call(*argsets[0])
     torch.cuda.synchronize()
@@ -239,6 +256,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(args.workload),
                      "kernel": "sv_verify"},
+        "copy_gbs": {"value": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
+                     "what": "1 GiB device-to-device copy on the same stream, read + written bytes"},
     }
 
     if not args.no_cpu_baseline:

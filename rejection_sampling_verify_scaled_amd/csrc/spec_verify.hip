@@ -632,6 +632,16 @@ __device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, Fo
   float M = -INFINITY, S = 0.f;
   int I = INT_MAX;
   bool expired = false;
+  if constexpr (!GREEDY) {
+    // A race workgroup may start long before the request's statistics are
+    // in.  It first waits, with one lane, for the slot of the request's last
+    // row-chunk, which the last statistics workgroup in grid order writes,
+    // and only then loads every slot: hundreds of racing workgroups each
+    // re-polling all their partials would load the memory system that the
+    // statistics stream through.
+    if (tid == 0) slot_wait(part_slot(p, b, row_slot(p, K, nrows - 1), p.nc - 1));
+    __syncthreads();
+  }
   for (int c0 = cb; c0 < ce; c0 += kFoldBlock) {
     uint64_t v[kFoldBlock];
 #pragma unroll
