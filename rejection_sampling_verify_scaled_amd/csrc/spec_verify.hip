@@ -70,7 +70,8 @@ constexpr int kItemsInFlight = 2;                 // row-chunks a wave loads bef
 constexpr int kGroupItems = kWaves * kItemsInFlight;  // flat grouping: row-chunks per workgroup
 constexpr int kChunkBytes = 64 * kItemVecs * 16;  // one row-chunk: 8 KiB
 constexpr int kRowsMax = 2 * SV_KMAX + 1;         // row slots per request
-constexpr int kFoldBlock = 16;                    // partials a lane holds while folding
+constexpr int kFoldChunks = 64;                   // chunks per block of a fold
+constexpr int kFoldSlotsPerThread = (kRowsMax * kFoldChunks + 255) / 256;  // slots a thread loads per block
 constexpr unsigned kSpinLimit = 1u << 16;
 constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
 constexpr float kLog2e = 1.4426950408889634f;
@@ -610,6 +611,7 @@ __device__ void stats_part(const Params& p, int b, int cg) {
 // ------------------------------------------------------------------ folding
 
 struct FoldShared {
+  uint64_t slots[kRowsMax * kFoldChunks];  // one block of the request's partials, [row][chunk]
   float m[kWaves][kRowsMax];
   float s[kWaves][kRowsMax];  // greedy: argmax index bits
   float row_m[kRowsMax];      // folded row maximum
@@ -617,18 +619,18 @@ struct FoldShared {
   int bad;                    // 1: a row is not finite, 2: a wait expired
 };
 
-// Folds the partials of rows 0..nrows-1 of request b: lane = row, each wave
-// takes a quarter of the chunks (in order), then wave 0 merges the waves in
-// order.  Every workgroup that folds the same request gets the same floats.
+// Folds the partials of rows 0..nrows-1 of request b.  The partials are
+// taken in blocks of kFoldChunks chunks: the workgroup loads a block with
+// adjacent threads on adjacent slots (few memory transactions), re-polls the
+// slots still missing, and stages the block in LDS.  Then lane = row, and
+// wave w merges its quarter of the block's chunks in order into its running
+// row statistics; at the end wave 0 merges the waves in order.  Every
+// workgroup that folds the same request gets the same floats.
 template <bool GREEDY>
 __device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, FoldShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   if (tid == 0) sh.bad = 0;
-  const int cpw = (p.nc + kWaves - 1) / kWaves;
-  const int cb = wave * cpw;
-  const int ce = min(cb + cpw, p.nc);
   const bool active = lane < nrows;
-  const int j = active ? row_slot(p, K, lane) : 0;
   float M = -INFINITY, S = 0.f;
   int I = INT_MAX;
   bool expired = false;
@@ -640,45 +642,68 @@ __device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, Fo
     // re-polling all their partials would load the memory system that the
     // statistics stream through.
     if (tid == 0) slot_wait(part_slot(p, b, row_slot(p, K, nrows - 1), p.nc - 1));
-    __syncthreads();
   }
-  for (int c0 = cb; c0 < ce; c0 += kFoldBlock) {
-    uint64_t v[kFoldBlock];
+  for (int cblk = 0; cblk < p.nc; cblk += kFoldChunks) {
+    const int ncb = min(kFoldChunks, p.nc - cblk);
+    const int n_slots = nrows * ncb;
+    __syncthreads();  // the previous block's LDS reads are done
+    uint64_t v[kFoldSlotsPerThread];
 #pragma unroll
-    for (int i = 0; i < kFoldBlock; ++i)  // issue every load before waiting on any
-      v[i] = (active && c0 + i < ce) ? slot_load(part_slot(p, b, j, c0 + i)) : 0u;
+    for (int i = 0; i < kFoldSlotsPerThread; ++i) {  // issue every load before waiting on any
+      // on one code path: past the block's last slot a thread loads that slot again
+      const int q = min(tid + i * kThreads, n_slots - 1);
+      const int row = q / ncb;
+      v[i] = slot_load(part_slot(p, b, row_slot(p, K, row), cblk + q - row * ncb));
+    }
     // re-poll every slot still missing together, one round trip per round
     uint32_t missing = 0u;
 #pragma unroll
-    for (int i = 0; i < kFoldBlock; ++i)
-      if (active && c0 + i < ce && v[i] == 0u) missing |= 1u << i;
+    for (int i = 0; i < kFoldSlotsPerThread; ++i)
+      if (tid + i * kThreads < n_slots && v[i] == 0u) missing |= 1u << i;
     for (unsigned it = 0; missing != 0u && it < kSpinLimit; ++it) {
       __builtin_amdgcn_s_sleep(SV_FOLD_SLEEP);
 #pragma unroll
-      for (int i = 0; i < kFoldBlock; ++i)
-        if (missing & (1u << i)) v[i] = slot_load(part_slot(p, b, j, c0 + i));
+      for (int i = 0; i < kFoldSlotsPerThread; ++i) {
+        if (missing & (1u << i)) {
+          const int q = tid + i * kThreads;
+          const int row = q / ncb;
+          v[i] = slot_load(part_slot(p, b, row_slot(p, K, row), cblk + q - row * ncb));
+        }
+      }
 #pragma unroll
-      for (int i = 0; i < kFoldBlock; ++i)
+      for (int i = 0; i < kFoldSlotsPerThread; ++i)
         if ((missing & (1u << i)) && v[i] != 0u) missing &= ~(1u << i);
     }
     if (missing != 0u) expired = true;
-    if (!active) continue;
-    if constexpr (GREEDY) {
 #pragma unroll
-      for (int i = 0; i < kFoldBlock; ++i)
-        if (c0 + i < ce && v[i] != 0u)
-          merge_argmax(M, I, slot_f(v[i]), static_cast<int>(slot_w(v[i])));
+    for (int i = 0; i < kFoldSlotsPerThread; ++i) {
+      const int q = tid + i * kThreads;
+      if (q < n_slots) sh.slots[q] = v[i];
+    }
+    __syncthreads();
+    if (!active) continue;
+    // wave w merges chunks [cb, ce) of the block for row = lane
+    const int cpw = (ncb + kWaves - 1) / kWaves;
+    const int cb = wave * cpw;
+    const int ce = min(cb + cpw, ncb);
+    const uint64_t* rs = sh.slots + lane * ncb;
+    if constexpr (GREEDY) {
+      for (int c = cb; c < ce; ++c) {
+        const uint64_t x = rs[c];
+        if (x != 0u) merge_argmax(M, I, slot_f(x), static_cast<int>(slot_w(x)));
+      }
     } else {
       float bm = M;
-#pragma unroll
-      for (int i = 0; i < kFoldBlock; ++i)
-        if (c0 + i < ce && v[i] != 0u) bm = fmaxf(bm, slot_f(v[i]));
+      for (int c = cb; c < ce; ++c) {
+        const uint64_t x = rs[c];
+        if (x != 0u) bm = fmaxf(bm, slot_f(x));
+      }
       const float bmc = (bm == -INFINITY) ? 0.f : scaled_max(bm, cf);
       S *= rescale(M, cf, bmc);
-#pragma unroll
-      for (int i = 0; i < kFoldBlock; ++i)
-        if (c0 + i < ce && v[i] != 0u)
-          S += __uint_as_float(slot_w(v[i])) * rescale(slot_f(v[i]), cf, bmc);
+      for (int c = cb; c < ce; ++c) {
+        const uint64_t x = rs[c];
+        if (x != 0u) S += __uint_as_float(slot_w(x)) * rescale(slot_f(x), cf, bmc);
+      }
       M = bm;
     }
   }
