@@ -8,6 +8,9 @@ What it computes is stated in ``spec_oracle.c``: the exact accept / residual /
 bonus rule and the greedy case of "Decodificación Especulativa y EAGLE"
 (section "La Regla de Exactitud"), with randomness drawn from Philox4x32-10 by
 counter, so that a result is a pure function of the inputs and the seed.
+It also holds the draft-side sampler that precedes verification
+(``draft_sample``: one token per request from softmax(z/T), or the argmax at
+T = 0).
 """
 from __future__ import annotations
 
@@ -63,6 +66,12 @@ def load(path: str = LIB):
         ctypes.c_int, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         vp, vp, vp, ctypes.c_uint64, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_spec_verify.restype = ctypes.c_int
+    lib.oracle_draft_exponential.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32]
+    lib.oracle_draft_exponential.restype = ctypes.c_double
+    lib.oracle_draft_sample.argtypes = [ctypes.c_int, vp, ctypes.c_int32, ctypes.c_int32, vp,
+                                        ctypes.c_uint64, ctypes.c_int32, vp, vp, vp, vp]
+    lib.oracle_draft_sample.restype = ctypes.c_int
     if path == LIB:
         _lib = lib
     return lib
@@ -148,3 +157,33 @@ def verify_batch(batch, reqs=None, greedy_only: bool = False, lib=None) -> dict:
     return verify(batch.dtype, batch.target, None if greedy_only else batch.draft,
                   batch.offsets, batch.tokens, temp, batch.seed, batch.V, batch.max_k,
                   reqs=reqs, lib=lib, n_draft_rows=batch.n_draft_rows)
+
+
+def draft_exponential(seed: int, b: int, step: int, v: int, lib=None) -> float:
+    return (lib or load()).oracle_draft_exponential(seed, b, step, v)
+
+
+def draft_sample(dtype: int, logits, temperature, seed: int, step: int, lib=None) -> dict:
+    """Draft-side sampler over B rows of logits [B, V] (one row per request).
+
+    Returns numpy arrays: tokens [B] (int32, -1 for a bad row or temperature),
+    q_at [B] (float64 softmax probability of the drawn token, NaN at T == 0),
+    flags [B] (bit 2: near tie in the race) and race_gap [B].
+    """
+    lib = lib or load()
+    np_dt = {F32: np.float32, BF16: np.uint16, F64: np.float64}.get(dtype)
+    if np_dt is None:
+        raise ValueError(f"unknown dtype {dtype}")
+    logits = np.ascontiguousarray(logits, dtype=np_dt)
+    B, V = logits.shape
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    tokens = np.full(B, -2, dtype=np.int32)
+    q_at = np.full(B, np.nan)
+    flags = np.zeros(B, dtype=np.uint32)
+    gap = np.full(B, np.nan)
+    rc = lib.oracle_draft_sample(dtype, _ptr(logits), B, V, _ptr(temperature),
+                                 ctypes.c_uint64(seed), step, _ptr(tokens), _ptr(q_at),
+                                 _ptr(flags), _ptr(gap))
+    if rc != 0:
+        raise ValueError(f"oracle_draft_sample rejected its arguments (rc={rc})")
+    return dict(tokens=tokens, q_at=q_at, flags=flags, race_gap=gap)

@@ -31,6 +31,11 @@
  *     r_t is word 0 of counter (0, t, request, 1);
  *   - U(x) = (2*(x >> 9) + 1) * 2^-24, an exact value in (0, 1).
  *
+ * It also holds the draft-side sampler that precedes verification
+ * (oracle_draft_sample, at the end of this file): one token per request from
+ * softmax(z / T) by the same kind of race on its own Philox stream (tag 2),
+ * or the argmax at T = 0.
+ *
  * Philox4x32-10 is written from its published definition (Salmon, Moraes,
  * Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): ten
  * rounds of two 32x32->64 multiplies, with a Weyl-sequence key schedule.
@@ -103,6 +108,12 @@ double oracle_accept_uniform(uint64_t seed, int32_t b, int32_t t) {
 /* Exponential variate E_v = -ln U_v of the race at (request b, position pos). */
 double oracle_race_exponential(uint64_t seed, int32_t b, int32_t pos, int32_t v) {
   uint32_t x = philox_word(seed, (uint32_t)v >> 2, (uint32_t)pos, (uint32_t)b, 0u, v & 3);
+  return -log(oracle_u01(x));
+}
+
+/* Exponential variate of the draft-side sampler at (request b, draft step). */
+double oracle_draft_exponential(uint64_t seed, int32_t b, int32_t step, int32_t v) {
+  uint32_t x = philox_word(seed, (uint32_t)v >> 2, (uint32_t)step, (uint32_t)b, 2u, v & 3);
   return -log(oracle_u01(x));
 }
 
@@ -344,6 +355,61 @@ int oracle_spec_verify(int dtype, const void* target, const void* draft, int32_t
     }
   } else {
     for (int32_t b = 0; b < B; ++b) oracle_verify_one(&in, &o, b);
+  }
+  return 0;
+}
+
+/*
+ * Draft-side sampler: the drafting step that precedes verification.  The
+ * lesson's concept (section "El Concepto", step 1) and its listing draw each
+ * draft token from softmax(q / T); Perplexity's draft-target scheme takes the
+ * top token at every draft step (greedy drafting, T = 0).  Row b of `logits`
+ * is the draft model's output for request b at draft step `step`.
+ *   T == 0: x = lowest index attaining the row maximum;
+ *   T > 0:  x = argmax_v (z_v / T - ln E_v) with E_v = -ln U_v, U_v from
+ *           Philox4x32-10 keyed by the seed, counter (v >> 2, step, b, 2),
+ *           word v & 3 (stream tag 2, apart from the verify step's tags 0
+ *           and 1); ties to the lowest index.  An exponential race, so x is
+ *           an exact draw from softmax(z / T).
+ * q_at[b] = exp(z_x / T - lse(z / T)) for T > 0 (NaN when T == 0).  A near
+ * tie (best - second < 1e-6 * max(1, |best|)) sets flags[b] bit 2.  A bad
+ * temperature (negative, NaN, infinite) or a row with no finite maximum
+ * gives x = -1.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_draft_sample(int dtype, const void* logits, int32_t B, int32_t V,
+                        const float* temperature, uint64_t seed, int32_t step, int32_t* tokens,
+                        double* q_at, uint32_t* flags, double* race_gap) {
+  if (!logits || !temperature || !tokens || B < 1 || V < 1) return -1;
+  if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_F64) return -1;
+  for (int32_t b = 0; b < B; ++b) {
+    const double T = (double)temperature[b];
+    if (flags) flags[b] = 0;
+    if (q_at) q_at[b] = NAN;
+    if (race_gap) race_gap[b] = NAN;
+    tokens[b] = -1;
+    if (!isfinite(T) || T < 0.0) continue;
+    if (T == 0.0) {
+      tokens[b] = row_argmax(logits, dtype, b, V);
+      continue;
+    }
+    const double lse = row_lse(logits, dtype, b, V, T);
+    if (!isfinite(lse)) continue;
+    double best = -INFINITY, second = -INFINITY;
+    int32_t x = -1;
+    for (int32_t v = 0; v < V; ++v) {
+      double key = logit(logits, dtype, b, V, v) / T - log(oracle_draft_exponential(seed, b, step, v));
+      if (key > best) {
+        second = best;
+        best = key;
+        x = v;
+      } else if (key > second) {
+        second = key;
+      }
+    }
+    tokens[b] = x;
+    if (x >= 0 && q_at) q_at[b] = exp(logit(logits, dtype, b, V, x) / T - lse);
+    if (race_gap) race_gap[b] = best - second;
+    if (best - second < 1e-6 * fmax(1.0, fabs(best)) && flags) flags[b] |= OR_FLAG_RACE_NEAR_TIE;
   }
   return 0;
 }

@@ -540,7 +540,73 @@ def pin_faults(lib):
     assert res["accept_len"][0] >= 0 and res["accept_len"][2] >= 0
 
 
+# ------------------------------------------------------------------ draft-side sampler
+
+
+def pin_draft_distribution(lib, V=8, N=400_000):
+    """The draft sampler draws exactly from softmax(z / T) (exponential race), at two T."""
+    rng = np.random.default_rng(21)
+    z = rng.normal(0, 1.5, size=V)
+    for T, seed in ((1.3, 5), (0.45, 6)):
+        Tf = float(np.float32(T))
+        p = scipy.special.softmax(z / Tf)
+        res = oracle.draft_sample(oracle.F64, np.tile(z, (N, 1)), np.full(N, T, np.float32),
+                                  seed, 3, lib=lib)
+        hist = np.bincount(res["tokens"], minlength=V) / N
+        assert 0.5 * np.abs(hist - p).sum() < 0.005, (T, hist, p)
+        assert scipy.stats.chisquare(hist * N, p * N).pvalue > 1e-5
+        # q(x) is the softmax probability of the drawn token
+        assert np.allclose(res["q_at"], p[res["tokens"]], rtol=1e-12, atol=0)
+
+
+def pin_draft_greedy(lib):
+    """T = 0 takes the first maximum (numpy's argmax), ties included."""
+    rng = np.random.default_rng(22)
+    B, V = 300, 33
+    z = rng.integers(-3, 4, size=(B, V)).astype(np.float64)  # many ties
+    res = oracle.draft_sample(oracle.F64, z, np.zeros(B, np.float32), 1, 0, lib=lib)
+    assert (res["tokens"] == np.argmax(z, axis=1)).all()
+    assert np.isnan(res["q_at"]).all()
+
+
+def pin_draft_streams(lib, V=5, N=200_000):
+    """Draft steps are independent draws, and independent of the verify step's race.
+
+    The joint law of the tokens drawn at steps 0 and 1 for the same requests is
+    the product law; the step-0 token agrees with the verify step's K = 0
+    plain sample (same seed, request and position) only as often as two
+    independent draws do (sum p^2), so the draft stream is a separate stream.
+    """
+    rng = np.random.default_rng(23)
+    z = rng.normal(0, 1.0, size=V)
+    p = scipy.special.softmax(z)
+    rows = np.tile(z, (N, 1))
+    temp = np.ones(N, np.float32)
+    a = oracle.draft_sample(oracle.F64, rows, temp, 9, 0, lib=lib)["tokens"]
+    b = oracle.draft_sample(oracle.F64, rows, temp, 9, 1, lib=lib)["tokens"]
+    joint = np.bincount(a * V + b, minlength=V * V)
+    assert scipy.stats.chisquare(joint, np.outer(p, p).ravel() * N).pvalue > 1e-5
+    v = oracle.verify(oracle.F64, rows, np.zeros((0, V)), np.zeros(N + 1, np.int32),
+                      np.zeros(0, np.int32), temp, 9, V, 0, lib=lib)["out_tokens"]
+    same = (a == v).mean()
+    want = float((p * p).sum())
+    assert abs(same - want) < 5 * math.sqrt(want * (1 - want) / N), (same, want)
+
+
+def pin_draft_faults(lib):
+    """A bad temperature or a row with no finite maximum gives -1 for that request only."""
+    rng = np.random.default_rng(24)
+    B, V = 6, 12
+    z = rng.normal(size=(B, V))
+    temp = np.array([1.0, -1.0, np.nan, np.inf, 0.7, 0.0], np.float32)
+    z[4, :] = -np.inf
+    res = oracle.draft_sample(oracle.F64, z, temp, 2, 0, lib=lib)
+    assert list(res["tokens"][1:5]) == [-1, -1, -1, -1]
+    assert 0 <= res["tokens"][0] < V and res["tokens"][5] == int(np.argmax(z[5]))
+
+
 ALL_PINS = [pin_philox_kat, pin_philox_rocrand, pin_u01, pin_softmax_vs_scipy,
             pin_greedy_vs_numpy, pin_exact_enumeration, pin_plain_sampling, pin_closed_form,
             pin_temperature_invariance, pin_identical_draft_accepts, pin_disjoint_draft_rejects,
-            pin_faults]
+            pin_faults, pin_draft_distribution, pin_draft_greedy, pin_draft_streams,
+            pin_draft_faults]

@@ -50,6 +50,18 @@ MUTANTS = {
                           "uint64_t p0 = (uint64_t)M1 * (uint64_t)c0;"),
     # Philox: wrong key increment
     "philox_key_schedule": ("k1 += W1;", "k1 += W0;"),
+    # draft sampler: exponential variate added instead of subtracted
+    "draft_race_sign": ("/ T - log(oracle_draft_exponential(seed, b, step, v));",
+                        "/ T + log(oracle_draft_exponential(seed, b, step, v));"),
+    # draft sampler: the draft step left out of the counter
+    "draft_step_ignored": ("(uint32_t)v >> 2, (uint32_t)step, (uint32_t)b, 2u",
+                           "(uint32_t)v >> 2, 0u, (uint32_t)b, 2u"),
+    # draft sampler: the verify race's stream tag reused
+    "draft_stream_tag": ("(uint32_t)v >> 2, (uint32_t)step, (uint32_t)b, 2u",
+                         "(uint32_t)v >> 2, (uint32_t)step, (uint32_t)b, 0u"),
+    # draft sampler: temperature ignored in the race key
+    "draft_untempered": ("double key = logit(logits, dtype, b, V, v) / T - log(",
+                         "double key = logit(logits, dtype, b, V, v) - log("),
     # uniform map that can return 0
     "u01_map": ("return (2.0 * (double)(x >> 9) + 1.0) / 16777216.0;",
                 "return (double)(x >> 8) / 16777216.0;"),
@@ -59,7 +71,8 @@ MUTANTS = {
 ORDER = [P.pin_philox_kat, P.pin_u01, P.pin_softmax_vs_scipy, P.pin_greedy_vs_numpy,
          P.pin_temperature_invariance, P.pin_identical_draft_accepts,
          P.pin_disjoint_draft_rejects, P.pin_faults, P.pin_plain_sampling,
-         P.pin_exact_enumeration, P.pin_closed_form]
+         P.pin_exact_enumeration, P.pin_closed_form, P.pin_draft_greedy, P.pin_draft_faults,
+         P.pin_draft_distribution, P.pin_draft_streams]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
