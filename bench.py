@@ -33,7 +33,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified draft positions/sec + HBM GB/s (% peak), B=64 K=4 V=128256 bf16"
-SRC = os.path.join(ROOT, "rejection_sampling_verify_scaled_amd", "csrc", "spec_verify.hip")
+# the verify kernel's sources: committed traffic counters apply while these are unchanged
+KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_scaled_amd", "csrc", name)
+                  for name in ("spec_verify.hip", "device_common.h")]
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -98,9 +108,7 @@ def traffic_record(workload: int):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != kernel_source_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
 

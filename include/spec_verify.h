@@ -134,6 +134,48 @@ int spec_verify_sample_timed(const void* target_logits, const void* draft_logits
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* event_start, void* event_end);
 
+/* ---------------------------------------------------------------- draft side */
+
+/* Host function.  Workspace bytes spec_draft_sample needs for B rows of V
+ * logits (either dtype); 0 for B < 1 or V < 1.  The workspace must be
+ * zero-filled once when allocated; every call leaves it zero again. */
+size_t spec_draft_workspace_bytes(int32_t B, int32_t V);
+
+/* Draft-side sampler: the drafting step that precedes verification draws
+ * each draft token from softmax(q / T) ("Decodificación Especulativa y
+ * EAGLE", section "El Concepto", step 1, and its listing's draft loop), or
+ * takes the top token at T = 0 (Perplexity's draft-target scheme drafts
+ * greedily).  One call draws one token for each of B requests, from row b of
+ * draft_logits, at draft step `step`:
+ *   temperature[b] == 0: tokens[b] = lowest index attaining the row maximum;
+ *   temperature[b] > 0:  tokens[b] = argmax_v (z_v / T - ln E_v), ties to the
+ *       lowest index, with E_v = -ln U_v and U_v from Philox4x32-10 keyed by
+ *       `seed`, counter (v >> 2, step, b, 2), word v & 3, mapped to
+ *       (2 (x >> 9) + 1) 2^-24.  An exponential race, so tokens[b] is an
+ *       exact draw from softmax(z / T); stream tag 2 keeps these draws apart
+ *       from the verify step's (tags 0 and 1).  Calling with step = t for
+ *       t = 0..K-1 gives independent draft steps.
+ *   draft_logits   device, [B][V] of `dtype`, row-major, contiguous
+ *   temperature    device, [B] float32; negative, NaN or infinite values fail
+ *                  that request (tokens[b] = -1)
+ *   seed, step     host; step >= 0
+ *   tokens         device out, [B] int32; -1 for a failed request: a bad
+ *                  temperature, a row with no finite maximum, a NaN or +inf
+ *                  logit in a sampled row, or an expired internal wait
+ *   q_at           device out, optional [B] float32: softmax(z / T) at
+ *                  tokens[b] for sampled requests, NaN for greedy or failed
+ *                  ones; may be NULL
+ *   workspace      device, >= spec_draft_workspace_bytes(B, V) bytes,
+ *                  16-byte aligned, zero-filled at allocation; calls that
+ *                  overlap in time need separate workspaces
+ *   stream         hipStream_t; the call only enqueues work on it
+ * Returns SV_OK, or a negative status with nothing enqueued (SV_ERR_NULL for
+ * a missing required pointer, SV_ERR_SHAPE for B < 1, V < 1 or step < 0,
+ * SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_LAUNCH). */
+int spec_draft_sample(const void* draft_logits, int32_t dtype, int32_t B, int32_t V,
+                      const float* temperature, uint64_t seed, int32_t step, int32_t* tokens,
+                      float* q_at, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host function.  Static description of a status code. */
 const char* spec_verify_status_string(int status);
 

@@ -54,6 +54,10 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_sample.restype = ctypes.c_int
     lib.spec_verify_sample_timed.argtypes = list(lib.spec_verify_sample.argtypes) + [vp, vp]
     lib.spec_verify_sample_timed.restype = ctypes.c_int
+    lib.spec_draft_workspace_bytes.argtypes = [i32, i32]
+    lib.spec_draft_workspace_bytes.restype = sz
+    lib.spec_draft_sample.argtypes = [vp, i32, i32, i32, vp, u64, i32, vp, vp, vp, sz, vp]
+    lib.spec_draft_sample.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -66,7 +70,7 @@ def header_functions(header: str = HEADER):
     with open(header) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|draft)_\w+)\s*\(", text)))
 
 
 def workspace_bytes(B: int, V: int, max_k: int) -> int:
@@ -185,6 +189,40 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     if rc != 0:
         raise SpecVerifyError("spec_verify_sample", rc, lib.spec_verify_status_string(rc).decode())
     return accept_len, out_tokens, p_at_draft, q_at_draft
+
+
+def draft_workspace_bytes(B: int, V: int) -> int:
+    return int(load_library().spec_draft_workspace_bytes(B, V))
+
+
+def spec_draft_sample(draft_logits: torch.Tensor, temperature: torch.Tensor, seed: int,
+                      step: int, tokens: Optional[torch.Tensor] = None,
+                      q_at: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      want_q: bool = True):
+    """Draft-side sampler over rows [B, V]; returns (tokens [B] int32, q_at [B] or None)."""
+    lib = load_library()
+    if draft_logits.dim() != 2 or not draft_logits.is_contiguous():
+        raise ValueError("draft_logits must be a contiguous [B, V] tensor")
+    B, V = draft_logits.shape
+    device = draft_logits.device
+    _check(temperature, "temperature", torch.float32, (B,), device)
+    if tokens is None:
+        tokens = torch.empty(B, dtype=torch.int32, device=device)
+    _check(tokens, "tokens", torch.int32, (B,), device)
+    if q_at is None and want_q:
+        q_at = torch.empty(B, dtype=torch.float32, device=device)
+    if q_at is not None:
+        _check(q_at, "q_at", torch.float32, (B,), device)
+    if workspace is None:
+        workspace = torch.zeros(draft_workspace_bytes(B, V), dtype=torch.uint8, device=device)
+    rc = lib.spec_draft_sample(
+        _ptr(draft_logits), _dtype_code(draft_logits), B, V, _ptr(temperature),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), int(step), _ptr(tokens), _ptr(q_at),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if rc != 0:
+        raise SpecVerifyError("spec_draft_sample", rc, lib.spec_verify_status_string(rc).decode())
+    return tokens, q_at
 
 
 def to_device_batch(batch, device="cuda"):

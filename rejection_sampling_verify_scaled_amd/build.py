@@ -11,7 +11,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "spec_verify.hip")
+SRCS = [os.path.join(PKG, "csrc", "spec_verify.hip"), os.path.join(PKG, "csrc", "draft_sample.hip")]
+SRC = SRCS[0]  # the verify kernel's source (its sha256 keys the committed traffic counters)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
@@ -37,9 +38,9 @@ def hipcc() -> str:
 
 
 def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
-    """Compile the HIP source to ``out`` (a fresh temp file renamed into place)."""
+    """Compile the HIP sources to ``out`` (a fresh temp file renamed into place)."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,0 +1,301 @@
+// draft_sample.hip -- gfx950 kernel and C ABI of the draft-side sampler.
+//
+// What is computed is stated in include/spec_verify.h (spec_draft_sample):
+// the drafting step that precedes verification draws one token per request
+// from softmax(z / T) of its draft row ("Decodificación Especulativa y
+// EAGLE", section "El Concepto", step 1, and the listing's draft loop), or
+// takes the row's argmax when T = 0 (the top-token drafting of Perplexity's
+// draft-target scheme).
+//
+// One launch.  Row b is cut into 8 KiB chunks; workgroup g serves request
+// b = g / ng and the 4 chunks cg * 4 + wave (cg = g mod ng, one chunk per
+// wave).  A wave of a sampled request makes one pass over its chunk for the
+// maximum, then a second pass that, per token, forms the weight
+// w = 2^(z c - fl(m c)) (c = log2(e) / T, m the chunk maximum), adds it to
+// the chunk's softmax sum and runs the exponential race: the token with the
+// largest w / e wins, e = -log2 U from Philox4x32-10 on stream tag 2,
+// counter (v >> 2, step, b, 2), word v & 3.  Candidates are compared by
+// cross-multiplication; the chunk's winner becomes the log2-domain key
+// log2(w / e) + fl(m c), which is comparable across chunks.  A greedy wave
+// reduces its chunk to (max, lowest argmax).  Each chunk leaves one or two
+// 8-byte slots in the workspace; the request's last workgroup in grid order
+// folds them (larger key, then lower index; softmax sums rescaled to the
+// row maximum), gathers z at the winner for q(x), writes the outputs and
+// zeroes the slots.  Hand-offs use the same device-coherent zero-slot
+// protocol as the verify kernel; waits are bounded, and an expired wait
+// gives token -1.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "spec_verify.h"
+#include "device_common.h"
+
+namespace {
+
+constexpr uint32_t kDraftTag = 2u;  // Philox stream tag of the draft sampler
+
+struct DraftParams {
+  const void* logits;        // [B][V]
+  const float* temperature;  // [B]
+  uint32_t k0, k1;           // Philox key
+  int32_t B, V, step;
+  int32_t nc;          // chunks per row
+  int32_t ng;          // workgroups per row, ceil(nc / 4)
+  uint64_t* part;      // [B][nc][2]: statistics slot, race slot
+  int32_t* tokens;     // [B]
+  float* q_at;         // [B] or NULL
+};
+
+__device__ __forceinline__ uint64_t* stat_slot(const DraftParams& p, int b, int c) {
+  return p.part + (static_cast<int64_t>(b) * p.nc + c) * 2;
+}
+__device__ __forceinline__ uint64_t* race_slot(const DraftParams& p, int b, int c) {
+  return stat_slot(p, b, c) + 1;
+}
+
+// Statistics and race of one sampled chunk held by a wave (lane elements as
+// in load_item).  Returns the statistics slot (max, sum relative to fl(max c))
+// and sets the race slot (log2-domain key, index).
+template <bool BF16>
+__device__ __forceinline__ uint64_t chunk_race(const uint4* buf, int64_t e0, float cf, uint32_t b,
+                                               uint32_t step, uint32_t k0, uint32_t k1,
+                                               uint64_t& race) {
+  constexpr int EPV = elems_per_vec(BF16);
+  const int lane = threadIdx.x & 63;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kItemVecs; ++u) {
+    float xs[EPV];
+    unpack<BF16>(buf[u], xs);
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) mx = fmaxf(mx, xs[k]);
+  }
+  mx = wave_max(mx);
+  // offset 0 when there is no finite max keeps a NaN visible in the sum
+  const float mc = (mx == -INFINITY) ? 0.f : scaled_max(mx, cf);
+  float s = 0.f, bw = 0.f, be = 1.f;
+  int bi = INT_MAX;
+#pragma unroll
+  for (int u = 0; u < kItemVecs; ++u) {
+    float xs[EPV];
+    unpack<BF16>(buf[u], xs);
+    const int64_t v0 = e0 + static_cast<int64_t>(u * 64 + lane) * EPV;
+#pragma unroll
+    for (int h = 0; h < EPV / 4; ++h) {
+      const Philox4 r = philox_race(static_cast<uint32_t>((v0 >> 2) + h), step, b, kDraftTag, k0, k1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float w = fast_exp2(scaled_logit(xs[4 * h + k], cf, mc));
+        s += w;
+        const float e = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
+        if (w * be > bw * e) {
+          bw = w;
+          be = e;
+          bi = static_cast<int>(v0) + 4 * h + k;
+        }
+      }
+    }
+  }
+  s = wave_sum(s);
+  float key = bi == INT_MAX ? -INFINITY : fast_log2(bw / be) + mc;
+  wave_merge_argmax(key, bi);
+  race = pack_slot(key, static_cast<uint32_t>(bi));
+  return pack_slot(mx, __float_as_uint(s));
+}
+
+// Poll the slots a thread folds until all are written; false if a wait expired.
+__device__ __forceinline__ bool wait_slots(uint64_t* const* slot, uint64_t* v, int n) {
+  uint32_t missing = 0u;
+  for (int i = 0; i < n; ++i) {
+    v[i] = slot_load(slot[i]);
+    if (v[i] == 0u) missing |= 1u << i;
+  }
+  for (unsigned it = 0; missing != 0u && it < kSpinLimit; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    for (int i = 0; i < n; ++i) {
+      if (missing & (1u << i)) {
+        v[i] = slot_load(slot[i]);
+        if (v[i] != 0u) missing &= ~(1u << i);
+      }
+    }
+  }
+  return missing == 0u;
+}
+
+// The request's last workgroup: fold every chunk's slots, write the outputs,
+// zero the slots.  Thread t folds chunks t, t + 256, ... in order; threads
+// merge in a fixed tree (wave shuffles, then the waves in order).
+template <bool BF16>
+__device__ void draft_finish(const DraftParams& p, int b, float T) {
+  __shared__ float sh_m[kWaves], sh_s[kWaves], sh_k[kWaves];
+  __shared__ int sh_i[kWaves], sh_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const bool greedy = T == 0.f;
+  const float cf = greedy ? 0.f : kLog2e / T;
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  float M = -INFINITY, S = 0.f, key = -INFINITY;
+  int idx = INT_MAX;
+  bool expired = false;
+  for (int c = tid; c < p.nc; c += kThreads) {
+    uint64_t* slots[2] = {stat_slot(p, b, c), race_slot(p, b, c)};
+    uint64_t v[2];
+    if (!wait_slots(slots, v, greedy ? 1 : 2)) {
+      expired = true;
+      continue;
+    }
+    if (greedy) {
+      merge_argmax(M, idx, slot_f(v[0]), static_cast<int>(slot_w(v[0])));
+    } else {
+      merge_stats(M, S, slot_f(v[0]), __uint_as_float(slot_w(v[0])), cf);
+      merge_argmax(key, idx, slot_f(v[1]), static_cast<int>(slot_w(v[1])));
+    }
+    slot_store(slots[0], 0u);
+    if (!greedy) slot_store(slots[1], 0u);
+  }
+  if (expired) atomicOr(&sh_bad, 1);
+  // fixed-order tree over the workgroup
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64);
+    const float k2 = __shfl_xor(key, o, 64);
+    const int i2 = __shfl_xor(idx, o, 64);
+    if (greedy) {
+      merge_argmax(M, idx, m2, i2);
+    } else {
+      merge_stats(M, S, m2, s2, cf);
+      merge_argmax(key, idx, k2, i2);
+    }
+  }
+  if (lane == 0) {
+    sh_m[wave] = M;
+    sh_s[wave] = S;
+    sh_k[wave] = key;
+    sh_i[wave] = idx;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  M = sh_m[0];
+  S = sh_s[0];
+  key = sh_k[0];
+  idx = sh_i[0];
+  for (int w = 1; w < kWaves; ++w) {
+    if (greedy) {
+      merge_argmax(M, idx, sh_m[w], sh_i[w]);
+    } else {
+      merge_stats(M, S, sh_m[w], sh_s[w], cf);
+      merge_argmax(key, idx, sh_k[w], sh_i[w]);
+    }
+  }
+  const bool finite_max = M > -INFINITY && M < INFINITY;
+  const bool ok = !sh_bad && finite_max && idx != INT_MAX && (greedy || S < INFINITY);
+  p.tokens[b] = ok ? idx : -1;
+  if (p.q_at) {
+    float q = NAN;
+    if (ok && !greedy) {
+      const float zx = load_logit<BF16>(p.logits, static_cast<int64_t>(b) * p.V + idx);
+      q = fast_exp2(scaled_logit(zx, cf, scaled_max(M, cf)) - fast_log2(S));
+    }
+    p.q_at[b] = q;
+  }
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void sd_sample(DraftParams p) {
+  constexpr int CHUNK = chunk_tokens(BF16);
+  const int g = blockIdx.x;
+  const int b = g / p.ng;
+  const int cg = g - b * p.ng;
+  const float T = p.temperature[b];
+  // NaN, negative and infinite temperatures fail the request
+  if (!(T >= 0.f && T < INFINITY)) {
+    if (cg == p.ng - 1 && threadIdx.x == 0) {
+      p.tokens[b] = -1;
+      if (p.q_at) p.q_at[b] = NAN;
+    }
+    return;
+  }
+  const int c = cg * kWaves + wave_id();
+  if (c < p.nc) {
+    uint4 buf[kItemVecs];
+    const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
+    load_item<BF16, VEC>(p.logits, b, p.V, e0, buf);
+    if (VEC && e0 + CHUNK > p.V) mask_tail<BF16>(buf, p.V, e0);
+    const int lane = threadIdx.x & 63;
+    if (T == 0.f) {
+      const uint64_t v = item_argmax<BF16>(buf, e0);
+      if (lane == 0) slot_store(stat_slot(p, b, c), v);
+    } else {
+      uint64_t race;
+      const uint64_t v = chunk_race<BF16>(buf, e0, kLog2e / T, static_cast<uint32_t>(b),
+                                          static_cast<uint32_t>(p.step), p.k0, p.k1, race);
+      if (lane == 0) {
+        slot_store(stat_slot(p, b, c), v);
+        slot_store(race_slot(p, b, c), race);
+      }
+    }
+  }
+  if (cg == p.ng - 1) draft_finish<BF16>(p, b, T);
+}
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Sized with the float32 chunk (the smaller one, so more chunks): either dtype fits.
+size_t draft_workspace(int32_t B, int32_t V) {
+  const int64_t nc = ceil_div64(V, chunk_tokens(false));
+  return static_cast<size_t>(B) * static_cast<size_t>(nc) * 2 * sizeof(uint64_t);
+}
+
+template <bool BF16, bool VEC>
+int draft_launch(const DraftParams& prm, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((sd_sample<BF16, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
+                     0, stream, prm);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_draft_workspace_bytes(int32_t B, int32_t V) {
+  if (B < 1 || V < 1) return 0;
+  return draft_workspace(B, V);
+}
+
+int spec_draft_sample(const void* draft_logits, int32_t dtype, int32_t B, int32_t V,
+                      const float* temperature, uint64_t seed, int32_t step, int32_t* tokens,
+                      float* q_at, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!draft_logits || !temperature || !tokens || !workspace) return SV_ERR_NULL;
+  if (B < 1 || V < 1 || step < 0) return SV_ERR_SHAPE;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (workspace_bytes < draft_workspace(B, V) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return SV_ERR_WORKSPACE;
+  const bool bf16 = dtype == SV_BF16;
+  DraftParams prm;
+  prm.logits = draft_logits;
+  prm.temperature = temperature;
+  prm.k0 = static_cast<uint32_t>(seed);
+  prm.k1 = static_cast<uint32_t>(seed >> 32);
+  prm.B = B;
+  prm.V = V;
+  prm.step = step;
+  prm.nc = static_cast<int32_t>(ceil_div64(V, chunk_tokens(bf16)));
+  prm.ng = static_cast<int32_t>(ceil_div64(prm.nc, kWaves));
+  prm.part = static_cast<uint64_t*>(workspace);
+  prm.tokens = tokens;
+  prm.q_at = q_at;
+  const int64_t grid = static_cast<int64_t>(B) * prm.ng;
+  if (grid > INT32_MAX) return SV_ERR_SHAPE;
+  const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
+  const bool vec = row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(draft_logits) & 15u) == 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bf16) return vec ? draft_launch<true, true>(prm, grid, s) : draft_launch<true, false>(prm, grid, s);
+  return vec ? draft_launch<false, true>(prm, grid, s) : draft_launch<false, false>(prm, grid, s);
+}
+
+}  // extern "C"

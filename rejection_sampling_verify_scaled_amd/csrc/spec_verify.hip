@@ -60,21 +60,14 @@
 #include <cstdint>
 
 #include "spec_verify.h"
+#include "device_common.h"
 
 namespace {
 
-constexpr int kThreads = 256;  // 4 wave64s per workgroup
-constexpr int kWaves = kThreads / 64;
-constexpr int kItemVecs = 8;                      // 16-byte loads per lane per row-chunk
-constexpr int kItemsInFlight = 2;                 // row-chunks a wave loads before reducing
-constexpr int kGroupItems = kWaves * kItemsInFlight;  // flat grouping: row-chunks per workgroup
-constexpr int kChunkBytes = 64 * kItemVecs * 16;  // one row-chunk: 8 KiB
 constexpr int kRowsMax = 2 * SV_KMAX + 1;         // row slots per request
 constexpr int kFoldChunks = 64;                   // chunks per block of a fold
 constexpr int kFoldSlotsPerThread = (kRowsMax * kFoldChunks + 255) / 256;  // slots a thread loads per block
-constexpr unsigned kSpinLimit = 1u << 16;
 constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
-constexpr float kLog2e = 1.4426950408889634f;
 // s_sleep units (64 clocks each) between polling rounds of a fold
 #ifndef SV_FOLD_SLEEP
 #define SV_FOLD_SLEEP 1
@@ -83,210 +76,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // waves per SIMD, so five 4-wave workgroups per CU).
 constexpr int kWorkgroupsPerCu = 5;
 
-__device__ __forceinline__ int ceil_div_dev(int a, int b) { return (a + b - 1) / b; }
-__host__ __device__ constexpr int elems_per_vec(bool bf16) { return bf16 ? 8 : 4; }
-__host__ __device__ constexpr int chunk_tokens(bool bf16) { return kChunkBytes / (bf16 ? 2 : 4); }
-
-// ------------------------------------------------------------------ helpers
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <bool BF16>
-__device__ __forceinline__ float load_logit(const void* base, int64_t i) {
-  if constexpr (BF16) {
-    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[i]) << 16);
-  } else {
-    return static_cast<const float*>(base)[i];
-  }
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-// Philox4x32-10 (Salmon et al., SC'11): ten rounds, each two 32x32->64
-// products; the key advances by the Weyl constants between rounds.
-struct Philox4 {
-  uint32_t w[4];
-};
-
-constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
-constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
-
-__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
-                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t a = static_cast<uint64_t>(kPhiloxM0) * c0;
-    const uint64_t d = static_cast<uint64_t>(kPhiloxM1) * c2;
-    const uint32_t n0 = static_cast<uint32_t>(d >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(a >> 32) ^ c3 ^ k1;
-    c1 = static_cast<uint32_t>(d);
-    c3 = static_cast<uint32_t>(a);
-    c0 = n0;
-    c2 = n2;
-    k0 += kPhiloxW0;
-    k1 += kPhiloxW1;
-  }
-  return Philox4{{c0, c1, c2, c3}};
-}
-
-// a ^ b ^ k in one instruction (gfx950's three-input bit operation; 0x96 is
-// the truth table of three-way exclusive or).  k is wave-uniform.
-__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
-  uint32_t r;
-  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
-}
-
-// The same generator for race counters (c0, c1, c2, 0) with c1, c2 and the key
-// wave-uniform.  Rounds 1-3 still mix uniform words (the compiler keeps those
-// on the scalar unit); from round 4 on every word varies per lane and each
-// output word takes one three-input xor.
-__device__ __forceinline__ Philox4 philox_race(uint32_t c0, uint32_t c1, uint32_t c2,
-                                               uint32_t k0, uint32_t k1) {
-  uint32_t c3 = 0u;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t a = static_cast<uint64_t>(kPhiloxM0) * c0;
-    const uint64_t d = static_cast<uint64_t>(kPhiloxM1) * c2;
-    uint32_t n0, n2;
-    if (r < 3) {
-      n0 = static_cast<uint32_t>(d >> 32) ^ c1 ^ k0;
-      n2 = static_cast<uint32_t>(a >> 32) ^ c3 ^ k1;
-    } else {
-      n0 = xor3(static_cast<uint32_t>(d >> 32), c1, k0);
-      n2 = xor3(static_cast<uint32_t>(a >> 32), c3, k1);
-    }
-    c1 = static_cast<uint32_t>(d);
-    c3 = static_cast<uint32_t>(a);
-    c0 = n0;
-    c2 = n2;
-    k0 += kPhiloxW0;
-    k1 += kPhiloxW1;
-  }
-  return Philox4{{c0, c1, c2, c3}};
-}
-
-// (2 * (x >> 9) + 1) * 2^-24, exact in float32, strictly inside (0, 1): the
-// float 1 + (x >> 9) 2^-23 (one funnel shift puts x >> 9 under the exponent
-// bits of 1.0) minus (1 - 2^-24); both lie in [0.5, 2], so the difference is
-// exact (Sterbenz).
-__device__ __forceinline__ float uniform_open01(uint32_t x) {
-  const uint32_t one_plus = __builtin_amdgcn_alignbit(0x7Fu, x, 9u);  // 0x3F800000 | x >> 9
-  return __uint_as_float(one_plus) - 0x1.fffffep-1f;
-}
-
-// fl(m * c): the row-maximum offset, rounded once (the build disables
-// contraction), so every place that needs it gets the identical float.
-__device__ __forceinline__ float scaled_max(float m, float cf) { return m * cf; }
-
-// log2 of the unnormalised weight 2^(z c - fl(m c)).
-__device__ __forceinline__ float scaled_logit(float z, float cf, float mc) {
-  return __fmaf_rn(z, cf, -mc);
-}
-
-// 2^(fl(m c) - Mc) for a partial with maximum m merging under offset Mc;
-// 0 for a partial with no finite maximum (0 * s keeps a NaN sum NaN).
-__device__ __forceinline__ float rescale(float m, float cf, float Mc) {
-  return (m == -INFINITY) ? 0.f : fast_exp2(scaled_max(m, cf) - Mc);
-}
-
-// (max, sum) pairs; a sum s is relative to fl(max * c).
-__device__ __forceinline__ void merge_stats(float& m, float& s, float m2, float s2, float cf) {
-  const float M = fmaxf(m, m2);
-  const float Mc = scaled_max(M, cf);
-  s = s * rescale(m, cf, Mc) + s2 * rescale(m2, cf, Mc);
-  m = M;
-}
-
-// Larger value wins; equal values keep the lower index.
-__device__ __forceinline__ void merge_argmax(float& v, int& i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-__device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, 64);
-    const int i2 = __shfl_xor(i, o, 64);
-    merge_argmax(v, i, v2, i2);
-  }
-}
-
-// All threads end with the workgroup's (key, idx) winner.
-__device__ __forceinline__ void block_argmax(float& key, int& idx, float* sh_k, int* sh_i) {
-  wave_merge_argmax(key, idx);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) {
-    sh_k[wave] = key;
-    sh_i[wave] = idx;
-  }
-  __syncthreads();
-  key = sh_k[0];
-  idx = sh_i[0];
-  for (int w = 1; w < kWaves; ++w) merge_argmax(key, idx, sh_k[w], sh_i[w]);
-}
-
-// This wave's index in the workgroup, known to the compiler as wave-uniform
-// (so per-wave decisions become scalar branches, not exec-masked ones).
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// A value every lane holds equally, moved to a scalar register.
-__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ float uniform_float(float v) {
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
-}
-
-// ------------------------------------------------------------------ hand-off slots
-
-// (float, word) packed so a written slot is never all-zero bits.
-__device__ __forceinline__ uint64_t pack_slot(float a, uint32_t b) {
-  uint32_t ab = __float_as_uint(a);
-  if (ab == 0u) ab = 0x80000000u;  // +0.0 -> -0.0 (equal as a number)
-  return static_cast<uint64_t>(ab) | (static_cast<uint64_t>(b) << 32);
-}
-__device__ __forceinline__ float slot_f(uint64_t v) {
-  return __uint_as_float(static_cast<uint32_t>(v));
-}
-__device__ __forceinline__ uint32_t slot_w(uint64_t v) { return static_cast<uint32_t>(v >> 32); }
-
-__device__ __forceinline__ void slot_store(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t slot_load(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Poll until the slot is written; 0 if the bounded wait expires.
-__device__ uint64_t slot_wait(const uint64_t* p) {
-  uint64_t v = slot_load(p);
-  for (unsigned it = 0; v == 0u && it < kSpinLimit; ++it) {
-    __builtin_amdgcn_s_sleep(2);
-    v = slot_load(p);
-  }
-  return v;
-}
-
-// Drain this thread's outstanding memory operations, so device-coherent
-// stores made so far are acknowledged before the next access.  The signal
-// fences keep the compiler from moving memory accesses across the wait.
 // ------------------------------------------------------------------ parameters
 
 struct Params {
@@ -364,159 +153,6 @@ __device__ void clear_request(const Params& p, int b, int K, int nrows) {
     const int r = i / p.nc;
     slot_store(part_slot(p, b, row_slot(p, K, r), i - r * p.nc), 0u);
   }
-}
-
-// ------------------------------------------------------------------ statistics
-
-// One wave's share of a row-chunk: lane elements e0 + (u * 64 + lane) * EPV +
-// [0, EPV), u = 0..kItemVecs-1.  The vector path loads every vector from an
-// in-row address (indices clamped to the row's last vector) on one code path,
-// so the loads of several row-chunks stay in flight together; mask_tail then
-// replaces the vectors past the row end with -inf.  The scalar path reads -inf
-// past V itself.
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void load_item(const void* base, int64_t row, int V, int64_t e0,
-                                          uint4* out) {
-  constexpr int EPV = elems_per_vec(BF16);
-  const int lane = threadIdx.x & 63;
-  if constexpr (VEC) {
-    const uint4* rowv = reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
-                                                       row * V * (BF16 ? 2 : 4));
-    const int last = V / EPV - 1;
-    const int i0 = static_cast<int>(e0 / EPV) + lane;
-#pragma unroll
-    for (int u = 0; u < kItemVecs; ++u) out[u] = rowv[min(i0 + u * 64, last)];
-  } else {
-    const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
-    const int64_t rb = row * V;
-#pragma unroll
-    for (int u = 0; u < kItemVecs; ++u) {
-      const int64_t e = e0 + static_cast<int64_t>(u * 64 + lane) * EPV;
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (BF16) {
-          const uint16_t* b16 = static_cast<const uint16_t*>(base);
-          const uint32_t lo = (e + 2 * k < V) ? b16[rb + e + 2 * k] : 0xff80u;
-          const uint32_t hi = (e + 2 * k + 1 < V) ? b16[rb + e + 2 * k + 1] : 0xff80u;
-          w[k] = lo | (hi << 16);
-        } else {
-          w[k] = (e + k < V) ? __float_as_uint(static_cast<const float*>(base)[rb + e + k])
-                             : ninf;
-        }
-      }
-      out[u] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
-}
-
-// Vector path, row-chunk reaching past the row end: vectors past it become -inf.
-template <bool BF16>
-__device__ __forceinline__ void mask_tail(uint4* buf, int V, int64_t e0) {
-  constexpr int EPV = elems_per_vec(BF16);
-  const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
-  const int last = V / EPV - 1;
-  const int i0 = static_cast<int>(e0 / EPV) + (threadIdx.x & 63);
-#pragma unroll
-  for (int u = 0; u < kItemVecs; ++u)
-    if (i0 + u * 64 > last) buf[u] = make_uint4(ninf, ninf, ninf, ninf);
-}
-
-template <bool BF16>
-__device__ __forceinline__ void unpack(const uint4& v, float* xs) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  if constexpr (BF16) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      xs[2 * k] = bf16_lo(w[k]);
-      xs[2 * k + 1] = bf16_hi(w[k]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) xs[k] = __uint_as_float(w[k]);
-  }
-}
-
-// Partial of one row-chunk held by the wave: (max, sum of 2^(z c - fl(max c))).
-// One pass: each vector's sum is formed relative to the vector's own maximum,
-// then rescaled to the wave maximum.
-template <bool BF16>
-__device__ __forceinline__ uint64_t item_stats(const uint4* buf, float cf) {
-  constexpr int EPV = elems_per_vec(BF16);
-  float vm[kItemVecs], vs[kItemVecs];
-#pragma unroll
-  for (int u = 0; u < kItemVecs; ++u) {
-    float xs[EPV];
-    unpack<BF16>(buf[u], xs);
-    float m = xs[0];
-#pragma unroll
-    for (int k = 1; k < EPV; ++k) m = fmaxf(m, xs[k]);
-    // offset 0 when there is no finite max keeps a NaN visible in the sum
-    const float mc = (m == -INFINITY) ? 0.f : scaled_max(m, cf);
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < EPV; k += 2) {
-      s0 += fast_exp2(scaled_logit(xs[k], cf, mc));
-      s1 += fast_exp2(scaled_logit(xs[k + 1], cf, mc));
-    }
-    vm[u] = m;
-    vs[u] = s0 + s1;
-  }
-  float mx = vm[0];
-#pragma unroll
-  for (int u = 1; u < kItemVecs; ++u) mx = fmaxf(mx, vm[u]);
-  mx = wave_max(mx);
-  const float Mc = (mx == -INFINITY) ? 0.f : scaled_max(mx, cf);
-  float s = 0.f;
-#pragma unroll
-  for (int u = 0; u < kItemVecs; ++u) s += vs[u] * rescale(vm[u], cf, Mc);
-  s = wave_sum(s);
-  return pack_slot(mx, __float_as_uint(s));
-}
-
-// Partial of one row-chunk for a greedy row: (max, lowest index attaining it).
-// The wave maximum from per-vector maxima; then each lane takes the first of
-// its vectors holding it (a backward scan keeps the last match, the lowest)
-// and the first element of that vector equal to it.  NaN never matches.
-template <bool BF16>
-__device__ __forceinline__ uint64_t item_argmax(const uint4* buf, int64_t e0) {
-  constexpr int EPV = elems_per_vec(BF16);
-  const int lane = threadIdx.x & 63;
-  float vm[kItemVecs];
-#pragma unroll
-  for (int u = 0; u < kItemVecs; ++u) {
-    float xs[EPV];
-    unpack<BF16>(buf[u], xs);
-    vm[u] = xs[0];
-#pragma unroll
-    for (int k = 1; k < EPV; ++k) vm[u] = fmaxf(vm[u], xs[k]);
-  }
-  float mx = vm[0];
-#pragma unroll
-  for (int u = 1; u < kItemVecs; ++u) mx = fmaxf(mx, vm[u]);
-  mx = wave_max(mx);
-  int us = -1;
-  uint4 sel = buf[0];
-#pragma unroll
-  for (int u = kItemVecs - 1; u >= 0; --u) {
-    if (vm[u] == mx) {
-      us = u;
-      sel = buf[u];
-    }
-  }
-  int idx = INT_MAX;
-  if (us >= 0) {
-    float xs[EPV];
-    unpack<BF16>(sel, xs);
-    int ks = 0;
-#pragma unroll
-    for (int k = EPV - 1; k >= 0; --k)
-      if (xs[k] == mx) ks = k;
-    idx = static_cast<int>(e0) + (us * 64 + lane) * EPV + ks;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) idx = min(idx, __shfl_xor(idx, o, 64));
-  return pack_slot(mx, static_cast<uint32_t>(idx));
 }
 
 __device__ void finish_greedy(const Params& p, int b, const Req& r);
@@ -809,7 +445,7 @@ __device__ __forceinline__ void race_group(const float zp[4], const float zq[4],
                                            const RaceRow& rr, int64_t g, int64_t v_end,
                                            uint32_t b, uint32_t k0, uint32_t k1, float& bw,
                                            float& be, int& bidx) {
-  const Philox4 r = philox_race(static_cast<uint32_t>(g), static_cast<uint32_t>(rr.n), b, k0, k1);
+  const Philox4 r = philox_race(static_cast<uint32_t>(g), static_cast<uint32_t>(rr.n), b, 0u, k0, k1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int v = static_cast<int>(g) * 4 + k;

@@ -299,3 +299,19 @@ def subset_requests(batch: Batch, reqs) -> Batch:
                  tokens=np.concatenate(toks).astype(np.int32) if toks else np.empty(0, np.int32),
                  temperature=batch.temperature[reqs].copy(), seed=batch.seed,
                  sigma=batch.sigma[reqs].copy(), label=batch.label + " (subset)")
+
+
+def draft_step_rows(batch: Batch, t: int) -> np.ndarray:
+    """Draft rows at draft step t, one per request ([B, V], storage dtype).
+
+    Request b contributes its draft row t (row offsets[b] + t); a request with
+    fewer than t + 1 drafts contributes its last draft row (or its first
+    target row when it has none), so every request has a row."""
+    rows = []
+    for b in range(batch.B):
+        k = int(batch.offsets[b + 1] - batch.offsets[b])
+        if k > 0:
+            rows.append(batch.draft[int(batch.offsets[b]) + min(t, k - 1)])
+        else:
+            rows.append(batch.target[int(batch.offsets[b]) + b])
+    return np.stack(rows)

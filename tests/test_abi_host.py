@@ -86,3 +86,39 @@ def test_greedy_rejects_bad_arguments(lib):
                                   None) == -3
     assert lib.spec_verify_greedy(base, 1, 2, 32, 1, 2, base, base, base, base, base, 16,
                                   None) == -4
+
+
+def test_draft_workspace_bytes(lib):
+    assert lib.spec_draft_workspace_bytes(64, 128256) >= 64 * 63 * 16
+    assert lib.spec_draft_workspace_bytes(0, 10) == 0
+    assert lib.spec_draft_workspace_bytes(1, 0) == 0
+
+
+@pytest.mark.parametrize("case", ["null_logits", "null_temp", "null_tokens", "null_ws", "B0",
+                                  "V0", "step_neg", "dtype", "ws_small", "ws_misaligned"])
+def test_draft_rejects_bad_arguments(lib, case):
+    B, V = 4, 64
+    keep = []
+    def p(n=4096):
+        ptr, buf = _fake(n + 64)
+        keep.append(buf)
+        return ctypes.c_void_p((ptr.value + 15) // 16 * 16)
+    ws_n = lib.spec_draft_workspace_bytes(B, V)
+    a = dict(logits=p(), dtype=1, B=B, V=V, temp=p(), seed=3, step=0, toks=p(), q=None,
+             ws=p(ws_n), ws_n=ws_n)
+    expect = {"null_logits": -1, "null_temp": -1, "null_tokens": -1, "null_ws": -1, "B0": -2,
+              "V0": -2, "step_neg": -2, "dtype": -3, "ws_small": -4, "ws_misaligned": -4}[case]
+    if case == "null_logits": a["logits"] = None
+    if case == "null_temp": a["temp"] = None
+    if case == "null_tokens": a["toks"] = None
+    if case == "null_ws": a["ws"] = None
+    if case == "B0": a["B"] = 0
+    if case == "V0": a["V"] = 0
+    if case == "step_neg": a["step"] = -1
+    if case == "dtype": a["dtype"] = 7
+    if case == "ws_small": a["ws_n"] = ws_n - 1
+    if case == "ws_misaligned": a["ws"] = ctypes.c_void_p(a["ws"].value + 4)
+    rc = lib.spec_draft_sample(a["logits"], a["dtype"], a["B"], a["V"], a["temp"],
+                               ctypes.c_uint64(a["seed"]), a["step"], a["toks"], a["q"],
+                               a["ws"], a["ws_n"], None)
+    assert rc == expect
