@@ -16,6 +16,11 @@ Reported:
                  that kernel), against 8 TB/s; the library's own events around
                  each launch are reported beside it as a cross-check
   cpu_baseline   the float64 oracle on a bounded sample of the same batch
+  copy_gbs       a plain 1 GiB device copy on the same stream (the achievable line)
+
+--op draft times the draft-side sampler instead (spec_draft_sample over the
+workload's draft rows at step 0, one row per request) against the VALU issue
+rate, since its exponential race is arithmetic-bound.
 """
 from __future__ import annotations
 
@@ -56,6 +61,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=("verify", "draft"), default="verify",
+                    help="verify: the verify step (the metric); draft: the draft-side "
+                         "sampler on the workload's draft rows at step 0")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -113,6 +121,115 @@ def traffic_record(workload: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+# VALU issue slots per token of the draft sampler (quarter-rate exp / log count
+# 4, a full-rate op 1), from its formulation: a sampled token costs a quarter
+# of a Philox4x32-10 call (10 rounds of two 32x32->64 products and two
+# three-input xors: 10 slots), the uniform map (2), -log2 U (4), the weight's
+# fma and exp2 (5), the sum (1), the cross-multiplied comparison with its
+# three selects (6) and unpack + max (2): 30.  A greedy token: unpack + max
+# and its share of the argmax search: 2.
+DRAFT_SLOTS_SAMPLED = 30
+DRAFT_SLOTS_GREEDY = 2
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: full-rate 32-bit VALU lane slots / s
+PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
+
+
+def bench_draft(args):
+    """Draft-side sampler: one spec_draft_sample call per step over the
+    workload's draft rows at draft step 0 (one row per request)."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_scaled_amd import binding
+    from rejection_sampling_verify_scaled_amd import workloads as W
+
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    batch = W.make_batch(args.workload, 0)
+    rows = W.draft_step_rows(batch, 0)
+    B, V = rows.shape
+    esz = 2 if batch.dtype == W.DTYPE_BF16 else 4
+    if batch.dtype == W.DTYPE_BF16:
+        x0 = torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+    else:
+        x0 = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.float32)).to(dev)
+    per_copy = B * V * esz
+    copies = args.copies or max(2, math.ceil(1.25e9 / per_copy))
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    temp = torch.from_numpy(batch.temperature.astype(np.float32)).to(dev)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+    q = torch.empty(B, dtype=torch.float32, device=dev)
+    ws = torch.zeros(binding.draft_workspace_bytes(B, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    vp = ctypes.c_void_p
+    dt = binding.SV_BF16 if batch.dtype == W.DTYPE_BF16 else binding.SV_F32
+
+    def call(i):
+        rc = lib.spec_draft_sample(vp(xs[i % copies].data_ptr()), dt, B, V, vp(temp.data_ptr()),
+                                   ctypes.c_uint64(batch.seed), 0, vp(tok.data_ptr()),
+                                   vp(q.data_ptr()), vp(ws.data_ptr()), ws.numel(), sh)
+        if rc != 0:
+            raise SystemExit(f"spec_draft_sample returned {rc}")
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    n_s = int((batch.temperature > 0).sum())
+    slots = (n_s * DRAFT_SLOTS_SAMPLED + (B - n_s) * DRAFT_SLOTS_GREEDY) * V
+    achieved = slots / (us * 1e-6)
+    call(0)
+    torch.cuda.synchronize()
+    gpu_tok = tok.cpu().numpy()
+    line = {
+        "metric": "draft tokens drawn/sec (draft-side sampler, one token per request)",
+        "value": B / (us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if batch.dtype == W.DTYPE_BF16 else "f32", "data": "synthetic",
+        "config": {"workload": batch.label + ", draft rows at step 0", "B": B, "V": V,
+                   "sampled_rows": n_s, "greedy_rows": B - n_s, "input_copies_rotated": copies},
+        "kernel_us": {"sd_sample": us},
+        "roofline": {"bound": "alu", "achieved": achieved / 1e12, "peak": PEAK_VALU_SLOTS / 1e12,
+                     "unit": "T VALU lane-slots/s", "frac": achieved / PEAK_VALU_SLOTS,
+                     "traffic": None, "kernel": "sd_sample"},
+        "hbm_gbs": per_copy / (us * 1e-6) / 1e9,
+        "hbm_frac": per_copy / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        olib = oracle.load()
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            ref = oracle.draft_sample(batch.dtype, rows, batch.temperature, batch.seed, 0,
+                                      lib=olib)
+            passes += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - t0
+        flagged = (ref["flags"] & oracle.FLAG_RACE_NEAR_TIE) != 0
+        line["cpu_baseline"] = {
+            "value": B * passes / cpu_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over the {B} draft rows (single-threaded float64 C "
+                      f"oracle, {cpu_s:.1f} s)"}
+        line["parity_check"] = {"rows": B, "unflagged_mismatches":
+                                int(((gpu_tok != ref["tokens"]) & ~flagged).sum()),
+                                "flagged": int(flagged.sum())}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -125,6 +242,9 @@ def main():
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a HIP GPU")
+    if args.op == "draft":
+        bench_draft(args)
+        return
     from rejection_sampling_verify_scaled_amd import binding
     from rejection_sampling_verify_scaled_amd import workloads as W
 
