@@ -5,29 +5,29 @@
 // Exactitud", and its greedy case).  How it runs on MI355X: one launch.
 //
 // Vocabulary chunks.  Every row is cut into chunks of 8 KiB (4096 bf16 or
-// 2048 float32 logits).  Workgroup g serves chunk group cg = g mod ng (m
-// consecutive chunks) of two requests, b1 = g / ng and b2 = b1 - lag:
-//   1. statistics of request b1: each wave streams whole row-chunks (8
-//      16-byte loads per lane, two row-chunks in flight) of every row the
-//      request reads -- K+1 target and K draft rows when it is sampled, the
-//      K+1 target rows when it is greedy -- and reduces each row-chunk to one
-//      8-byte partial: (max, sum of 2^(z c - fl(max c))), c = log2(e) / T, or
-//      (max, lowest argmax index) for greedy rows;
-//   2. race of request b2 (sampled requests only): fold the partials of all
-//      rows of b2 (every workgroup of b2 does the same fold in the same order,
-//      so all of them find the same values), gather p_t(x_t) and q_t(x_t),
-//      draw r_t, find the first rejection n with a wave ballot, then run the
-//      exponential race over this workgroup's chunks of row n -- the residual
-//      (p_n - q_n)+ after a rejection, p_K otherwise.
-// The last workgroup of a request in grid order finishes it: the last
-// statistics workgroup of a greedy request folds its argmaxes and writes the
-// outputs; the last race workgroup of a sampled request folds the chunk
-// winners and writes the outputs.  Each polls the slots of its siblings,
-// which sit earlier in the grid.  The lag puts a request's races a few
-// hundred workgroups after its statistics, so they usually find the partials
-// ready, and the race arithmetic of one request overlaps the streaming of
-// later ones.  After the B x ng workgroups with statistics comes a tail of
-// lag x ngr race-only workgroups (empty for greedy requests).
+// 2048 float32 logits).  Each workgroup does one task:
+//   1. statistics of one group of a request's row-chunks (8 row-chunks in
+//      row-major order when every request has max_k drafts, else one column
+//      of m chunks across the request's rows): each wave streams whole
+//      row-chunks (8 16-byte loads per lane, two row-chunks in flight) and
+//      reduces each to one 8-byte partial: (max, sum of 2^(z c - fl(max c))),
+//      c = log2(e) / T, for the K+1 target and K draft rows of a sampled
+//      request, or (max, lowest argmax index) for the K+1 target rows of a
+//      greedy one;
+//   2. race over one range of chunks of a sampled request: fold the partials
+//      of all its rows (every race workgroup of the request does the same
+//      fold in the same order, so all of them find the same values), gather
+//      p_t(x_t) and q_t(x_t), draw r_t, find the first rejection n with a
+//      wave ballot, then run the exponential race over its chunks of row n --
+//      the residual (p_n - q_n)+ after a rejection, p_K otherwise.
+// Grid order: a request's ngr race workgroups follow its statistics by lag
+// requests' worth of statistics workgroups, so they usually find the
+// partials ready and one request's race arithmetic overlaps the streaming
+// of later ones.  The last workgroup of a request in grid order finishes it:
+// the last statistics workgroup with items of a greedy request folds its
+// argmaxes and writes the outputs; the last race workgroup of a sampled
+// request folds the chunk winners and writes the outputs.  Each polls the
+// slots of its siblings, which sit earlier in the grid.
 //
 // Hand-offs between workgroups use 8-byte slots in the workspace that are
 // all-zero until written (a written slot never has all-zero bits: +0.0 is
@@ -92,7 +92,7 @@ struct Params {
   int32_t ng;   // workgroups per request: ceil(nc / m), or ceil(rows nc / 8) when flat
   int32_t mr;   // race chunks per race workgroup
   int32_t ngr;  // race workgroups per request, ceil(nc / mr) <= ng
-  int32_t lag;  // request b's race runs in the first ngr workgroups of request b + lag
+  int32_t lag;  // request b's race workgroups follow the statistics of request b + lag
   uint64_t* part;    // [B][2 max_k + 1][nc] row-chunk partials
   uint64_t* race;    // [B][ngr] race winner of each race workgroup
   int32_t* accept_len;
@@ -752,30 +752,44 @@ __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceR
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
-  // B x ng workgroups with statistics, then a tail of lag x ngr race-only ones
+  // Grid order, with L = lag: the statistics of requests 0..L-1 (ng workgroups
+  // each); then, for k = L..B-1, the statistics of request k followed by the
+  // ngr race workgroups of request k - L; then the races of the last L
+  // requests.  A request's races thus follow its statistics by about L ng
+  // workgroups, and every race has workgroups of its own.
   const int g = blockIdx.x;
-  const int main_wgs = p.B * p.ng;
-  int b1, cg;
-  if (g < main_wgs) {
+  const int L = p.lag, seg = p.ng + p.ngr;
+  int b1 = p.B, cg = 0, b2 = -1, rc = 0;
+  if (g < L * p.ng) {
     b1 = g / p.ng;
     cg = g - b1 * p.ng;
+  } else if (g < L * p.ng + (p.B - L) * seg) {
+    const int t = g - L * p.ng;
+    const int k = L + t / seg;
+    const int tt = t - (k - L) * seg;
+    if (tt < p.ng) {
+      b1 = k;
+      cg = tt;
+    } else {
+      b2 = k - L;
+      rc = tt - p.ng;
+    }
   } else {
-    const int t = g - main_wgs;
-    b1 = p.B + t / p.ngr;
-    cg = t - (b1 - p.B) * p.ngr;
+    const int t = g - L * p.ng - (p.B - L) * seg;
+    b2 = p.B - L + t / p.ngr;
+    rc = t - (b2 - (p.B - L)) * p.ngr;
   }
-  const int b2 = b1 - p.lag;
-  // the race request's draft tokens, loaded before the statistics stream
+  // the race request's draft tokens, loaded before anything waits
   Req r2{};
   bool race = false;
   int32_t x = 0;
   if (b2 >= 0 && b2 < p.B) {
     r2 = load_req(p, b2);
-    race = r2.sampled() && cg < p.ngr;
+    race = r2.sampled();
     if (race && static_cast<int>(threadIdx.x) < r2.K) x = p.tokens[r2.off0 + threadIdx.x];
   }
   if (b1 < p.B) stats_part<BF16, VEC>(p, b1, cg);
-  if (race) race_part<BF16, VEC>(p, b2, cg, r2, x);
+  if (race) race_part<BF16, VEC>(p, b2, rc, r2, x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -889,16 +903,18 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   }
   prm.ngr = static_cast<int32_t>(ceil_div(prm.nc, prm.mr));
   // Race placement.  A race workgroup polls, holding its slot, until its
-  // request's statistics are in, so it is placed about when they complete:
-  // four fifths of a resident generation of workgroups after them.  When
-  // the whole statistics grid is at most two generations, every race goes
-  // after all statistics workgroups instead (lag = B).
+  // request's statistics are in; placed too early it idles a slot the stream
+  // needs, too late it starts the request's dependent chain late.  The lag,
+  // in workgroups between a request's statistics and its races, was tuned
+  // on MI355X: about 0.45 of a resident generation (5 workgroups per CU)
+  // with flat grouping, 1.2 with column grouping (ragged batches).  An
+  // all-greedy call has no races: lag = B puts every statistics workgroup
+  // first and the grid ends there.
   const int64_t resident = kWorkgroupsPerCu * compute_units();
-  const int64_t stats_wgs = static_cast<int64_t>(B) * prm.ng;
-  prm.lag = static_cast<int32_t>(
-      stats_wgs <= 2 * resident
-          ? B
-          : std::min<int64_t>(B, std::max<int64_t>(1, ceil_div(4 * resident / 5, prm.ng))));
+  const int64_t lag_wgs = prm.flat ? resident * 9 / 20 : resident * 6 / 5;
+  prm.lag = all_greedy ? B
+                       : static_cast<int32_t>(std::min<int64_t>(
+                             B, std::max<int64_t>(1, ceil_div(lag_wgs, prm.ng))));
   prm.part = reinterpret_cast<uint64_t*>(ws + L.part_off);
   prm.race = reinterpret_cast<uint64_t*>(ws + L.race_off);
   prm.accept_len = accept_len;
@@ -906,8 +922,10 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.p_at = p_at;
   prm.q_at = q_at;
   // all-greedy calls have no races, so no race-only tail
+  // every request has ngr race workgroups (they find nothing to do for a
+  // greedy request); an all-greedy call has none
   const int64_t grid = static_cast<int64_t>(B) * prm.ng +
-                       (all_greedy ? 0 : static_cast<int64_t>(prm.lag) * prm.ngr);
+                       (all_greedy ? 0 : static_cast<int64_t>(B) * prm.ngr);
   if (grid <= 0 || grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 && aligned16(target) && (!draft || aligned16(draft));
