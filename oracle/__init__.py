@@ -10,7 +10,8 @@ bonus rule and the greedy case of "Decodificación Especulativa y EAGLE"
 counter, so that a result is a pure function of the inputs and the seed.
 It also holds the draft-side sampler that precedes verification
 (``draft_sample``: one token per request from softmax(z/T), or the argmax at
-T = 0).
+T = 0) and the commit step that follows it (``commit_tokens``: the emitted
+tokens appended to each request's token history).
 """
 from __future__ import annotations
 
@@ -72,6 +73,9 @@ def load(path: str = LIB):
     lib.oracle_draft_sample.argtypes = [ctypes.c_int, vp, ctypes.c_int32, ctypes.c_int32, vp,
                                         ctypes.c_uint64, ctypes.c_int32, vp, vp, vp, vp]
     lib.oracle_draft_sample.restype = ctypes.c_int
+    lib.oracle_commit_tokens.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                         vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, vp]
+    lib.oracle_commit_tokens.restype = ctypes.c_int
     if path == LIB:
         _lib = lib
     return lib
@@ -187,3 +191,24 @@ def draft_sample(dtype: int, logits, temperature, seed: int, step: int, lib=None
     if rc != 0:
         raise ValueError(f"oracle_draft_sample rejected its arguments (rc={rc})")
     return dict(tokens=tokens, q_at=q_at, flags=flags, race_gap=gap)
+
+
+def commit_tokens(offsets, accept_len, out_tokens, seq_tokens, seq_len, max_k: int,
+                  n_draft_rows=None, lib=None) -> dict:
+    """Commit step: returns new copies of seq_tokens [B, capacity] and seq_len [B],
+    with next_tokens [B] and status [B] (see spec_oracle.c)."""
+    lib = lib or load()
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    accept_len = np.ascontiguousarray(accept_len, dtype=np.int32)
+    out_tokens = np.ascontiguousarray(out_tokens, dtype=np.int32)
+    seq = np.array(seq_tokens, dtype=np.int32, copy=True, order="C")
+    lens = np.array(seq_len, dtype=np.int32, copy=True)
+    B, cap = seq.shape
+    n_d = int(offsets[-1]) if n_draft_rows is None else int(n_draft_rows)
+    nxt = np.full(B, -3, dtype=np.int32)
+    st = np.full(B, -3, dtype=np.int32)
+    rc = lib.oracle_commit_tokens(B, max_k, n_d, _ptr(offsets), _ptr(accept_len), _ptr(out_tokens),
+                                  _ptr(seq), cap, _ptr(lens), cap, _ptr(nxt), _ptr(st))
+    if rc != 0:
+        raise ValueError(f"oracle_commit_tokens rejected its arguments (rc={rc})")
+    return dict(seq_tokens=seq, seq_len=lens, next_tokens=nxt, status=st)

@@ -34,7 +34,9 @@
  * It also holds the draft-side sampler that precedes verification
  * (oracle_draft_sample, at the end of this file): one token per request from
  * softmax(z / T) by the same kind of race on its own Philox stream (tag 2),
- * or the argmax at T = 0.
+ * or the argmax at T = 0; and the commit step that follows it
+ * (oracle_commit_tokens): the emitted tokens appended to each request's
+ * token history on the device.
  *
  * Philox4x32-10 is written from its published definition (Salmon, Moraes,
  * Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): ten
@@ -410,6 +412,49 @@ int oracle_draft_sample(int dtype, const void* logits, int32_t B, int32_t V,
     if (x >= 0 && q_at) q_at[b] = exp(logit(logits, dtype, b, V, x) / T - lse);
     if (race_gap) race_gap[b] = best - second;
     if (best - second < 1e-6 * fmax(1.0, fabs(best)) && flags) flags[b] |= OR_FLAG_RACE_NEAR_TIE;
+  }
+  return 0;
+}
+
+/*
+ * Commit step after verification (Perplexity's page, section on MTP
+ * scheduling: once the verify step has decided, a kernel writes the
+ * accepted tokens into their places on the device, so the host never waits
+ * for the outcome).  For request b with n = accept_len[b] and history row
+ * seq_tokens[b * seq_stride .. + capacity), length L = seq_len[b]:
+ *   - a failed verify (n < 0), n > K_b, or a slice outside the packed
+ *     layout (offsets as in the verify step, K_b <= max_k): status -1;
+ *   - L < 0 or L + n + 1 > capacity: status -2;
+ *   - otherwise the n + 1 emitted tokens out_tokens[offsets[b] + b + i],
+ *     i = 0..n, are written at positions L..L+n, seq_len[b] = L + n + 1,
+ *     next_tokens[b] = the last of them, status n + 1.
+ * A failed request keeps its history and length and gets next_tokens -1.
+ */
+int oracle_commit_tokens(int32_t B, int32_t max_k, int32_t n_draft_rows, const int32_t* offsets,
+                         const int32_t* accept_len, const int32_t* out_tokens,
+                         int32_t* seq_tokens, int64_t seq_stride, int32_t* seq_len,
+                         int32_t capacity, int32_t* next_tokens, int32_t* status) {
+  if (B < 1 || !offsets || !accept_len || !out_tokens || !seq_tokens || !seq_len ||
+      !next_tokens || !status || capacity < 0 || seq_stride < capacity)
+    return -1;
+  for (int32_t b = 0; b < B; ++b) {
+    next_tokens[b] = -1;
+    const int32_t off = offsets[b], off1 = offsets[b + 1], n = accept_len[b];
+    const int slice_ok = off >= 0 && off1 >= off && off1 <= n_draft_rows && off1 - off <= max_k;
+    if (!slice_ok || n < 0 || n > off1 - off) {
+      status[b] = -1;
+      continue;
+    }
+    const int32_t L = seq_len[b];
+    if (L < 0 || (int64_t)L + n + 1 > capacity) {
+      status[b] = -2;
+      continue;
+    }
+    for (int32_t i = 0; i <= n; ++i)
+      seq_tokens[(int64_t)b * seq_stride + L + i] = out_tokens[(int64_t)off + b + i];
+    seq_len[b] = L + n + 1;
+    next_tokens[b] = out_tokens[(int64_t)off + b + n];
+    status[b] = n + 1;
   }
   return 0;
 }

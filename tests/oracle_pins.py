@@ -605,8 +605,57 @@ def pin_draft_faults(lib):
     assert 0 <= res["tokens"][0] < V and res["tokens"][5] == int(np.argmax(z[5]))
 
 
+# ------------------------------------------------------------------ commit step
+
+
+def pin_commit_example(lib):
+    """A hand-checked batch: append, empty draft, failed verify, capacity overflow,
+    and an append that fills the history exactly."""
+    offsets = np.array([0, 2, 2, 5, 6, 7], np.int32)       # K = 2, 0, 3, 1, 1
+    accept = np.array([1, 0, -1, 1, 1], np.int32)
+    # packed outputs: request b's block of K_b + 1 starts at offsets[b] + b
+    out = np.array([7, 9, -1, 4, -1, -1, -1, -1, 11, 12, 13, 14], np.int32)
+    seq = np.array([[1, 2, 3, 0, 0, 0], [5, 0, 0, 0, 0, 0], [6, 6, 6, 6, 6, 0],
+                    [8, 8, 8, 8, 8, 0], [2, 2, 2, 2, 0, 0]], np.int32)
+    lens = np.array([3, 1, 5, 5, 4], np.int32)
+    r = oracle.commit_tokens(offsets, accept, out, seq, lens, 3, lib=lib)
+    assert r["seq_tokens"].tolist() == [[1, 2, 3, 7, 9, 0], [5, 4, 0, 0, 0, 0],
+                                        [6, 6, 6, 6, 6, 0], [8, 8, 8, 8, 8, 0],
+                                        [2, 2, 2, 2, 13, 14]]
+    assert r["seq_len"].tolist() == [5, 2, 5, 5, 6]
+    assert r["next_tokens"].tolist() == [9, 4, -1, -1, 14]
+    assert r["status"].tolist() == [2, 1, -1, -2, 2]
+
+
+def pin_commit_after_verify(lib):
+    """Committing a verify result appends the accepted drafts, then the emitted token,
+    and leaves every earlier token of the history in place."""
+    rng = np.random.default_rng(25)
+    B, V, cap = 50, 30, 40
+    ks = rng.integers(0, 6, size=B)
+    offsets = np.zeros(B + 1, np.int32)
+    offsets[1:] = np.cumsum(ks)
+    n_d = int(offsets[-1])
+    z = rng.normal(0, 2, size=(n_d + B, V))
+    d = z[np.concatenate([np.arange(offsets[b] + b, offsets[b] + b + ks[b]) for b in range(B)])
+          .astype(int)] + rng.normal(0, 0.7, size=(n_d, V)) if n_d else np.zeros((0, V))
+    toks = rng.integers(0, V, size=n_d).astype(np.int32)
+    temps = rng.choice([0.0, 1.0], size=B).astype(np.float32)
+    v = oracle.verify(oracle.F64, z, d, offsets, toks, temps, 17, V, 5, lib=lib)
+    seq = rng.integers(0, V, size=(B, cap)).astype(np.int32)
+    lens = rng.integers(0, cap - 5, size=B).astype(np.int32)
+    r = oracle.commit_tokens(offsets, v["accept_len"], v["out_tokens"], seq, lens, 5, lib=lib)
+    for b in range(B):
+        n, L = int(v["accept_len"][b]), int(lens[b])
+        assert r["status"][b] == n + 1 and r["seq_len"][b] == L + n + 1
+        row = r["seq_tokens"][b]
+        assert (row[:L] == seq[b, :L]).all() and (row[L + n + 1:] == seq[b, L + n + 1:]).all()
+        assert (row[L:L + n] == toks[offsets[b]:offsets[b] + n]).all()
+        assert row[L + n] == v["out_tokens"][offsets[b] + b + n] == r["next_tokens"][b]
+
+
 ALL_PINS = [pin_philox_kat, pin_philox_rocrand, pin_u01, pin_softmax_vs_scipy,
             pin_greedy_vs_numpy, pin_exact_enumeration, pin_plain_sampling, pin_closed_form,
             pin_temperature_invariance, pin_identical_draft_accepts, pin_disjoint_draft_rejects,
             pin_faults, pin_draft_distribution, pin_draft_greedy, pin_draft_streams,
-            pin_draft_faults]
+            pin_draft_faults, pin_commit_example, pin_commit_after_verify]

@@ -62,6 +62,13 @@ MUTANTS = {
     # draft sampler: temperature ignored in the race key
     "draft_untempered": ("double key = logit(logits, dtype, b, V, v) / T - log(",
                          "double key = logit(logits, dtype, b, V, v) - log("),
+    # commit: the emitted token left out (only the accepted drafts appended)
+    "commit_drops_emitted": ("for (int32_t i = 0; i <= n; ++i)\n      seq_tokens",
+                             "for (int32_t i = 0; i < n; ++i)\n      seq_tokens"),
+    # commit: the request's block read at the draft offset (missing + b)
+    "commit_block_base": ("out_tokens[(int64_t)off + b + i]", "out_tokens[(int64_t)off + i]"),
+    # commit: a history exactly at capacity rejected
+    "commit_capacity": ("(int64_t)L + n + 1 > capacity", "(int64_t)L + n + 1 >= capacity"),
     # uniform map that can return 0
     "u01_map": ("return (2.0 * (double)(x >> 9) + 1.0) / 16777216.0;",
                 "return (double)(x >> 8) / 16777216.0;"),
@@ -72,7 +79,8 @@ ORDER = [P.pin_philox_kat, P.pin_u01, P.pin_softmax_vs_scipy, P.pin_greedy_vs_nu
          P.pin_temperature_invariance, P.pin_identical_draft_accepts,
          P.pin_disjoint_draft_rejects, P.pin_faults, P.pin_plain_sampling,
          P.pin_exact_enumeration, P.pin_closed_form, P.pin_draft_greedy, P.pin_draft_faults,
-         P.pin_draft_distribution, P.pin_draft_streams]
+         P.pin_draft_distribution, P.pin_draft_streams, P.pin_commit_example,
+         P.pin_commit_after_verify]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
