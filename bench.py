@@ -20,7 +20,8 @@ Reported:
 
 --op draft times the draft-side sampler instead (spec_draft_sample over the
 workload's draft rows at step 0, one row per request) against the VALU issue
-rate, since its exponential race is arithmetic-bound.
+rate, since its exponential race is arithmetic-bound; --op commit times the
+commit step (spec_commit_tokens) on the workload's verify outputs.
 """
 from __future__ import annotations
 
@@ -61,9 +62,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("verify", "draft"), default="verify",
+    ap.add_argument("--op", choices=("verify", "draft", "commit"), default="verify",
                     help="verify: the verify step (the metric); draft: the draft-side "
-                         "sampler on the workload's draft rows at step 0")
+                         "sampler on the workload's draft rows at step 0; commit: the "
+                         "commit step on the workload's verify outputs")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -230,6 +232,95 @@ def bench_draft(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_commit(args):
+    """Commit step: one spec_commit_tokens call per step, appending the
+    workload's verify outputs (computed by the oracle before timing) to
+    token histories of 4096 entries."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from rejection_sampling_verify_scaled_amd import binding
+    from rejection_sampling_verify_scaled_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    batch = W.make_batch(args.workload, 0)
+    B = batch.B
+    reqs = None if B <= 64 else list(range(0, B, 16))
+    v = oracle.verify_batch(batch, reqs=reqs)
+    acc = v["accept_len"].copy()
+    acc[acc == -2] = -1
+    cap = 4096
+    rng = np.random.default_rng(args.workload)
+    lens0 = rng.integers(0, 1024, size=B).astype(np.int32)
+    seq = torch.zeros((B, cap), dtype=torch.int32, device=dev)
+    lens = torch.from_numpy(lens0).to(dev)
+    offs = torch.from_numpy(batch.offsets.astype(np.int32)).to(dev)
+    acc_d = torch.from_numpy(acc).to(dev)
+    out_d = torch.from_numpy(v["out_tokens"].astype(np.int32)).to(dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = min(args.steps, (cap - 1024) // (batch.max_k + 1))  # histories never fill
+
+    lib = binding.load_library()
+    vp = ctypes.c_void_p
+    cargs = (B, batch.max_k, batch.n_draft_rows, vp(offs.data_ptr()), vp(acc_d.data_ptr()),
+             vp(out_d.data_ptr()), vp(seq.data_ptr()), cap, vp(lens.data_ptr()), cap,
+             vp(nxt.data_ptr()), vp(st.data_ptr()), vp(stream.cuda_stream))
+
+    def call():
+        rc = lib.spec_commit_tokens(*cargs)
+        if rc != 0:
+            raise SystemExit(f"spec_commit_tokens returned {rc}")
+
+    for _ in range(min(args.warmup, 5)):
+        call()
+    torch.cuda.synchronize()
+    lens.copy_(torch.from_numpy(lens0))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    # bytes each call must move: slices, accept_len, lengths (read and written),
+    # the emitted tokens (read and written), next_tokens and status
+    n_emit = int(np.where(acc >= 0, acc + 1, 0).sum())
+    moved = 4 * (2 * (B + 1) + B + 2 * B + 2 * n_emit + 2 * B)
+    line = {
+        "metric": "requests committed/sec (commit step after verification)",
+        "value": B / (us * 1e-6), "unit": "requests/s", "n_gpus": 1, "steps": steps,
+        "warmup": min(args.warmup, 5), "ms_per_step": us * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": batch.label + ", its verify outputs", "B": B,
+                   "emitted_tokens": n_emit, "history_capacity": cap},
+        "kernel_us": {"commit_kernel": us},
+        "roofline": {"bound": "hbm", "achieved": moved / (us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": moved / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "kernel": "commit_kernel",
+                     "note": "a few KB per call: launch- and latency-bound"},
+    }
+    if not args.no_cpu_baseline:
+        seq0 = np.zeros((B, cap), np.int32)
+        t0 = time.perf_counter()
+        passes = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 3.0):
+            oracle.commit_tokens(batch.offsets, acc, v["out_tokens"], seq0, lens0, batch.max_k,
+                                 n_draft_rows=batch.n_draft_rows)
+            passes += 1
+        cpu_s = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": B * passes / cpu_s, "unit": "requests/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over the {B} requests (C oracle, {cpu_s:.1f} s, "
+                      "including its copy of the histories)"}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -244,6 +335,9 @@ def main():
         raise SystemExit("bench.py needs a HIP GPU")
     if args.op == "draft":
         bench_draft(args)
+        return
+    if args.op == "commit":
+        bench_commit(args)
         return
     from rejection_sampling_verify_scaled_amd import binding
     from rejection_sampling_verify_scaled_amd import workloads as W

@@ -176,6 +176,42 @@ int spec_draft_sample(const void* draft_logits, int32_t dtype, int32_t B, int32_
                       const float* temperature, uint64_t seed, int32_t step, int32_t* tokens,
                       float* q_at, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- commit step */
+
+/* Commit step after verification: appends each request's emitted tokens to
+ * its token history on the device, so the serving loop needs no host round
+ * trip to learn the verify step's outcome (Perplexity's "Accelerating Sonar
+ * through speculation", section on MTP scheduling: a kernel writes the
+ * accepted tokens into their places).  For request b with
+ * n = accept_len[b] and history length L = seq_len[b]:
+ *   - n < 0 (a failed verify), n > K_b, or a slice outside the packed
+ *     layout (draft_offsets as for the verify step, K_b <= max_k): the
+ *     request is left unchanged, status[b] = -1;
+ *   - L < 0 or L + n + 1 > capacity: unchanged, status[b] = -2;
+ *   - otherwise out_tokens[draft_offsets[b] + b + i], i = 0..n (the
+ *     accepted drafts, then the emitted token) are written to
+ *     seq_tokens[b * seq_stride + L + i], seq_len[b] becomes L + n + 1,
+ *     next_tokens[b] the last of them, status[b] = n + 1.
+ * next_tokens[b] is -1 for a request left unchanged.  Each call appends
+ * again: call it once per verify step.
+ *   draft_offsets  device, [B+1] int32 (the verify step's)
+ *   accept_len     device, [B] int32 (the verify step's output)
+ *   out_tokens     device, [n_draft_rows + B] int32 (the verify step's output)
+ *   seq_tokens     device in/out, [B][seq_stride] int32 token histories
+ *   seq_len        device in/out, [B] int32 history lengths
+ *   capacity       host; usable entries per history row (<= seq_stride)
+ *   next_tokens, status   device out, optional [B] int32; either may be NULL
+ *   stream         hipStream_t; the call only enqueues work on it
+ * Returns SV_OK, or a negative status with nothing enqueued (SV_ERR_NULL for
+ * a missing required pointer; SV_ERR_SHAPE for B < 1, max_k outside
+ * [0, SV_KMAX], n_draft_rows < 0, capacity < 0 or seq_stride < capacity;
+ * SV_ERR_LAUNCH). */
+int spec_commit_tokens(int32_t B, int32_t max_k, int32_t n_draft_rows,
+                       const int32_t* draft_offsets, const int32_t* accept_len,
+                       const int32_t* out_tokens, int32_t* seq_tokens, int64_t seq_stride,
+                       int32_t* seq_len, int32_t capacity, int32_t* next_tokens, int32_t* status,
+                       void* stream);
+
 /* Host function.  Static description of a status code. */
 const char* spec_verify_status_string(int status);
 

@@ -58,6 +58,9 @@ def load_library(path: str = LIB_PATH):
     lib.spec_draft_workspace_bytes.restype = sz
     lib.spec_draft_sample.argtypes = [vp, i32, i32, i32, vp, u64, i32, vp, vp, vp, sz, vp]
     lib.spec_draft_sample.restype = ctypes.c_int
+    lib.spec_commit_tokens.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_int64, vp, i32, vp,
+                                       vp, vp]
+    lib.spec_commit_tokens.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -70,7 +73,7 @@ def header_functions(header: str = HEADER):
     with open(header) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_(?:verify|draft)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|draft|commit)_\w+)\s*\(", text)))
 
 
 def workspace_bytes(B: int, V: int, max_k: int) -> int:
@@ -223,6 +226,38 @@ def spec_draft_sample(draft_logits: torch.Tensor, temperature: torch.Tensor, see
     if rc != 0:
         raise SpecVerifyError("spec_draft_sample", rc, lib.spec_verify_status_string(rc).decode())
     return tokens, q_at
+
+
+def spec_commit_tokens(draft_offsets: torch.Tensor, accept_len: torch.Tensor,
+                       out_tokens: torch.Tensor, seq_tokens: torch.Tensor,
+                       seq_len: torch.Tensor, max_k: int, capacity: Optional[int] = None,
+                       next_tokens: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None, stream=None):
+    """Append the verify step's emitted tokens to the histories seq_tokens [B, S]
+    (in place) and advance seq_len [B]; returns (next_tokens [B], status [B])."""
+    lib = load_library()
+    B = accept_len.shape[0]
+    device = accept_len.device
+    _check(draft_offsets, "draft_offsets", torch.int32, (B + 1,), device)
+    _check(accept_len, "accept_len", torch.int32, (B,), device)
+    if seq_tokens.dim() != 2 or seq_tokens.shape[0] != B or seq_tokens.dtype != torch.int32 \
+            or seq_tokens.stride(1) != 1:
+        raise ValueError("seq_tokens must be an int32 [B, S] tensor with unit column stride")
+    _check(seq_len, "seq_len", torch.int32, (B,), device)
+    n_d = out_tokens.shape[0] - B
+    _check(out_tokens, "out_tokens", torch.int32, (n_d + B,), device)
+    if next_tokens is None:
+        next_tokens = torch.empty(B, dtype=torch.int32, device=device)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=device)
+    cap = seq_tokens.shape[1] if capacity is None else int(capacity)
+    rc = lib.spec_commit_tokens(B, max_k, n_d, _ptr(draft_offsets), _ptr(accept_len),
+                                _ptr(out_tokens), _ptr(seq_tokens), seq_tokens.stride(0),
+                                _ptr(seq_len), cap, _ptr(next_tokens), _ptr(status),
+                                _stream_handle(stream))
+    if rc != 0:
+        raise SpecVerifyError("spec_commit_tokens", rc, lib.spec_verify_status_string(rc).decode())
+    return next_tokens, status
 
 
 def to_device_batch(batch, device="cuda"):

@@ -122,3 +122,32 @@ def test_draft_rejects_bad_arguments(lib, case):
                                ctypes.c_uint64(a["seed"]), a["step"], a["toks"], a["q"],
                                a["ws"], a["ws_n"], None)
     assert rc == expect
+
+
+@pytest.mark.parametrize("case", ["null_offsets", "null_accept", "null_out", "null_seq",
+                                  "null_len", "B0", "maxk_big", "ndraft_neg", "cap_neg",
+                                  "stride_small"])
+def test_commit_rejects_bad_arguments(lib, case):
+    keep = []
+    def p(n=4096):
+        ptr, buf = _fake(n + 64)
+        keep.append(buf)
+        return ctypes.c_void_p((ptr.value + 15) // 16 * 16)
+    a = dict(B=4, max_k=2, nd=8, offs=p(), acc=p(), out=p(), seq=p(), stride=32, lens=p(),
+             cap=32)
+    expect = {"null_offsets": -1, "null_accept": -1, "null_out": -1, "null_seq": -1,
+              "null_len": -1, "B0": -2, "maxk_big": -2, "ndraft_neg": -2, "cap_neg": -2,
+              "stride_small": -2}[case]
+    if case == "null_offsets": a["offs"] = None
+    if case == "null_accept": a["acc"] = None
+    if case == "null_out": a["out"] = None
+    if case == "null_seq": a["seq"] = None
+    if case == "null_len": a["lens"] = None
+    if case == "B0": a["B"] = 0
+    if case == "maxk_big": a["max_k"] = 9
+    if case == "ndraft_neg": a["nd"] = -1
+    if case == "cap_neg": a["cap"] = -1
+    if case == "stride_small": a["stride"] = 16
+    rc = lib.spec_commit_tokens(a["B"], a["max_k"], a["nd"], a["offs"], a["acc"], a["out"],
+                                a["seq"], a["stride"], a["lens"], a["cap"], None, None, None)
+    assert rc == expect
