@@ -134,6 +134,40 @@ int spec_verify_sample_timed(const void* target_logits, const void* draft_logits
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* event_start, void* event_end);
 
+/* ---------------------------------------------------------------- early exit */
+
+/* Host function.  Workspace bytes spec_verify_sample_early_exit needs (either
+ * dtype); 0 for a bad shape.  The workspace must be zero-filled once when
+ * allocated; calls keep it usable without further clearing. */
+size_t spec_verify_early_exit_workspace_bytes(int32_t B, int32_t V, int32_t max_k);
+
+/* Early-exit verify: the decision of spec_verify_sample without reading the
+ * rows past each request's stop.  The ratio tests run left to right and stop
+ * at the first rejection ("Decodificación Especulativa y EAGLE", section "La
+ * Regla de Exactitud"; "El Concepto", steps 3-4), so target and draft rows
+ * after the stop position cannot change the outcome; this entry point
+ * streams a request's rows one position at a time and skips the rest.
+ * Arguments, layout, ownership and status codes as for spec_verify_sample,
+ * with these differences:
+ *   - accept_len and out_tokens equal spec_verify_sample's (same Philox
+ *     streams and race keys; a race near-tie may resolve differently, as
+ *     between any two float orders of the same keys);
+ *   - p_at_draft / q_at_draft are written for positions t <= n and are NaN
+ *     for positions past the stop n, which are never evaluated;
+ *   - a non-finite row past the stop is not read, so it does not fail the
+ *     request (spec_verify_sample reads every row and fails it);
+ *   - it trades parallelism inside a request for bytes: worthwhile for large
+ *     batches, slower than spec_verify_sample for small ones.
+ * The workspace is the one sized by spec_verify_early_exit_workspace_bytes.
+ * Calls that overlap in time need separate workspaces. */
+int spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits,
+                                  int32_t dtype, int32_t B, int32_t V, int32_t max_k,
+                                  int32_t n_draft_rows, const int32_t* draft_offsets,
+                                  const int32_t* draft_tokens, const float* temperature,
+                                  uint64_t seed, int32_t* accept_len, int32_t* out_tokens,
+                                  float* p_at_draft, float* q_at_draft, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- draft side */
 
 /* Host function.  Workspace bytes spec_draft_sample needs for B rows of V

@@ -54,6 +54,10 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_sample.restype = ctypes.c_int
     lib.spec_verify_sample_timed.argtypes = list(lib.spec_verify_sample.argtypes) + [vp, vp]
     lib.spec_verify_sample_timed.restype = ctypes.c_int
+    lib.spec_verify_early_exit_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_verify_early_exit_workspace_bytes.restype = sz
+    lib.spec_verify_sample_early_exit.argtypes = list(lib.spec_verify_sample.argtypes)
+    lib.spec_verify_sample_early_exit.restype = ctypes.c_int
     lib.spec_draft_workspace_bytes.argtypes = [i32, i32]
     lib.spec_draft_workspace_bytes.restype = sz
     lib.spec_draft_sample.argtypes = [vp, i32, i32, i32, vp, u64, i32, vp, vp, vp, sz, vp]
@@ -191,6 +195,50 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if rc != 0:
         raise SpecVerifyError("spec_verify_sample", rc, lib.spec_verify_status_string(rc).decode())
+    return accept_len, out_tokens, p_at_draft, q_at_draft
+
+
+def early_exit_workspace_bytes(B: int, V: int, max_k: int) -> int:
+    return int(load_library().spec_verify_early_exit_workspace_bytes(B, V, max_k))
+
+
+def spec_verify_sample_early_exit(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                                  draft_offsets: torch.Tensor, draft_tokens: torch.Tensor,
+                                  temperature: torch.Tensor, seed: int, max_k: int,
+                                  accept_len: Optional[torch.Tensor] = None,
+                                  out_tokens: Optional[torch.Tensor] = None,
+                                  p_at_draft: Optional[torch.Tensor] = None,
+                                  q_at_draft: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """Early-exit verify (rows past each request's stop are not read); returns
+    (accept_len, out_tokens, p_at, q_at) like spec_verify_sample, with p/q NaN
+    past the stop."""
+    lib = load_library()
+    B = draft_offsets.shape[0] - 1
+    V = target_logits.shape[1]
+    n_d = draft_tokens.shape[0]
+    device = target_logits.device
+    if workspace is None:
+        workspace = torch.zeros(early_exit_workspace_bytes(B, V, max_k), dtype=torch.uint8,
+                                device=device)
+    B, V, n_d, accept_len, out_tokens, _ = _prepare(
+        target_logits, draft_offsets, draft_tokens, max_k, accept_len, out_tokens, workspace)
+    if not target_logits.is_contiguous():
+        raise ValueError("target_logits must be contiguous")
+    _check(draft_logits, "draft_logits", target_logits.dtype, (n_d, V), device)
+    _check(temperature, "temperature", torch.float32, (B,), device)
+    for name, t in (("p_at_draft", p_at_draft), ("q_at_draft", q_at_draft)):
+        if t is not None:
+            _check(t, name, torch.float32, (n_d,), device)
+    rc = lib.spec_verify_sample_early_exit(
+        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), B, V, max_k, n_d,
+        _ptr(draft_offsets), _ptr(draft_tokens), _ptr(temperature),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(accept_len), _ptr(out_tokens),
+        _ptr(p_at_draft), _ptr(q_at_draft), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if rc != 0:
+        raise SpecVerifyError("spec_verify_sample_early_exit", rc,
+                              lib.spec_verify_status_string(rc).decode())
     return accept_len, out_tokens, p_at_draft, q_at_draft
 
 

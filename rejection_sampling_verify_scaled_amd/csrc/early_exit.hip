@@ -1,0 +1,615 @@
+// early_exit.hip -- gfx950 kernel and C ABI of the early-exit verify step.
+//
+// Same decision as spec_verify_sample (include/spec_verify.h; "Decodificación
+// Especulativa y EAGLE", section "La Regla de Exactitud"): the ratio tests run
+// left to right and stop at the first rejection, so rows past it never
+// influence the result.  This variant does not read them.  It trades
+// parallelism inside a request for bytes: a request's rows are streamed one
+// position (stage) at a time, and later stages are skipped once a stage
+// rejects (sampled) or mismatches (greedy).
+//
+// One launch, stage-major.  The grid is max_k + 1 regions; region s holds,
+// for every request b, ngs statistics workgroups for stage s and ngr race
+// workgroups:
+//   statistics (b, s), s < K_b: if stage s - 1 accepted (or s = 0), stream
+//     target row s and, for a sampled request, draft row s (8 row-chunks per
+//     workgroup, two in flight per wave), one 8-byte partial per row-chunk.
+//     A greedy request also streams target row K_b at s = K_b (its stop
+//     token's row).  The stage's last workgroup with items folds the partials
+//     and decides: sampled -- p_s(x_s), q_s(x_s), r_s, accept iff
+//     r_s q_s < p_s; greedy -- accept iff argmax equals x_s, else (or at
+//     s = K_b) write the outputs.  The decision goes to a record for
+//     (b, s), and a stop is copied into the records of the later stages so
+//     their workgroups need not wait.
+//   race (b, s), sampled requests: after a rejection at s - 1, the residual
+//     race over row s - 1 with the normalisers the decision carried; at
+//     s = K_b after acceptances only, the bonus race over target row K_b
+//     (keys in the log2 domain relative to each chunk's maximum, so it needs
+//     no statistics of that row).  The last race workgroup folds the chunk
+//     winners and writes the outputs.
+// A region's workgroups find the previous stage's decisions ready when the
+// regions are large (many requests); small batches wait on them.
+//
+// Hand-offs use the zero-slot protocol of the verify kernel: a slot is
+// written once per call and is all-zero until then.  Partials and race
+// winners have one reader each, which zeroes them.  The decision records
+// are read by many workgroups, so none of them can tell when the record is
+// free; a small second kernel on the same stream zeroes them after the
+// verify kernel, so the workspace is all-zero again after every call.  A
+// record's upper word is 1 (a payload of 0, such as a zero maximum, still
+// reads as written).  All waits are bounded; an expired wait reports
+// accept_len = -1.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "spec_verify.h"
+#include "device_common.h"
+
+namespace {
+
+constexpr int kRaceChunks = 8;     // chunks per race workgroup
+constexpr int kStageRows = 2;      // a stage streams target row s and draft row s
+constexpr int kDecSlots = 5;       // decision record: code, fl(m_p c), log2 S_p, fl(m_q c), log2 S_q
+constexpr uint32_t kCont = 1u, kRej = 2u, kDone = 3u;  // decision codes (low byte)
+
+struct EeParams {
+  const void* target;
+  const void* draft;
+  const int32_t* offsets;
+  const int32_t* tokens;
+  const float* temperature;
+  uint32_t k0, k1;
+  int32_t B, V, max_k, n_draft_rows;
+  int32_t nc;   // chunks per row
+  int32_t ngs;  // statistics workgroups per (request, stage): ceil(2 nc / 8)
+  int32_t ngr;  // race workgroups per (request, region): ceil(nc / kRaceChunks)
+  uint64_t* part;  // [B][max_k + 1][2][nc] stage partials
+  uint64_t* race;  // [B][ngr] race winners
+  uint64_t* dec;   // [B][max_k + 1][kDecSlots] decision records
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* p_at;
+  float* q_at;
+};
+
+struct EeReq {
+  int32_t off0, K;
+  float T;
+  bool valid, greedy;
+};
+
+// Request b's scalars, checked as the verify step checks them (slice inside
+// the packed layout, K_b <= max_k, a finite non-negative temperature, draft
+// tokens inside the vocabulary); uniform, so the loads are scalar.  With
+// stage >= 0, a request whose drafts end before that stage is returned as
+// not valid without loading its tokens (its workgroups of that region only
+// exit).
+__device__ EeReq ee_req(const EeParams& p, int b, int stage = -1) {
+  EeReq r;
+  r.off0 = p.offsets[b];
+  const int32_t off1 = p.offsets[b + 1];
+  r.K = static_cast<int32_t>(static_cast<uint32_t>(off1) - static_cast<uint32_t>(r.off0));
+  r.T = p.temperature[b];
+  r.greedy = r.T == 0.f;
+  const bool slice_ok =
+      r.off0 >= 0 && off1 <= p.n_draft_rows && off1 >= r.off0 && r.K <= p.max_k;
+  bool ok = slice_ok && r.T >= 0.f && r.T < INFINITY && stage <= r.K;
+  if (ok) {
+    for (int t = 0; t < r.K; ++t) {
+      const int32_t x = p.tokens[r.off0 + t];
+      ok = ok && x >= 0 && x < p.V;
+    }
+  }
+  r.valid = ok;
+  return r;
+}
+
+__device__ __forceinline__ uint64_t* ee_part(const EeParams& p, int b, int s, int row, int c) {
+  return p.part + ((static_cast<int64_t>(b) * (p.max_k + 1) + s) * kStageRows + row) * p.nc + c;
+}
+__device__ __forceinline__ uint64_t* ee_dec(const EeParams& p, int b, int s, int k) {
+  return p.dec + (static_cast<int64_t>(b) * (p.max_k + 1) + s) * kDecSlots + k;
+}
+constexpr uint64_t kDecWritten = 1ull << 32;  // upper word of a written record
+__device__ __forceinline__ void dec_store(const EeParams& p, int b, int s, int k, uint32_t v) {
+  slot_store(ee_dec(p, b, s, k), kDecWritten | v);
+}
+// Payload of a record once written; false if the wait expired.
+__device__ bool dec_wait(const EeParams& p, int b, int s, int k, uint32_t& v) {
+  const uint64_t x = slot_wait(ee_dec(p, b, s, k));
+  v = static_cast<uint32_t>(x);
+  return x != 0u;
+}
+
+// A stop at stage s: the records of stages s..K-1 say so, so that the
+// statistics workgroups of those stages exit without waiting.
+__device__ void publish_stop(const EeParams& p, int b, int s, int K, uint32_t code) {
+  for (int t = s + static_cast<int>(threadIdx.x); t < K; t += kThreads) dec_store(p, b, t, 0, code);
+}
+
+__device__ void ee_fault(const EeParams& p, int b, const EeReq& r, bool slice_ok) {
+  const int tid = threadIdx.x;
+  if (slice_ok) {
+    const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+    if (tid <= r.K) p.out_tokens[trow0 + tid] = -1;
+    if (tid < r.K) {
+      if (p.p_at) p.p_at[r.off0 + tid] = NAN;
+      if (p.q_at) p.q_at[r.off0 + tid] = NAN;
+    }
+  }
+  if (tid == 0) p.accept_len[b] = -1;
+}
+
+// Outputs of a decided request: accept_len = n, tokens x_0..x_{n-1}, y, -1 padding;
+// p/q past position n (never evaluated) are NaN, greedy requests have none.
+__device__ void ee_outputs(const EeParams& p, int b, const EeReq& r, int n, int32_t y) {
+  const int tid = threadIdx.x;
+  const int64_t trow0 = static_cast<int64_t>(r.off0) + b;
+  if (tid <= r.K) {
+    const int32_t xt = tid < n ? p.tokens[r.off0 + tid] : 0;
+    p.out_tokens[trow0 + tid] = tid < n ? xt : (tid == n ? y : -1);
+  }
+  if (tid < r.K && (r.greedy || tid > n)) {
+    if (p.p_at) p.p_at[r.off0 + tid] = NAN;
+    if (p.q_at) p.q_at[r.off0 + tid] = NAN;
+  }
+  if (tid == 0) p.accept_len[b] = n;
+}
+
+// ------------------------------------------------------------------ statistics of a stage
+
+template <bool BF16, bool VEC>
+__device__ void ee_stats(const EeParams& p, int b, int s, int j, const EeReq& r) {
+  constexpr int CHUNK = chunk_tokens(BF16);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int nrows = r.greedy ? 1 : kStageRows;
+  const int i_lo = j * kGroupItems;
+  const int i_hi = min(i_lo + kGroupItems, nrows * p.nc);
+  const float cf = r.greedy ? 0.f : kLog2e / r.T;
+  constexpr int IN_FLIGHT = VEC ? kItemsInFlight : 1;
+  for (int i0 = i_lo + wave * IN_FLIGHT; i0 < i_hi; i0 += kWaves * IN_FLIGHT) {
+    uint4 buf[IN_FLIGHT][kItemVecs];
+#pragma unroll
+    for (int k = 0; k < IN_FLIGHT; ++k) {
+      const int i = min(i0 + k, i_hi - 1);
+      const int row = i / p.nc;
+      const int c = i - row * p.nc;
+      const int64_t prow = row == 0 ? static_cast<int64_t>(r.off0) + b + s
+                                    : static_cast<int64_t>(r.off0) + s;
+      load_item<BF16, VEC>(row == 0 ? p.target : p.draft, prow, p.V,
+                           static_cast<int64_t>(c) * CHUNK, buf[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < IN_FLIGHT; ++k) {
+      const int i = i0 + k;
+      if (i < i_hi) {
+        const int row = i / p.nc;
+        const int c = i - row * p.nc;
+        if (VEC && static_cast<int64_t>(c + 1) * CHUNK > p.V)
+          mask_tail<BF16>(buf[k], p.V, static_cast<int64_t>(c) * CHUNK);
+        const uint64_t v = r.greedy ? item_argmax<BF16>(buf[k], static_cast<int64_t>(c) * CHUNK)
+                                    : item_stats<BF16>(buf[k], cf);
+        if (lane == 0) slot_store(ee_part(p, b, s, row, c), v);
+      }
+    }
+  }
+}
+
+// The stage's last workgroup: fold the stage's partials (wave w < nrows folds
+// row w: lane l takes chunks l, l + 64, ... in order, then a fixed shuffle
+// tree), then decide.
+template <bool BF16>
+__device__ void ee_decide(const EeParams& p, int b, int s, const EeReq& r) {
+  __shared__ float sh_m[kStageRows], sh_s[kStageRows];
+  __shared__ int sh_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int nrows = r.greedy ? 1 : kStageRows;
+  const float cf = r.greedy ? 0.f : kLog2e / r.T;
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  if (wave < nrows) {
+    float M = -INFINITY, S = 0.f;
+    int I = INT_MAX;
+    bool expired = false;
+    for (int c = lane; c < p.nc; c += 64) {
+      uint64_t* slot = ee_part(p, b, s, wave, c);
+      const uint64_t v = slot_wait(slot);
+      if (v == 0u) {
+        expired = true;
+        continue;
+      }
+      slot_store(slot, 0u);
+      if (r.greedy)
+        merge_argmax(M, I, slot_f(v), static_cast<int>(slot_w(v)));
+      else
+        merge_stats(M, S, slot_f(v), __uint_as_float(slot_w(v)), cf);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64);
+      const int i2 = __shfl_xor(I, o, 64);
+      if (r.greedy)
+        merge_argmax(M, I, m2, i2);
+      else
+        merge_stats(M, S, m2, s2, cf);
+    }
+    if (expired) atomicOr(&sh_bad, 2);
+    if (lane == 0) {
+      const bool finite = M > -INFINITY && M < INFINITY && (r.greedy || S < INFINITY);
+      if (!finite) atomicOr(&sh_bad, 1);
+      sh_m[wave] = M;
+      sh_s[wave] = r.greedy ? __int_as_float(I) : S;
+    }
+  }
+  __syncthreads();
+  const int bad = sh_bad;
+  if (bad) {
+    // a stage that cannot be evaluated fails the request (an expired wait
+    // reports -1 like a failure); later stages are told to stop
+    publish_stop(p, b, s, r.K, kDone);
+    ee_fault(p, b, r, true);
+    return;
+  }
+  if (r.greedy) {
+    const int32_t g = __float_as_int(sh_s[0]);
+    const int32_t x = s < r.K ? p.tokens[r.off0 + s] : -1;
+    if (s < r.K && g == x) {
+      if (tid == 0) dec_store(p, b, s, 0, kCont);
+    } else {
+      publish_stop(p, b, s, r.K, kDone);
+      ee_outputs(p, b, r, s, g);
+    }
+    return;
+  }
+  // sampled: ratio test at position s
+  __shared__ int sh_rej;
+  if (tid == 0) {
+    const float mcp = scaled_max(sh_m[0], cf), lsp = fast_log2(sh_s[0]);
+    const float mcq = scaled_max(sh_m[1], cf), lsq = fast_log2(sh_s[1]);
+    const int32_t x = p.tokens[r.off0 + s];
+    const float zp = load_logit<BF16>(p.target, (static_cast<int64_t>(r.off0) + b + s) * p.V + x);
+    const float zq = load_logit<BF16>(p.draft, (static_cast<int64_t>(r.off0) + s) * p.V + x);
+    const float pp = fast_exp2(scaled_logit(zp, cf, mcp) - lsp);
+    const float qq = fast_exp2(scaled_logit(zq, cf, mcq) - lsq);
+    const float u = uniform_open01(philox4x32_10(0u, s, b, 1u, p.k0, p.k1).w[0]);
+    if (p.p_at) p.p_at[r.off0 + s] = pp;
+    if (p.q_at) p.q_at[r.off0 + s] = qq;
+    sh_rej = !(u * qq < pp);
+    if (!sh_rej) {
+      dec_store(p, b, s, 0, kCont);
+    } else {
+      dec_store(p, b, s, 1, __float_as_uint(mcp));
+      dec_store(p, b, s, 2, __float_as_uint(lsp));
+      dec_store(p, b, s, 3, __float_as_uint(mcq));
+      dec_store(p, b, s, 4, __float_as_uint(lsq));
+      dec_store(p, b, s, 0, kRej | (static_cast<uint32_t>(s) << 8));
+    }
+  }
+  __syncthreads();
+  // a rejection also stops the later stages (their races see a stop at s,
+  // not at the stage before them, and do nothing)
+  if (sh_rej) publish_stop(p, b, s + 1, r.K, kRej | (static_cast<uint32_t>(s) << 8));
+}
+
+// ------------------------------------------------------------------ races
+
+struct EeRace {
+  float cf, mcp, lsp, mcq, lsq;
+  int n;
+  bool residual;
+};
+
+// One chunk of the race held in registers (target chunk bp, draft chunk bq
+// for the residual), folded into (key, idx): keys are log2(w / e) plus the
+// chunk's weight offset, comparable across chunks.
+template <bool BF16, bool RESIDUAL>
+__device__ __forceinline__ void ee_race_chunk(const uint4* bp, const uint4* bq, int64_t e0,
+                                              const EeRace& rr, uint32_t b, uint32_t k0,
+                                              uint32_t k1, float& key, int& idx) {
+  constexpr int EPV = elems_per_vec(BF16);
+  const int lane = threadIdx.x & 63;
+  float shift = 0.f;
+  if constexpr (!RESIDUAL) {
+    // bonus weights relative to the chunk maximum
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kItemVecs; ++u) {
+      float xs[EPV];
+      unpack<BF16>(bp[u], xs);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) mx = fmaxf(mx, xs[k]);
+    }
+    mx = wave_max(mx);
+    shift = (mx == -INFINITY) ? 0.f : scaled_max(mx, rr.cf);
+  }
+  float bw = 0.f, be = 1.f;
+  int bi = INT_MAX;
+#pragma unroll
+  for (int u = 0; u < kItemVecs; ++u) {
+    float zp[EPV], zq[EPV];
+    unpack<BF16>(bp[u], zp);
+    if constexpr (RESIDUAL) unpack<BF16>(bq[u], zq);
+    const int64_t v0 = e0 + static_cast<int64_t>(u * 64 + lane) * EPV;
+#pragma unroll
+    for (int h = 0; h < EPV / 4; ++h) {
+      const Philox4 ph = philox_race(static_cast<uint32_t>((v0 >> 2) + h),
+                                     static_cast<uint32_t>(rr.n), b, 0u, k0, k1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float w;
+        if constexpr (RESIDUAL) {
+          w = fast_exp2(scaled_logit(zp[4 * h + k], rr.cf, rr.mcp) - rr.lsp) -
+              fast_exp2(scaled_logit(zq[4 * h + k], rr.cf, rr.mcq) - rr.lsq);
+        } else {
+          w = fast_exp2(scaled_logit(zp[4 * h + k], rr.cf, shift));
+        }
+        const float e = -fast_log2(uniform_open01(ph.w[k]));  // E / ln 2
+        if (w * be > bw * e) {
+          bw = w;
+          be = e;
+          bi = static_cast<int>(v0) + 4 * h + k;
+        }
+      }
+    }
+  }
+  float kk = bi == INT_MAX ? -INFINITY : fast_log2(bw / be) + shift;
+  wave_merge_argmax(kk, bi);
+  merge_argmax(key, idx, kk, bi);
+}
+
+template <bool BF16, bool VEC>
+__device__ void ee_race_range(const EeParams& p, int b, const EeReq& r, const EeRace& rr,
+                              int c_lo, int c_hi, float& key, int& idx) {
+  constexpr int CHUNK = chunk_tokens(BF16);
+  const int wave = wave_id();
+  const int64_t prow = static_cast<int64_t>(r.off0) + b + rr.n;
+  const int64_t qrow = static_cast<int64_t>(r.off0) + rr.n;
+  for (int c = c_lo + wave; c < c_hi; c += kWaves) {
+    uint4 bp[kItemVecs], bq[kItemVecs];
+    const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
+    load_item<BF16, VEC>(p.target, prow, p.V, e0, bp);
+    if (rr.residual) load_item<BF16, VEC>(p.draft, qrow, p.V, e0, bq);
+    if (VEC && e0 + CHUNK > p.V) {
+      mask_tail<BF16>(bp, p.V, e0);
+      if (rr.residual) mask_tail<BF16>(bq, p.V, e0);
+    }
+    if (rr.residual)
+      ee_race_chunk<BF16, true>(bp, bq, e0, rr, static_cast<uint32_t>(b), p.k0, p.k1, key, idx);
+    else
+      ee_race_chunk<BF16, false>(bp, bp, e0, rr, static_cast<uint32_t>(b), p.k0, p.k1, key, idx);
+  }
+}
+
+template <bool BF16, bool VEC>
+__device__ void ee_race(const EeParams& p, int b, int s, int rc, const EeReq& r) {
+  __shared__ float sh_k[kWaves];
+  __shared__ int sh_i[kWaves];
+  __shared__ int sh_expired;
+  const int tid = threadIdx.x;
+  EeRace rr{};
+  rr.cf = kLog2e / r.T;
+  if (s == 0) {
+    if (r.K != 0) return;
+    rr.n = 0;
+    rr.residual = false;
+  } else {
+    uint32_t code = 0;
+    if (!dec_wait(p, b, s - 1, 0, code)) {
+      if (rc == p.ngr - 1 && tid == 0) p.accept_len[b] = -1;
+      return;
+    }
+    const uint32_t kind = code & 0xFFu;
+    if (kind == kRej && static_cast<int>(code >> 8) == s - 1) {
+      rr.n = s - 1;
+      rr.residual = true;
+      uint32_t v[4];
+      bool ok = true;
+      for (int k = 0; k < 4; ++k) ok = dec_wait(p, b, s - 1, k + 1, v[k]) && ok;
+      if (!ok) {
+        if (rc == p.ngr - 1 && tid == 0) p.accept_len[b] = -1;
+        return;
+      }
+      rr.mcp = __uint_as_float(v[0]);
+      rr.lsp = __uint_as_float(v[1]);
+      rr.mcq = __uint_as_float(v[2]);
+      rr.lsq = __uint_as_float(v[3]);
+    } else if (kind == kCont && s == r.K) {
+      rr.n = s;
+      rr.residual = false;
+    } else {
+      return;
+    }
+  }
+  float key = -INFINITY;
+  int idx = INT_MAX;
+  const int c_lo = rc * kRaceChunks, c_hi = min(c_lo + kRaceChunks, p.nc);
+  ee_race_range<BF16, VEC>(p, b, r, rr, c_lo, c_hi, key, idx);
+  block_argmax(key, idx, sh_k, sh_i);
+  if (tid == 0) slot_store(p.race + static_cast<int64_t>(b) * p.ngr + rc, pack_slot(key, static_cast<uint32_t>(idx)));
+  if (rc != p.ngr - 1) return;
+  // the request's last race workgroup: fold the winners, write the outputs
+  if (tid == 0) sh_expired = 0;
+  __syncthreads();
+  key = -INFINITY;
+  idx = INT_MAX;
+  for (int i = tid; i < p.ngr; i += kThreads) {
+    uint64_t* slot = p.race + static_cast<int64_t>(b) * p.ngr + i;
+    const uint64_t v = slot_wait(slot);
+    slot_store(slot, 0u);
+    if (v == 0u) {
+      atomicOr(&sh_expired, 1);
+      continue;
+    }
+    merge_argmax(key, idx, slot_f(v), static_cast<int>(slot_w(v)));
+  }
+  block_argmax(key, idx, sh_k, sh_i);
+  if (sh_expired) {
+    if (tid == 0) p.accept_len[b] = -1;
+    return;
+  }
+  if (idx == INT_MAX) {
+    // no token had p > q (rounding can only cause this when p == q): race on p_n
+    EeRace rb = rr;
+    rb.residual = false;
+    key = -INFINITY;
+    ee_race_range<BF16, VEC>(p, b, r, rb, 0, p.nc, key, idx);
+    block_argmax(key, idx, sh_k, sh_i);
+  }
+  ee_outputs(p, b, r, rr.n, idx);
+}
+
+// ------------------------------------------------------------------ kernel
+
+// at most 128 VGPRs: four waves per SIMD (four workgroups per CU)
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_verify_ee(
+    EeParams p) {
+  const int g = blockIdx.x;
+  const int per_req = p.ngs + p.ngr;
+  const int region = p.B * per_req;
+  const int s = g / region;
+  const int t = g - s * region;
+  const int b = t / per_req;
+  const int j = t - b * per_req;
+  const EeReq r = ee_req(p, b, s);
+  if (!r.valid) {
+    // (s = 0 never exceeds K_b, so region 0 sees every genuine failure)
+    if (s == 0 && j == 0) {
+      const int32_t off1 = p.offsets[b + 1];
+      const bool slice_ok = r.off0 >= 0 && off1 <= p.n_draft_rows && off1 >= r.off0 &&
+                            r.K <= p.max_k;
+      ee_fault(p, b, r, slice_ok);
+    }
+    return;
+  }
+  if (s > r.K) return;
+  if (j < p.ngs) {
+    // statistics of stage s (a sampled request has none at s = K)
+    if (!r.greedy && s == r.K) return;
+    const int n_items = (r.greedy ? 1 : kStageRows) * p.nc;
+    const int last = (n_items + kGroupItems - 1) / kGroupItems - 1;
+    if (j > last) return;
+    if (s > 0) {
+      uint32_t code = 0;
+      if (!dec_wait(p, b, s - 1, 0, code)) {
+        if (j == last && threadIdx.x == 0) p.accept_len[b] = -1;
+        return;
+      }
+      if ((code & 0xFFu) != kCont) return;
+    }
+    ee_stats<BF16, VEC>(p, b, s, j, r);
+    if (j == last) {
+      __syncthreads();
+      ee_decide<BF16>(p, b, s, r);
+    }
+  } else if (!r.greedy) {
+    ee_race<BF16, VEC>(p, b, s, j - p.ngs, r);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+int64_t ee_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct EeLayout {
+  size_t part_off, race_off, dec_off, total;
+};
+
+size_t ee_round256(size_t x) { return (x + 255) / 256 * 256; }
+
+EeLayout ee_layout(int32_t B, int32_t V, int32_t max_k) {
+  const size_t nc = static_cast<size_t>(ee_ceil_div(V, chunk_tokens(false)));
+  const size_t S = static_cast<size_t>(max_k) + 1;
+  EeLayout L;
+  L.part_off = 0;
+  L.race_off = ee_round256(static_cast<size_t>(B) * S * kStageRows * nc * sizeof(uint64_t));
+  L.dec_off = L.race_off + ee_round256(static_cast<size_t>(B) * nc * sizeof(uint64_t));
+  L.total = L.dec_off + ee_round256(static_cast<size_t>(B) * S * kDecSlots * sizeof(uint64_t));
+  return L;
+}
+
+// Zeroes the decision records after the verify kernel (same stream).
+__global__ __launch_bounds__(kThreads) void ee_clear_records(uint64_t* dec, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    dec[i] = 0u;
+}
+
+template <bool BF16, bool VEC>
+int ee_launch(const EeParams& prm, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((sv_verify_ee<BF16, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
+                     0, stream, prm);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  const int64_t n_dec = static_cast<int64_t>(prm.B) * (prm.max_k + 1) * kDecSlots;
+  const int64_t clear_wgs = std::min<int64_t>(1024, (n_dec + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(ee_clear_records, dim3(static_cast<uint32_t>(clear_wgs)), dim3(kThreads), 0,
+                     stream, prm.dec, n_dec);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_early_exit_workspace_bytes(int32_t B, int32_t V, int32_t max_k) {
+  if (B < 1 || V < 1 || max_k < 0 || max_k > SV_KMAX) return 0;
+  return ee_layout(B, V, max_k).total;
+}
+
+int spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits,
+                                  int32_t dtype, int32_t B, int32_t V, int32_t max_k,
+                                  int32_t n_draft_rows, const int32_t* draft_offsets,
+                                  const int32_t* draft_tokens, const float* temperature,
+                                  uint64_t seed, int32_t* accept_len, int32_t* out_tokens,
+                                  float* p_at_draft, float* q_at_draft, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!target_logits || !draft_offsets || !accept_len || !out_tokens || !workspace ||
+      !temperature)
+    return SV_ERR_NULL;
+  if (n_draft_rows > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_NULL;
+  if (B < 1 || V < 1 || max_k < 0 || max_k > SV_KMAX || n_draft_rows < 0) return SV_ERR_SHAPE;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (workspace_bytes < spec_verify_early_exit_workspace_bytes(B, V, max_k) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return SV_ERR_WORKSPACE;
+  const bool bf16 = dtype == SV_BF16;
+  const EeLayout L = ee_layout(B, V, max_k);
+  char* ws = static_cast<char*>(workspace);
+  EeParams prm;
+  prm.target = target_logits;
+  prm.draft = draft_logits;
+  prm.offsets = draft_offsets;
+  prm.tokens = draft_tokens;
+  prm.temperature = temperature;
+  prm.k0 = static_cast<uint32_t>(seed);
+  prm.k1 = static_cast<uint32_t>(seed >> 32);
+  prm.B = B;
+  prm.V = V;
+  prm.max_k = max_k;
+  prm.n_draft_rows = n_draft_rows;
+  prm.nc = static_cast<int32_t>(ee_ceil_div(V, chunk_tokens(bf16)));
+  prm.ngs = static_cast<int32_t>(ee_ceil_div(static_cast<int64_t>(kStageRows) * prm.nc, kGroupItems));
+  prm.ngr = static_cast<int32_t>(ee_ceil_div(prm.nc, kRaceChunks));
+  prm.part = reinterpret_cast<uint64_t*>(ws + L.part_off);
+  prm.race = reinterpret_cast<uint64_t*>(ws + L.race_off);
+  prm.dec = reinterpret_cast<uint64_t*>(ws + L.dec_off);
+  prm.accept_len = accept_len;
+  prm.out_tokens = out_tokens;
+  prm.p_at = p_at_draft;
+  prm.q_at = q_at_draft;
+  const int64_t grid = static_cast<int64_t>(max_k + 1) * B * (prm.ngs + prm.ngr);
+  if (grid > INT32_MAX) return SV_ERR_SHAPE;
+  const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
+  const bool vec = row_bytes % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(target_logits) & 15u) == 0 &&
+                   (!draft_logits || (reinterpret_cast<uintptr_t>(draft_logits) & 15u) == 0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (bf16) return vec ? ee_launch<true, true>(prm, grid, st) : ee_launch<true, false>(prm, grid, st);
+  return vec ? ee_launch<false, true>(prm, grid, st) : ee_launch<false, false>(prm, grid, st);
+}
+
+}  // extern "C"
