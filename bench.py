@@ -21,7 +21,9 @@ Reported:
 --op draft times the draft-side sampler instead (spec_draft_sample over the
 workload's draft rows at step 0, one row per request) against the VALU issue
 rate, since its exponential race is arithmetic-bound; --op commit times the
-commit step (spec_commit_tokens) on the workload's verify outputs.
+commit step (spec_commit_tokens) on the workload's verify outputs; --op
+early-exit times spec_verify_sample_early_exit on the same batch, whose
+roofline counts only the rows a request needs up to its first rejection.
 """
 from __future__ import annotations
 
@@ -40,13 +42,14 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified draft positions/sec + HBM GB/s (% peak), B=64 K=4 V=128256 bf16"
 # the verify kernel's sources: committed traffic counters apply while these are unchanged
-KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_scaled_amd", "csrc", name)
-                  for name in ("spec_verify.hip", "device_common.h")]
+CSRC = os.path.join(ROOT, "rejection_sampling_verify_scaled_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, name) for name in ("spec_verify.hip", "device_common.h")]
+EE_KERNEL_SOURCES = [os.path.join(CSRC, name) for name in ("early_exit.hip", "device_common.h")]
 
 
-def kernel_source_sha256() -> str:
+def kernel_source_sha256(sources=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources or KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -62,10 +65,12 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("verify", "draft", "commit"), default="verify",
+    ap.add_argument("--op", choices=("verify", "draft", "commit", "early-exit"),
+                    default="verify",
                     help="verify: the verify step (the metric); draft: the draft-side "
                          "sampler on the workload's draft rows at step 0; commit: the "
-                         "commit step on the workload's verify outputs")
+                         "commit step on the workload's verify outputs; early-exit: the "
+                         "early-exit verify on the same batch")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -80,6 +85,24 @@ def algorithmic_bytes(batch) -> int:
     for b in range(batch.B):
         k = int(batch.offsets[b + 1] - batch.offsets[b])
         rows = (2 * k + 1) if batch.temperature[b] > 0 else (k + 1)
+        tot += rows * batch.V * esz
+    return tot
+
+
+def early_exit_bytes(batch, accept_len) -> int:
+    """The rows an early exit needs, each read once: a sampled request that
+    rejects at position n reads target and draft rows 0..n, one that accepts
+    all K_b reads all of them and the bonus row; a greedy request reads target
+    rows 0..n."""
+    esz = 2 if batch.dtype == 1 else 4
+    tot = 0
+    for b in range(batch.B):
+        k = int(batch.offsets[b + 1] - batch.offsets[b])
+        n = int(accept_len[b])
+        if batch.temperature[b] > 0:
+            rows = 2 * k + 1 if n == k else 2 * (n + 1)
+        else:
+            rows = n + 1
         tot += rows * batch.V * esz
     return tot
 
@@ -110,15 +133,15 @@ class Hip:
         return float(ms.value)
 
 
-def traffic_record(workload: int):
+def traffic_record(workload: int, kernel: str = "sv_verify", sources=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_sv_verify_workload{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_workload{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_sha256():
+    if rec.get("source_sha256") != kernel_source_sha256(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -361,7 +384,8 @@ def main():
     out = torch.empty(n_d + B, dtype=torch.int32, device=dev)
     pa = torch.empty(n_d, dtype=torch.float32, device=dev)
     qa = torch.empty(n_d, dtype=torch.float32, device=dev)
-    ws_n = binding.workspace_bytes(B, V, K)
+    ee = args.op == "early-exit"
+    ws_n = binding.early_exit_workspace_bytes(B, V, K) if ee else binding.workspace_bytes(B, V, K)
     ws = torch.zeros(ws_n, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -374,14 +398,15 @@ def main():
                         vp(d["temperature"].data_ptr()), ctypes.c_uint64(batch.seed),
                         vp(acc.data_ptr()), vp(out.data_ptr()), vp(pa.data_ptr()),
                         vp(qa.data_ptr()), vp(ws.data_ptr()), ws_n, sh))
-    call = lib.spec_verify_sample
+    call = lib.spec_verify_sample_early_exit if ee else lib.spec_verify_sample
+    name = "spec_verify_sample_early_exit" if ee else "spec_verify_sample"
     torch.cuda.synchronize()
     print(f"[bench] B={B} K={K} V={V} copies={copies} ({copies * per_copy / 1e9:.2f} GB); "
           f"warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         rc = call(*argsets[i % copies])
         if rc != 0:
-            raise SystemExit(f"spec_verify_sample returned {rc}")
+            raise SystemExit(f"{name} returned {rc}")
     torch.cuda.synchronize()
 
     if args.traffic_probe:
@@ -415,20 +440,26 @@ def main():
 
     # ---- cross-check: events the library records around each single launch
     # (each pair of event records adds its own small overhead to the figure)
-    n_t = min(args.steps, 200)
-    evs = [(hip.event(), hip.event()) for _ in range(n_t)]
-    timed = lib.spec_verify_sample_timed
-    for i in range(n_t):
-        rc = timed(*argsets[i % copies], evs[i][0], evs[i][1])
-        if rc != 0:
-            raise SystemExit(f"spec_verify_sample_timed returned {rc}")
-    torch.cuda.synchronize()
-    ev_us = 1e3 * sum(hip.elapsed_ms(a, b) for a, b in evs) / n_t
-    # the timed region is `steps` back-to-back launches of the one kernel
     k_us = ms_per_step * 1e3
-    achieved = alg / (k_us * 1e-6) / 1e9
-    print(f"[bench] sv_verify kernel {k_us:.2f} us per launch over the timed region, "
-          f"{ev_us:.2f} us with events around each launch", file=sys.stderr, flush=True)
+    if ee:
+        # the timed region is `steps` back-to-back calls of two launches each:
+        # sv_verify_ee, then the small kernel that clears its decision records
+        ev_us = None
+        print(f"[bench] sv_verify_ee + ee_clear_records {k_us:.2f} us per call over the "
+              "timed region", file=sys.stderr, flush=True)
+    else:
+        n_t = min(args.steps, 200)
+        evs = [(hip.event(), hip.event()) for _ in range(n_t)]
+        timed = lib.spec_verify_sample_timed
+        for i in range(n_t):
+            rc = timed(*argsets[i % copies], evs[i][0], evs[i][1])
+            if rc != 0:
+                raise SystemExit(f"spec_verify_sample_timed returned {rc}")
+        torch.cuda.synchronize()
+        ev_us = 1e3 * sum(hip.elapsed_ms(a, b) for a, b in evs) / n_t
+        # the timed region is `steps` back-to-back launches of the one kernel
+        print(f"[bench] sv_verify kernel {k_us:.2f} us per launch over the timed region, "
+              f"{ev_us:.2f} us with events around each launch", file=sys.stderr, flush=True)
 
     # ---- the achievable line: a plain 1 GiB device-to-device copy (torch's copy
     # kernel) on the same stream, counted as bytes read plus bytes written
@@ -452,6 +483,11 @@ def main():
     torch.cuda.synchronize()
     gpu_acc = acc.cpu().numpy()
     gpu_out = out.cpu().numpy()
+    if ee:
+        # the rows this outcome needs (the accept lengths are checked against
+        # the oracle below)
+        alg = early_exit_bytes(batch, gpu_acc)
+    achieved = alg / (k_us * 1e-6) / 1e9
 
     line = {
         "metric": METRIC,
@@ -469,15 +505,19 @@ def main():
         "config": {"workload": batch.label, "B": B, "K": K, "V": V,
                    "sampled_requests": int((batch.temperature > 0).sum()),
                    "greedy_requests": int((batch.temperature == 0).sum()),
-                   "input_copies_rotated": copies},
+                   "input_copies_rotated": copies,
+                   "entry_point": name},
         "hbm_gbs_step": alg / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac_step": alg / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg,
         "bytes_per_verified_position": alg / positions,
-        "kernel_us": {"sv_verify": k_us, "sv_verify_single_launch_events": ev_us},
+        "kernel_us": ({"sv_verify_ee_and_clear": k_us} if ee else
+                      {"sv_verify": k_us, "sv_verify_single_launch_events": ev_us}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(args.workload),
-                     "kernel": "sv_verify"},
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": (traffic_record(args.workload, "sv_verify_ee", EE_KERNEL_SOURCES)
+                                 if ee else traffic_record(args.workload)),
+                     "kernel": "sv_verify_ee" if ee else "sv_verify"},
         "copy_gbs": {"value": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                      "what": "1 GiB device-to-device copy on the same stream, read + written bytes"},
     }
