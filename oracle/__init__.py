@@ -10,8 +10,10 @@ bonus rule and the greedy case of "Decodificación Especulativa y EAGLE"
 counter, so that a result is a pure function of the inputs and the seed.
 It also holds the draft-side sampler that precedes verification
 (``draft_sample``: one token per request from softmax(z/T), or the argmax at
-T = 0) and the commit step that follows it (``commit_tokens``: the emitted
-tokens appended to each request's token history).
+T = 0), the commit step that follows it (``commit_tokens``: the emitted
+tokens appended to each request's token history), and greedy verification of
+a draft tree (``tree_verify``: the longest accepted root-to-node path, then
+the argmax of its last node's row).
 """
 from __future__ import annotations
 
@@ -76,6 +78,10 @@ def load(path: str = LIB):
     lib.oracle_commit_tokens.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
                                          vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, vp]
     lib.oracle_commit_tokens.restype = ctypes.c_int
+    lib.oracle_tree_verify_greedy.argtypes = [ctypes.c_int, vp, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp,
+                                              vp]
+    lib.oracle_tree_verify_greedy.restype = ctypes.c_int
     if path == LIB:
         _lib = lib
     return lib
@@ -105,6 +111,16 @@ def race_exponential(seed: int, b: int, pos: int, v: int, lib=None) -> float:
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_logits(dtype: int, a):
+    if dtype == F32:
+        return np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == BF16:
+        return np.ascontiguousarray(a, dtype=np.uint16)
+    if dtype == F64:
+        return np.ascontiguousarray(a, dtype=np.float64)
+    raise ValueError(f"unknown dtype {dtype}")
 
 
 def verify(dtype: int, target, draft, offsets, tokens, temperature, seed: int, V: int,
@@ -212,3 +228,25 @@ def commit_tokens(offsets, accept_len, out_tokens, seq_tokens, seq_len, max_k: i
     if rc != 0:
         raise ValueError(f"oracle_commit_tokens rejected its arguments (rc={rc})")
     return dict(seq_tokens=seq, seq_len=lens, next_tokens=nxt, status=st)
+
+
+def tree_verify(dtype: int, target, node_offsets, parents, tokens, V: int, max_nodes: int,
+                n_rows=None, lib=None) -> dict:
+    """Greedy tree verification (see oracle_tree_verify_greedy in spec_oracle.c):
+    accept_len [B], out_tokens [n_rows], accept_nodes [n_rows]."""
+    lib = lib or load()
+    target = _as_logits(dtype, target)
+    node_offsets = np.ascontiguousarray(node_offsets, dtype=np.int32)
+    parents = np.ascontiguousarray(parents, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    B = node_offsets.size - 1
+    n = int(node_offsets[-1]) if n_rows is None else int(n_rows)
+    acc = np.full(B, -3, dtype=np.int32)
+    out = np.full(max(n, 1), -3, dtype=np.int32)
+    nodes = np.full(max(n, 1), -3, dtype=np.int32)
+    rc = lib.oracle_tree_verify_greedy(dtype, _ptr(target), B, V, max_nodes, n,
+                                       _ptr(node_offsets), _ptr(parents), _ptr(tokens), _ptr(acc),
+                                       _ptr(out), _ptr(nodes))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_verify_greedy rejected its arguments (rc={rc})")
+    return dict(accept_len=acc, out_tokens=out[:n], accept_nodes=nodes[:n])

@@ -34,9 +34,11 @@
  * It also holds the draft-side sampler that precedes verification
  * (oracle_draft_sample, at the end of this file): one token per request from
  * softmax(z / T) by the same kind of race on its own Philox stream (tag 2),
- * or the argmax at T = 0; and the commit step that follows it
+ * or the argmax at T = 0; the commit step that follows it
  * (oracle_commit_tokens): the emitted tokens appended to each request's
- * token history on the device.
+ * token history on the device; and greedy verification of a draft tree
+ * (oracle_tree_verify_greedy): the longest root-to-node path whose every
+ * token is the argmax of its parent's target row.
  *
  * Philox4x32-10 is written from its published definition (Salmon, Moraes,
  * Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): ten
@@ -455,6 +457,98 @@ int oracle_commit_tokens(int32_t B, int32_t max_k, int32_t n_draft_rows, const i
     seq_len[b] = L + n + 1;
     next_tokens[b] = out_tokens[(int64_t)off + b + n];
     status[b] = n + 1;
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------- tree verify */
+
+/* Greedy verification of a draft tree ("Decodificación Especulativa y EAGLE",
+ * section on tree attention verification: every node of the tree is scored in
+ * one target pass, each node seeing only its ancestors, and the result is the
+ * longest prefix along any accepted root-to-node path; Perplexity's post,
+ * section "EAGLE": the chosen sequence is followed by one extra token from the
+ * target).  With the greedy rule of section "La Regla de Exactitud" a draft
+ * node is accepted when its parent is accepted and its token is the argmax of
+ * the parent's target row.
+ *
+ * Request b owns nodes i = 0..N_b-1, N_b = node_offsets[b+1] - node_offsets[b],
+ * at packed rows node_offsets[b] + i.  Node 0 is the root (the last committed
+ * token; its parent and token entries are not read).  Node i >= 1 has parent
+ * parents[off + i] in [0, i) and token tokens[off + i] in [0, V).  Target row
+ * of node i: the distribution of the token that follows the path root..i.
+ *
+ * Per request:
+ *   g_i = argmax of node i's row (lowest index on ties), for every node;
+ *   accepted(0) = 1; accepted(i) = accepted(parent) and token_i == g_parent;
+ *   depth(0) = 0; depth(i) = depth(parent) + 1;
+ *   c = the accepted node of greatest depth, lowest index among equals (two
+ *       accepted nodes of equal depth need siblings with equal tokens);
+ *   d = depth(c); path = root = a_0, a_1, ..., a_d = c (each the parent of the
+ *       next).
+ * Outputs: accept_len[b] = d; out_tokens[off + j] = token of a_{j+1} for j < d,
+ * out_tokens[off + d] = g_c, -1 after; accept_nodes[off + j] = a_j for j <= d,
+ * -1 after.  Failures set accept_len[b] = -1: a slice outside [0, n_rows) or
+ * N_b outside [1, max_nodes] (nothing else written), or a parent outside
+ * [0, i), a token outside [0, V), a row with no finite maximum (the request's
+ * outputs filled with -1).
+ */
+int oracle_tree_verify_greedy(int dtype, const void* target, int32_t B, int32_t V,
+                              int32_t max_nodes, int32_t n_rows, const int32_t* node_offsets,
+                              const int32_t* parents, const int32_t* tokens,
+                              int32_t* accept_len, int32_t* out_tokens,
+                              int32_t* accept_nodes) {
+  if (B < 1 || V < 1 || max_nodes < 1 || max_nodes > 1024 || !target || !node_offsets ||
+      !parents || !tokens || !accept_len || !out_tokens || !accept_nodes)
+    return -1;
+  int32_t g[1024], depth[1024], path[1024];
+  unsigned char acc[1024];
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t off = node_offsets[b], off1 = node_offsets[b + 1];
+    const int32_t N = off1 - off;
+    if (off < 0 || off1 > n_rows || off1 < off || N < 1 || N > max_nodes) {
+      accept_len[b] = -1;
+      continue;
+    }
+    int ok = 1;
+    for (int32_t i = 1; i < N && ok; ++i) {
+      const int32_t par = parents[off + i], tok = tokens[off + i];
+      if (par < 0 || par >= i || tok < 0 || tok >= V) ok = 0;
+    }
+    for (int32_t i = 0; i < N && ok; ++i) {
+      g[i] = row_argmax(target, dtype, (int64_t)off + i, V);
+      if (g[i] < 0) ok = 0;
+    }
+    if (!ok) {
+      accept_len[b] = -1;
+      for (int32_t i = 0; i < N; ++i) {
+        out_tokens[off + i] = -1;
+        accept_nodes[off + i] = -1;
+      }
+      continue;
+    }
+    /* acceptance and depth, parents before children */
+    acc[0] = 1;
+    depth[0] = 0;
+    for (int32_t i = 1; i < N; ++i) {
+      const int32_t par = parents[off + i];
+      acc[i] = acc[par] && tokens[off + i] == g[par];
+      depth[i] = depth[par] + 1;
+    }
+    int32_t c = 0;
+    for (int32_t i = 1; i < N; ++i)
+      if (acc[i] && depth[i] > depth[c]) c = i;
+    const int32_t d = depth[c];
+    int32_t u = c;
+    for (int32_t j = d; j >= 0; --j) {
+      path[j] = u;
+      u = j > 0 ? parents[off + u] : u;
+    }
+    accept_len[b] = d;
+    for (int32_t j = 0; j < N; ++j) {
+      out_tokens[off + j] = j < d ? tokens[off + path[j + 1]] : (j == d ? g[c] : -1);
+      accept_nodes[off + j] = j <= d ? path[j] : -1;
+    }
   }
   return 0;
 }

@@ -315,3 +315,137 @@ def draft_step_rows(batch: Batch, t: int) -> np.ndarray:
         else:
             rows.append(batch.target[int(batch.offsets[b]) + b])
     return np.stack(rows)
+
+
+# ------------------------------------------------------------------ draft trees
+
+@dataclasses.dataclass(frozen=True)
+class TreeWorkload:
+    """A synthetic draft-tree workload (EAGLE-style trees: a few candidates per
+    level, a few levels; "Decodificación Especulativa y EAGLE", section on
+    EAGLE's tree drafting, and the tree drawn in its tree-attention section)."""
+
+    name: str
+    B: int
+    depth: tuple             # (lo, hi) inclusive levels below the root
+    width: tuple             # (lo, hi) inclusive nodes per level
+    V: int
+    dtype: int
+    target_sigma: float
+    peak_frac: float
+    peak_boost: float
+    draft_sigma: tuple       # ("uniform", lo, hi) per request
+
+    @property
+    def max_nodes(self) -> int:
+        return 1 + self.depth[1] * self.width[1]
+
+
+TREE_WORKLOADS = {
+    "tree-small": TreeWorkload("tree-small B=8 depth 3 width 3 V=1000 f32", 8, (3, 3), (3, 3),
+                               1000, DTYPE_F32, 2.0, 0.01, 6.0, ("uniform", 0.25, 1.0)),
+    "tree-eagle": TreeWorkload("tree-eagle B=16 depth 5 width 8 V=128256 bf16", 16, (5, 5),
+                               (8, 8), 128256, DTYPE_BF16, 3.0, 0.01, 8.0,
+                               ("uniform", 0.25, 2.0)),
+    "tree-ragged": TreeWorkload("tree-ragged B=64 depth 2..6 width 2..8 V=152064 bf16", 64,
+                                (2, 6), (2, 8), 152064, DTYPE_BF16, 3.0, 0.01, 8.0,
+                                ("uniform", 0.25, 2.0)),
+}
+
+
+@dataclasses.dataclass
+class TreeBatch:
+    """A packed batch of draft trees (host numpy arrays).
+
+    Request b owns nodes i = 0..N_b-1 at packed rows offsets[b] + i; node 0 is the
+    root (parents / tokens entry -1), node i >= 1 has parents[offsets[b] + i] in
+    [0, i) and token tokens[offsets[b] + i].  target[offsets[b] + i] is the target
+    row after the path root..i."""
+
+    dtype: int
+    B: int
+    V: int
+    max_nodes: int
+    target: np.ndarray       # [sum(N_b), V] float32 or uint16 (bf16 bits)
+    offsets: np.ndarray      # [B+1] int32
+    parents: np.ndarray      # [sum(N_b)] int32
+    tokens: np.ndarray       # [sum(N_b)] int32
+    label: str = ""
+
+
+def make_tree_batch(name: str, step: int = 0, B: Optional[int] = None,
+                    workers: Optional[int] = None) -> TreeBatch:
+    """Generate a draft-tree workload by name.
+
+    Seeds: tree shapes and noise levels from ``default_rng([0x5356, 0x7472, k, step])``
+    (k = the workload's position in TREE_WORKLOADS), request b's rows and tokens
+    from ``default_rng([0x5356, 0x7472, k, step, b])``.  Per request: D levels
+    below the root and W nodes per level (uniform in the workload's ranges).
+    Level l's W nodes hang under the nodes of level l - 1, which the drafter
+    ranks by its own confidence (creation order): node j of level l goes to
+    the parent of rank min(floor(G), W_prev - 1), G geometric with mean 1.5,
+    so the leading nodes get most children.  Every node has a target row
+    ~ N(0, sigma^2) with round(peak_frac V) entries raised by peak_boost.  A
+    parent's children take, in order, the top tokens of the drafter's row for
+    that parent (the parent's target row + N(0, sigma_b^2)): distinct
+    sibling tokens, as a top-k expansion gives.  Rows are rounded to the
+    storage dtype.  Nodes are numbered level by level.
+    """
+    w = TREE_WORKLOADS[name]
+    k_id = list(TREE_WORKLOADS).index(name)
+    rng = np.random.default_rng([GEN_TAG, 0x7472, k_id, step])
+    Bn = w.B if B is None else min(B, w.B)
+    depth = rng.integers(w.depth[0], w.depth[1] + 1, size=w.B)[:Bn]
+    width = rng.integers(w.width[0], w.width[1] + 1, size=w.B)[:Bn]
+    sigma = rng.uniform(w.draft_sigma[1], w.draft_sigma[2], size=w.B)[:Bn]
+    sizes = 1 + depth * width
+    offsets = np.zeros(Bn + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(sizes)
+    n = int(offsets[-1])
+    V = w.V
+    sdt = np.float32 if w.dtype == DTYPE_F32 else np.uint16
+    target = np.empty((n, V), dtype=sdt)
+    parents = np.full(n, -1, dtype=np.int32)
+    tokens = np.full(n, -1, dtype=np.int32)
+    n_pk = int(round(w.peak_frac * V))
+
+    def one(b: int) -> None:
+        r = np.random.default_rng([GEN_TAG, 0x7472, k_id, step, b])
+        D, W, o = int(depth[b]), int(width[b]), int(offsets[b])
+        N = 1 + D * W
+        z = r.standard_normal((N, V), dtype=np.float32) * np.float32(w.target_sigma)
+        if n_pk > 0:
+            for i in range(N):
+                z[i, r.choice(V, size=n_pk, replace=False)] += np.float32(w.peak_boost)
+        target[o:o + N] = to_storage(z, w.dtype)
+        prev = [0]
+        nxt = 1
+        for _ in range(D):
+            ranks = np.minimum(np.floor(r.geometric(1.0 / 1.5, size=W) - 1).astype(int),
+                               len(prev) - 1)
+            kids = {}
+            for j in range(W):
+                kids.setdefault(prev[int(ranks[j])], []).append(j)
+            level = []
+            for par in sorted(kids):
+                cnt = len(kids[par])
+                drow = storage_to_f64(target[o + par], w.dtype) + \
+                    r.standard_normal(V) * float(sigma[b])
+                top = np.argsort(-drow, kind="stable")[:cnt]
+                for t in top:
+                    parents[o + nxt] = par
+                    tokens[o + nxt] = int(t)
+                    level.append(nxt)
+                    nxt += 1
+            prev = level
+
+    nw = workers or _workers()
+    if nw == 1 or Bn < 8:
+        for b in range(Bn):
+            one(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(nw) as ex:
+            list(ex.map(one, range(Bn)))
+    return TreeBatch(dtype=w.dtype, B=Bn, V=V, max_nodes=w.max_nodes, target=target,
+                     offsets=offsets.astype(np.int32), parents=parents, tokens=tokens,
+                     label=w.name)

@@ -654,8 +654,163 @@ def pin_commit_after_verify(lib):
         assert row[L + n] == v["out_tokens"][offsets[b] + b + n] == r["next_tokens"][b]
 
 
+# ------------------------------------------------------------------ tree verify
+
+
+def read_tree_cases():
+    """Cases of tests/golden/tree_example.txt: (name, parents, tokens, argmax spec,
+    expected accept, out, nodes); parents and tokens with the root's -1 prepended."""
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "tree_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "case":
+                cur = {"name": vals[0]}
+                cases.append(cur)
+            elif key in ("parents", "tokens"):
+                cur[key] = [-1] + [int(v) for v in vals]
+            elif key == "argmax":
+                cur[key] = vals
+            elif key == "accept":
+                cur[key] = int(vals[0])
+            else:
+                cur[key] = [int(v) for v in vals]
+    return cases
+
+
+def pin_tree_page_example(lib):
+    """The page's two-level tree, argmaxes fixed by hand, expected outputs by hand."""
+    V = 10
+    for c in read_tree_cases():
+        N = len(c["parents"])
+        rows = np.full((N, V), -1.0)
+        for i, spec in enumerate(c["argmax"]):
+            g = int(spec.rstrip("t"))
+            rows[i, g] = 2.0
+            if spec.endswith("t"):
+                rows[i, g + 1] = 2.0
+        r = oracle.tree_verify(oracle.F64, rows, [0, N], c["parents"], c["tokens"], V, N, lib=lib)
+        assert r["accept_len"].tolist() == [c["accept"]], (c["name"], r["accept_len"])
+        assert r["out_tokens"].tolist() == c["out"], (c["name"], r["out_tokens"])
+        assert r["accept_nodes"].tolist() == c["nodes"], (c["name"], r["accept_nodes"])
+
+
+def pin_tree_chain_is_linear(lib):
+    """A tree whose node i has parent i - 1 is a linear draft: the same rows, tokens
+    and outputs as the greedy linear verify (itself pinned above)."""
+    rng = np.random.default_rng(41)
+    V, B = 12, 120
+    ks = rng.integers(0, 8, size=B)
+    offs = np.zeros(B + 1, np.int32)
+    offs[1:] = np.cumsum(ks + 1)
+    rows = rng.normal(0, 1.5, size=(int(offs[-1]), V))
+    g = rows.argmax(axis=1)
+    lin_tok, parents, tree_tok = [], [], []
+    for b in range(B):
+        o = int(offs[b])
+        for t in range(int(ks[b])):
+            # mostly the target's argmax, so that long prefixes occur
+            x = int(g[o + t]) if rng.random() < 0.75 else int(rng.integers(0, V))
+            lin_tok.append(x)
+            tree_tok.append(x)
+            parents.append(t)
+        parents.insert(len(parents) - int(ks[b]), -1)
+        tree_tok.insert(len(tree_tok) - int(ks[b]), -1)
+    doffs = np.zeros(B + 1, np.int32)
+    doffs[1:] = np.cumsum(ks)
+    lin = oracle.verify(oracle.F64, rows, None, doffs, np.array(lin_tok, np.int32),
+                        np.zeros(B, np.float32), 0, V, 8, lib=lib)
+    tree = oracle.tree_verify(oracle.F64, rows, offs, parents, tree_tok, V, 9, lib=lib)
+    assert (tree["accept_len"] == lin["accept_len"]).all()
+    assert (tree["out_tokens"] == lin["out_tokens"]).all()
+    for b in range(B):
+        o, n = int(offs[b]), int(lin["accept_len"][b])
+        assert tree["accept_nodes"][o:o + n + 1].tolist() == list(range(n + 1))
+        assert (tree["accept_nodes"][o + n + 1:int(offs[b + 1])] == -1).all()
+    assert 0 < (lin["accept_len"] > 2).sum() < B
+
+
+def tree_by_paths(rows, parents, tokens):
+    """Brute force: every node's root path, accepted if each token on it is numpy's
+    first-occurrence argmax of its parent's row; the longest such path wins, the
+    lowest end node among equally long ones."""
+    N = len(parents)
+    best = (0, 0, [0])
+    for i in range(N):
+        path = [i]
+        while path[-1] != 0:
+            path.append(parents[path[-1]])
+        path.reverse()
+        if all(tokens[v] == int(np.argmax(rows[u])) for u, v in zip(path, path[1:])):
+            if len(path) - 1 > best[0]:
+                best = (len(path) - 1, i, path)
+    d, c, path = best
+    out = [tokens[v] for v in path[1:]] + [int(np.argmax(rows[c]))]
+    return d, out + [-1] * (N - d - 1), path + [-1] * (N - d - 1)
+
+
+def pin_tree_brute_force(lib):
+    """Random trees of up to 14 nodes over a 4-token vocabulary (so that siblings often
+    share tokens and several paths are accepted) against path enumeration."""
+    rng = np.random.default_rng(43)
+    V, B = 4, 300
+    sizes = rng.integers(1, 15, size=B)
+    offs = np.zeros(B + 1, np.int32)
+    offs[1:] = np.cumsum(sizes)
+    rows = rng.integers(-3, 3, size=(int(offs[-1]), V)).astype(np.float64)  # many ties
+    parents, tokens, want = [], [], []
+    for b in range(B):
+        N = int(sizes[b])
+        par = [-1] + [int(rng.integers(max(0, i - 3), i)) for i in range(1, N)]  # deep trees
+        blk = rows[offs[b]:offs[b + 1]]
+        # half the tokens planted on the first maximum of the parent's row
+        tok = [-1] + [int(np.argmax(blk[par[i]])) if rng.random() < 0.5 else
+                      int(rng.integers(0, V)) for i in range(1, N)]
+        parents += par
+        tokens += tok
+        want.append(tree_by_paths(rows[offs[b]:offs[b + 1]], par, tok))
+    r = oracle.tree_verify(oracle.F64, rows, offs, parents, tokens, V, 14, lib=lib)
+    for b in range(B):
+        o, o1 = int(offs[b]), int(offs[b + 1])
+        d, out, nodes = want[b]
+        assert r["accept_len"][b] == d, (b, r["accept_len"][b], d)
+        assert r["out_tokens"][o:o1].tolist() == out, b
+        assert r["accept_nodes"][o:o1].tolist() == nodes, b
+    assert (r["accept_len"] >= 3).sum() > 10
+
+
+def pin_tree_faults(lib):
+    """Bad parents, bad tokens, non-finite rows and bad slices fail only their own
+    request; a request whose slice is bad gets no output writes."""
+    V = 6
+    rows = np.zeros((30, V))
+    rows[:, 2] = 1.0
+    offs = [0, 3, 6, 9, 12, 15, 15, 18, 21, 30]
+    parents = [-1, 0, 1] * 10
+    tokens = [-1, 2, 2] * 10
+    parents[5] = 2          # request 1: a node's parent is itself
+    tokens[7] = V           # request 2: token outside the vocabulary
+    rows[10] = np.nan       # request 3: a row with no finite maximum
+    rows[13] = -np.inf      # request 4: likewise
+    parents[19] = -5        # request 7: negative parent
+    r = oracle.tree_verify(oracle.F64, rows, offs, parents, tokens, V, 8, lib=lib)
+    assert r["accept_len"].tolist() == [2, -1, -1, -1, -1, -1, 2, -1, -1]
+    out = r["out_tokens"]
+    assert out[0:3].tolist() == [2, 2, 2] and out[15:18].tolist() == [2, 2, 2]
+    assert r["accept_nodes"][15:18].tolist() == [0, 1, 2]
+    for o, o1 in ((3, 6), (6, 9), (9, 12), (12, 15), (18, 21)):
+        assert (out[o:o1] == -1).all() and (r["accept_nodes"][o:o1] == -1).all()
+    # request 5 is empty (N = 0), request 8 has 9 nodes > max_nodes = 8: nothing written
+    assert (out[21:30] == -3).all() and (r["accept_nodes"][21:30] == -3).all()
+
+
 ALL_PINS = [pin_philox_kat, pin_philox_rocrand, pin_u01, pin_softmax_vs_scipy,
             pin_greedy_vs_numpy, pin_exact_enumeration, pin_plain_sampling, pin_closed_form,
             pin_temperature_invariance, pin_identical_draft_accepts, pin_disjoint_draft_rejects,
             pin_faults, pin_draft_distribution, pin_draft_greedy, pin_draft_streams,
-            pin_draft_faults, pin_commit_example, pin_commit_after_verify]
+            pin_draft_faults, pin_commit_example, pin_commit_after_verify,
+            pin_tree_page_example, pin_tree_chain_is_linear, pin_tree_brute_force,
+            pin_tree_faults]

@@ -69,6 +69,19 @@ MUTANTS = {
     "commit_block_base": ("out_tokens[(int64_t)off + b + i]", "out_tokens[(int64_t)off + i]"),
     # commit: a history exactly at capacity rejected
     "commit_capacity": ("(int64_t)L + n + 1 > capacity", "(int64_t)L + n + 1 >= capacity"),
+    # tree: a node's token compared with its own row instead of its parent's
+    "tree_own_row": ("acc[i] = acc[par] && tokens[off + i] == g[par];",
+                     "acc[i] = acc[par] && tokens[off + i] == g[i];"),
+    # tree: a match under a rejected parent accepted
+    "tree_parent_ignored": ("acc[i] = acc[par] && tokens[off + i] == g[par];",
+                            "acc[i] = tokens[off + i] == g[par];"),
+    # tree: equally deep accepted nodes resolved to the highest index
+    "tree_last_tie": ("if (acc[i] && depth[i] > depth[c]) c = i;",
+                      "if (acc[i] && depth[i] >= depth[c]) c = i;"),
+    # tree: depth taken as the node index (right for chains only)
+    "tree_depth_index": ("depth[i] = depth[par] + 1;", "depth[i] = i;"),
+    # tree: the extra token taken from the parent of the chosen node
+    "tree_bonus_row": ("(j == d ? g[c] : -1)", "(j == d ? g[path[d > 0 ? d - 1 : 0]] : -1)"),
     # uniform map that can return 0
     "u01_map": ("return (2.0 * (double)(x >> 9) + 1.0) / 16777216.0;",
                 "return (double)(x >> 8) / 16777216.0;"),
@@ -80,7 +93,8 @@ ORDER = [P.pin_philox_kat, P.pin_u01, P.pin_softmax_vs_scipy, P.pin_greedy_vs_nu
          P.pin_disjoint_draft_rejects, P.pin_faults, P.pin_plain_sampling,
          P.pin_exact_enumeration, P.pin_closed_form, P.pin_draft_greedy, P.pin_draft_faults,
          P.pin_draft_distribution, P.pin_draft_streams, P.pin_commit_example,
-         P.pin_commit_after_verify]
+         P.pin_commit_after_verify, P.pin_tree_page_example, P.pin_tree_faults,
+         P.pin_tree_chain_is_linear, P.pin_tree_brute_force]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
