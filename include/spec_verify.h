@@ -71,6 +71,7 @@ extern "C" {
 #endif
 
 #define SV_KMAX 8 /* largest per-request draft length */
+#define SV_TREE_MAX_NODES 64 /* largest draft tree (root included), spec_verify_tree_greedy */
 
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
@@ -248,6 +249,62 @@ int spec_commit_tokens(int32_t B, int32_t max_k, int32_t n_draft_rows,
 
 /* Host function.  Static description of a status code. */
 const char* spec_verify_status_string(int status);
+
+/* ---------------------------------------------------------------- draft trees */
+
+/* Host function.  Workspace bytes spec_verify_tree_greedy needs (either
+ * dtype); 0 unless B >= 1, V >= 1 and 1 <= max_nodes <= SV_TREE_MAX_NODES.
+ * The workspace must be zero-filled once when allocated; every call leaves it
+ * zero again (unless a bounded wait expired, as for the verify step). */
+size_t spec_verify_tree_workspace_bytes(int32_t B, int32_t V, int32_t max_nodes);
+
+/* Greedy verification of a draft tree.  The drafter expanded several
+ * candidates per position into a tree and the target scored every node in
+ * one pass, each node attending only to its ancestors; the result is the
+ * longest prefix along an accepted root-to-node path ("Decodificación
+ * Especulativa y EAGLE", section on tree attention verification), followed by
+ * one extra target token (Perplexity's post, section "EAGLE").  With the
+ * greedy rule of section "La Regla de Exactitud" a node is accepted when its
+ * parent is accepted and its token is the argmax of the parent's target row
+ * (lowest index on ties).  Only the greedy rule is provided: the pages give
+ * no rule for sampling over a tree.
+ *
+ * Layout (DEVICE pointers, packed like the linear verify's target rows):
+ *   node_offsets  [B + 1] int32  request b owns nodes i = 0..N_b - 1,
+ *                                N_b = node_offsets[b+1] - node_offsets[b]
+ *   target_logits [n_rows][V]    row of node i at node_offsets[b] + i: the
+ *                                target distribution after the path root..i
+ *   parents       [n_rows] int32 parent of node i >= 1, in [0, i) (parents
+ *                                are numbered before their children); the
+ *                                root's entry (i = 0) is not read
+ *   tokens        [n_rows] int32 draft token of node i >= 1, in [0, V); the
+ *                                root's entry is not read (the root is the
+ *                                last token already emitted)
+ * Per request, with g_i the argmax of node i's row and c the accepted node
+ * of greatest depth d (lowest index among equally deep ones; two exist only
+ * when siblings share a token), path root = a_0, ..., a_d = c:
+ *   accept_len[b]                    = d (drafts accepted; d + 1 tokens emitted)
+ *   out_tokens[node_offsets[b] + j]  = token of a_{j+1} for j < d, g_c for j = d,
+ *                                      -1 for d < j < N_b
+ *   accept_nodes[node_offsets[b] + j] = a_j for j <= d, -1 after (optional:
+ *                                      NULL skips it; the node indices tell the
+ *                                      caller which KV-cache entries to keep)
+ * Per-request failures set accept_len[b] = -1: a slice outside [0, n_rows),
+ * N_b outside [1, max_nodes] (nothing else written); a parent outside
+ * [0, i), a token outside [0, V), or a row whose maximum is not finite (the
+ * request's out_tokens and accept_nodes entries set to -1).
+ * Ownership, streams and the workspace as for spec_verify_greedy; the
+ * workspace is the one sized by spec_verify_tree_workspace_bytes.  One
+ * kernel is enqueued on `stream`.
+ * Returns SV_OK, or a negative status with nothing enqueued (SV_ERR_NULL for
+ * a missing required pointer; SV_ERR_SHAPE for B < 1, V < 1, max_nodes
+ * outside [1, SV_TREE_MAX_NODES], n_rows < 0 or a grid too large;
+ * SV_ERR_DTYPE; SV_ERR_WORKSPACE; SV_ERR_LAUNCH). */
+int spec_verify_tree_greedy(const void* target_logits, int32_t dtype, int32_t B, int32_t V,
+                            int32_t max_nodes, int32_t n_rows, const int32_t* node_offsets,
+                            const int32_t* parents, const int32_t* tokens, int32_t* accept_len,
+                            int32_t* out_tokens, int32_t* accept_nodes, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "spec_verify.h")
 SV_F32 = 0
 SV_BF16 = 1
 SV_KMAX = 8
+SV_TREE_MAX_NODES = 64
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
           -4: "SV_ERR_WORKSPACE", -5: "SV_ERR_LAUNCH"}
 
@@ -65,6 +66,11 @@ def load_library(path: str = LIB_PATH):
     lib.spec_commit_tokens.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_int64, vp, i32, vp,
                                        vp, vp]
     lib.spec_commit_tokens.restype = ctypes.c_int
+    lib.spec_verify_tree_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_verify_tree_workspace_bytes.restype = sz
+    lib.spec_verify_tree_greedy.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]
+    lib.spec_verify_tree_greedy.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -306,6 +312,73 @@ def spec_commit_tokens(draft_offsets: torch.Tensor, accept_len: torch.Tensor,
     if rc != 0:
         raise SpecVerifyError("spec_commit_tokens", rc, lib.spec_verify_status_string(rc).decode())
     return next_tokens, status
+
+
+def tree_workspace_bytes(B: int, V: int, max_nodes: int) -> int:
+    return int(load_library().spec_verify_tree_workspace_bytes(B, V, max_nodes))
+
+
+def spec_verify_tree_greedy(target_logits: torch.Tensor, node_offsets: torch.Tensor,
+                            parents: torch.Tensor, tokens: torch.Tensor, max_nodes: int,
+                            accept_len: Optional[torch.Tensor] = None,
+                            out_tokens: Optional[torch.Tensor] = None,
+                            accept_nodes: Optional[torch.Tensor] = None,
+                            want_nodes: bool = True,
+                            workspace: Optional[torch.Tensor] = None, stream=None):
+    """Greedy draft-tree verify; returns (accept_len [B], out_tokens [n_rows],
+    accept_nodes [n_rows] or None)."""
+    lib = load_library()
+    if target_logits.dim() != 2:
+        raise ValueError("target_logits must be 2-D [rows, V]")
+    device = target_logits.device
+    if device.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
+    B = node_offsets.shape[0] - 1
+    if B < 1:
+        raise ValueError("need at least one request (node_offsets has B+1 entries)")
+    n, V = target_logits.shape
+    _check(target_logits, "target_logits", target_logits.dtype, (n, V), device)
+    _check(node_offsets, "node_offsets", torch.int32, (B + 1,), device)
+    _check(parents, "parents", torch.int32, (n,), device)
+    _check(tokens, "tokens", torch.int32, (n,), device)
+    if not 1 <= max_nodes <= SV_TREE_MAX_NODES:
+        raise ValueError(f"max_nodes must be in [1, {SV_TREE_MAX_NODES}]")
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=device)
+    if out_tokens is None:
+        out_tokens = torch.empty(max(n, 1), dtype=torch.int32, device=device)[:n]
+    if accept_nodes is None and want_nodes:
+        accept_nodes = torch.empty(max(n, 1), dtype=torch.int32, device=device)[:n]
+    _check(accept_len, "accept_len", torch.int32, (B,), device)
+    _check(out_tokens, "out_tokens", torch.int32, (n,), device)
+    if accept_nodes is not None:
+        _check(accept_nodes, "accept_nodes", torch.int32, (n,), device)
+    need = tree_workspace_bytes(B, V, max_nodes)
+    if workspace is None:  # zero-filled once; every completed call leaves it zeroed
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    rc = lib.spec_verify_tree_greedy(
+        _ptr(target_logits), _dtype_code(target_logits), B, V, max_nodes, n, _ptr(node_offsets),
+        _ptr(parents), _ptr(tokens), _ptr(accept_len), _ptr(out_tokens), _ptr(accept_nodes),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if rc != 0:
+        raise SpecVerifyError("spec_verify_tree_greedy", rc,
+                              lib.spec_verify_status_string(rc).decode())
+    return accept_len, out_tokens, accept_nodes
+
+
+def to_device_tree_batch(tb, device="cuda"):
+    """Upload a workloads.TreeBatch to the device."""
+    import numpy as np
+    if tb.target.dtype == np.uint16:
+        target = torch.from_numpy(tb.target.view(np.int16)).to(device).view(torch.bfloat16)
+    else:
+        target = torch.from_numpy(np.ascontiguousarray(tb.target, dtype=np.float32)).to(device)
+    return dict(target=target.reshape(-1, tb.V),
+                offsets=torch.from_numpy(tb.offsets).to(device),
+                parents=torch.from_numpy(tb.parents).to(device),
+                tokens=torch.from_numpy(tb.tokens).to(device))
 
 
 def to_device_batch(batch, device="cuda"):

@@ -12,7 +12,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", name)
-        for name in ("spec_verify.hip", "early_exit.hip", "draft_sample.hip", "commit_tokens.hip")]
+        for name in ("spec_verify.hip", "early_exit.hip", "draft_sample.hip", "commit_tokens.hip",
+                     "tree_verify.hip")]
 SRC = SRCS[0]  # the verify kernel's source (its sha256 keys the committed traffic counters)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")

@@ -151,3 +151,47 @@ def test_commit_rejects_bad_arguments(lib, case):
     rc = lib.spec_commit_tokens(a["B"], a["max_k"], a["nd"], a["offs"], a["acc"], a["out"],
                                 a["seq"], a["stride"], a["lens"], a["cap"], None, None, None)
     assert rc == expect
+
+
+def test_tree_workspace_bytes(lib):
+    n = lib.spec_verify_tree_workspace_bytes(16, 128256, 41)
+    assert n > 0 and n % 256 == 0
+    # float32 chunks (2048 tokens): 16 requests x 41 nodes x 63 chunks x 8 bytes
+    assert n >= 16 * 41 * 63 * 8
+    for bad in ((0, 10, 1), (1, 0, 1), (1, 10, 0), (1, 10, binding.SV_TREE_MAX_NODES + 1)):
+        assert lib.spec_verify_tree_workspace_bytes(*bad) == 0
+    assert binding.SV_TREE_MAX_NODES == 64
+
+
+@pytest.mark.parametrize("case", ["null_target", "null_offsets", "null_parents", "null_tokens",
+                                  "null_accept", "null_out", "null_ws", "B0", "V0", "nodes0",
+                                  "nodes_big", "rows_neg", "dtype", "ws_small", "ws_misaligned"])
+def test_tree_rejects_bad_arguments(lib, case):
+    keep = []
+
+    def p(n=1 << 16):
+        ptr, buf = _fake(n + 64)
+        keep.append(buf)
+        return ctypes.c_void_p((ptr.value + 15) // 16 * 16)
+    a = dict(tgt=p(), dtype=binding.SV_BF16, B=2, V=100, nodes=8, rows=12, offs=p(), par=p(),
+             tok=p(), acc=p(), out=p(), ws=p())
+    a["ws_n"] = lib.spec_verify_tree_workspace_bytes(2, 100, 8)
+    expect = {"null_target": -1, "null_offsets": -1, "null_parents": -1, "null_tokens": -1,
+              "null_accept": -1, "null_out": -1, "null_ws": -1, "B0": -2, "V0": -2,
+              "nodes0": -2, "nodes_big": -2, "rows_neg": -2, "dtype": -3, "ws_small": -4,
+              "ws_misaligned": -4}[case]
+    key = {"null_target": "tgt", "null_offsets": "offs", "null_parents": "par",
+           "null_tokens": "tok", "null_accept": "acc", "null_out": "out", "null_ws": "ws"}
+    if case in key: a[key[case]] = None
+    if case == "B0": a["B"] = 0
+    if case == "V0": a["V"] = 0
+    if case == "nodes0": a["nodes"] = 0
+    if case == "nodes_big": a["nodes"] = binding.SV_TREE_MAX_NODES + 1
+    if case == "rows_neg": a["rows"] = -1
+    if case == "dtype": a["dtype"] = 7
+    if case == "ws_small": a["ws_n"] -= 8
+    if case == "ws_misaligned": a["ws"] = ctypes.c_void_p(a["ws"].value + 4)
+    rc = lib.spec_verify_tree_greedy(a["tgt"], a["dtype"], a["B"], a["V"], a["nodes"], a["rows"],
+                                     a["offs"], a["par"], a["tok"], a["acc"], a["out"], None,
+                                     a["ws"], a["ws_n"], None)
+    assert rc == expect
