@@ -23,7 +23,9 @@ workload's draft rows at step 0, one row per request) against the VALU issue
 rate, since its exponential race is arithmetic-bound; --op commit times the
 commit step (spec_commit_tokens) on the workload's verify outputs; --op
 early-exit times spec_verify_sample_early_exit on the same batch, whose
-roofline counts only the rows a request needs up to its first rejection.
+roofline counts only the rows a request needs up to its first rejection; --op
+tree times greedy draft-tree verification (spec_verify_tree_greedy) on a
+seeded tree workload (--tree).
 """
 from __future__ import annotations
 
@@ -65,12 +67,16 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("verify", "draft", "commit", "early-exit"),
+    ap.add_argument("--tree", default="tree-eagle",
+                    choices=("tree-small", "tree-eagle", "tree-ragged"),
+                    help="tree workload for --op tree")
+    ap.add_argument("--op", choices=("verify", "draft", "commit", "early-exit", "tree"),
                     default="verify",
                     help="verify: the verify step (the metric); draft: the draft-side "
                          "sampler on the workload's draft rows at step 0; commit: the "
                          "commit step on the workload's verify outputs; early-exit: the "
-                         "early-exit verify on the same batch")
+                         "early-exit verify on the same batch; tree: greedy draft-tree "
+                         "verification on --tree")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -344,6 +350,100 @@ def bench_commit(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_tree(args):
+    """Greedy draft-tree verification: one spec_verify_tree_greedy call per step
+    over a seeded tree workload; every node's row is read once."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_scaled_amd import binding
+    from rejection_sampling_verify_scaled_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {args.tree}", file=sys.stderr, flush=True)
+    tb = W.make_tree_batch(args.tree)
+    d = binding.to_device_tree_batch(tb, dev)
+    B, V, n = tb.B, tb.V, int(tb.offsets[-1])
+    nodes = n - B  # draft nodes verified per step
+    alg = n * V * (2 if tb.dtype == W.DTYPE_BF16 else 4)
+    copies = args.copies or max(1, math.ceil(1.25e9 / alg))
+    targets = [d["target"]] + [d["target"].clone() for _ in range(copies - 1)]
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+    acc_nodes = torch.empty(n, dtype=torch.int32, device=dev)
+    lib = binding.load_library()
+    ws_n = binding.tree_workspace_bytes(B, V, tb.max_nodes)
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    vp = ctypes.c_void_p
+    dtype = binding.SV_BF16 if tb.dtype == W.DTYPE_BF16 else binding.SV_F32
+    argsets = [(vp(t.data_ptr()), dtype, B, V, tb.max_nodes, n, vp(d["offsets"].data_ptr()),
+                vp(d["parents"].data_ptr()), vp(d["tokens"].data_ptr()), vp(acc.data_ptr()),
+                vp(out.data_ptr()), vp(acc_nodes.data_ptr()), vp(ws.data_ptr()), ws_n,
+                vp(stream.cuda_stream)) for t in targets]
+
+    def call(i):
+        rc = lib.spec_verify_tree_greedy(*argsets[i % copies])
+        if rc != 0:
+            raise SystemExit(f"spec_verify_tree_greedy returned {rc}")
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    us = ms * 1e3
+    print(f"[bench] tv_verify {us:.2f} us per launch over the timed region", file=sys.stderr,
+          flush=True)
+    call(0)
+    torch.cuda.synchronize()
+    g_acc, g_out, g_nodes = acc.cpu().numpy(), out.cpu().numpy(), acc_nodes.cpu().numpy()
+    achieved = alg / (us * 1e-6) / 1e9
+    line = {
+        "metric": "verified draft-tree nodes/sec (greedy tree verification) + HBM GB/s",
+        "value": nodes / (us * 1e-6), "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if dtype == binding.SV_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": tb.label, "B": B, "V": V, "nodes": n, "max_nodes": tb.max_nodes,
+                   "input_copies_rotated": copies, "entry_point": "spec_verify_tree_greedy"},
+        "algorithmic_bytes_per_step": alg,
+        "kernel_us": {"tv_verify": us},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "tv_verify"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        olib = oracle.load()
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            res = oracle.tree_verify(tb.dtype, tb.target, tb.offsets, tb.parents, tb.tokens, V,
+                                     tb.max_nodes, lib=olib)
+            passes += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": nodes * passes / cpu_s, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over the full {B}-tree batch (single-threaded float64 C "
+                      f"oracle, {cpu_s:.1f} s)"}
+        line["parity_check"] = {
+            "requests": B,
+            "mismatches": int((g_acc != res["accept_len"]).sum()
+                              + (g_out != res["out_tokens"]).any()
+                              + (g_nodes != res["accept_nodes"]).any())}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -361,6 +461,9 @@ def main():
         return
     if args.op == "commit":
         bench_commit(args)
+        return
+    if args.op == "tree":
+        bench_tree(args)
         return
     from rejection_sampling_verify_scaled_amd import binding
     from rejection_sampling_verify_scaled_amd import workloads as W
