@@ -100,6 +100,8 @@ __device__ void tree_items(const TreeParams& p, int b, int32_t off, int items, i
 
 struct TreeShared {
   uint64_t slots[kFoldBlock];
+  float wave_v[kWaves][SV_TREE_MAX_NODES];  // each wave's share of a block's rows
+  int wave_i[kWaves][SV_TREE_MAX_NODES];
   float row_v[SV_TREE_MAX_NODES];  // folded row maximum
   int row_i[SV_TREE_MAX_NODES];    // lowest index attaining it
   int expired;
@@ -107,8 +109,10 @@ struct TreeShared {
 
 // Every node's row argmax, from the partials (which are zeroed once read).
 // Rows are taken R at a time with all their chunks, R * nc <= 2048; a row of
-// more than 2048 chunks is taken alone, 2048 chunks at a time (then R = 1 and
-// wave 0 owns it in every block).  Wave w owns rows w, w + 4, ... of a block.
+// more than 2048 chunks is taken alone, 2048 chunks at a time.  In a block,
+// lane l holds row l and wave w scans its quarter of the chunks from LDS (a
+// chain of independent LDS reads, not of cross-lane shuffles); wave 0 then
+// merges the four quarters in order into the running row results.
 __device__ void fold_tree_rows(const TreeParams& p, int b, int N, TreeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   if (tid < SV_TREE_MAX_NODES) {
@@ -162,21 +166,26 @@ __device__ void fold_tree_rows(const TreeParams& p, int b, int N, TreeShared& sh
         }
       }
       __syncthreads();
-      for (int rl = wave; rl < rr; rl += kWaves) {
+      const int cpw = (cc + kWaves - 1) / kWaves;
+      const int cb = wave * cpw, ce = min(cb + cpw, cc);
+      if (lane < rr) {
         float mv = -INFINITY;
         int mi = INT_MAX;
-        for (int c = lane; c < cc; c += 64) {
-          const uint64_t x = sh.slots[rl * cc + c];
+        const uint64_t* rs = sh.slots + lane * cc;
+        for (int c = cb; c < ce; ++c) {
+          const uint64_t x = rs[c];
           if (x != 0u) merge_argmax(mv, mi, slot_f(x), static_cast<int>(slot_w(x)));
         }
-        wave_merge_argmax(mv, mi);
-        if (lane == 0) {
-          float rv = sh.row_v[r0 + rl];
-          int ri = sh.row_i[r0 + rl];
-          merge_argmax(rv, ri, mv, mi);
-          sh.row_v[r0 + rl] = rv;
-          sh.row_i[r0 + rl] = ri;
-        }
+        sh.wave_v[wave][lane] = mv;
+        sh.wave_i[wave][lane] = mi;
+      }
+      __syncthreads();
+      if (wave == 0 && lane < rr) {
+        float rv = sh.row_v[r0 + lane];
+        int ri = sh.row_i[r0 + lane];
+        for (int w = 0; w < kWaves; ++w) merge_argmax(rv, ri, sh.wave_v[w][lane], sh.wave_i[w][lane]);
+        sh.row_v[r0 + lane] = rv;
+        sh.row_i[r0 + lane] = ri;
       }
     }
   }
