@@ -148,25 +148,82 @@ __device__ __forceinline__ void merge_argmax(float& v, int& i, float v2, int i2)
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+// Exact wave reductions (max, argmax, min) through DPP: within each 16-lane
+// row, lane i combines with lanes i-1, i-2, i-4, i-8 (row_shr), so lane 15 of
+// a row holds the row's result; row_bcast:15 then carries rows 0 and 2 into
+// rows 1 and 3, and row_bcast:31 carries row 1 into rows 2 and 3, leaving the
+// wave's result in lane 63, which readlane makes wave-uniform.  Each step is
+// a VALU operation on the register file, not a round trip through the LDS
+// permute path.  A lane whose DPP source does not exist keeps its own value
+// (combining a value with itself changes nothing, and keeps an all-NaN
+// maximum NaN).  Called with every lane of the wave active.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_float(float v) {
+  return __int_as_float(dpp_int<CTRL, ROW_MASK>(__float_as_int(v)));
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_float<kDppRowShr1>(x));
+  x = fmaxf(x, dpp_float<kDppRowShr2>(x));
+  x = fmaxf(x, dpp_float<kDppRowShr4>(x));
+  x = fmaxf(x, dpp_float<kDppRowShr8>(x));
+  x = fmaxf(x, dpp_float<kDppRowBcast15, 0xa>(x));
+  x = fmaxf(x, dpp_float<kDppRowBcast31, 0xc>(x));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+__device__ __forceinline__ int wave_min_int(int x) {
+  x = min(x, dpp_int<kDppRowShr1>(x));
+  x = min(x, dpp_int<kDppRowShr2>(x));
+  x = min(x, dpp_int<kDppRowShr4>(x));
+  x = min(x, dpp_int<kDppRowShr8>(x));
+  x = min(x, dpp_int<kDppRowBcast15, 0xa>(x));
+  x = min(x, dpp_int<kDppRowBcast31, 0xc>(x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ int wave_max_int(int x) {
+  x = max(x, dpp_int<kDppRowShr1>(x));
+  x = max(x, dpp_int<kDppRowShr2>(x));
+  x = max(x, dpp_int<kDppRowShr4>(x));
+  x = max(x, dpp_int<kDppRowShr8>(x));
+  x = max(x, dpp_int<kDppRowBcast15, 0xa>(x));
+  x = max(x, dpp_int<kDppRowBcast31, 0xc>(x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Float sums keep the butterfly (its rounding order is the one the results
+// were validated with).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
 
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ void dpp_merge_argmax(float& v, int& i) {
+  const float v2 = dpp_float<CTRL, ROW_MASK>(v);
+  const int i2 = dpp_int<CTRL, ROW_MASK>(i);
+  merge_argmax(v, i, v2, i2);
+}
+
+// Every lane ends with the wave's (value, lowest index) winner.
 __device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, 64);
-    const int i2 = __shfl_xor(i, o, 64);
-    merge_argmax(v, i, v2, i2);
-  }
+  dpp_merge_argmax<kDppRowShr1>(v, i);
+  dpp_merge_argmax<kDppRowShr2>(v, i);
+  dpp_merge_argmax<kDppRowShr4>(v, i);
+  dpp_merge_argmax<kDppRowShr8>(v, i);
+  dpp_merge_argmax<kDppRowBcast15, 0xa>(v, i);
+  dpp_merge_argmax<kDppRowBcast31, 0xc>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // All threads end with the workgroup's (key, idx) winner.
@@ -372,8 +429,7 @@ __device__ __forceinline__ uint64_t item_argmax(const uint4* buf, int64_t e0) {
       if (xs[k] == mx) ks = k;
     idx = static_cast<int>(e0) + (us * 64 + lane) * EPV + ks;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) idx = min(idx, __shfl_xor(idx, o, 64));
+  idx = wave_min_int(idx);
   return pack_slot(mx, static_cast<uint32_t>(idx));
 }
 

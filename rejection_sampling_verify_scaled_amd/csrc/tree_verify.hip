@@ -241,8 +241,7 @@ __device__ void tree_finish(const TreeParams& p, int b, int32_t off, int N) {
   }
   // deepest accepted node, lowest index among equals: maximise (depth, 63 - i)
   int key = (live && acc) ? ((dep + 1) << 8) | (63 - i) : 0;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) key = max(key, __shfl_xor(key, o, 64));
+  key = wave_max_int(key);
   const int c = 63 - (key & 255);
   const int d = (key >> 8) - 1;
   // mark the path root .. c (d + 1 nodes)
