@@ -25,7 +25,8 @@ commit step (spec_commit_tokens) on the workload's verify outputs; --op
 early-exit times spec_verify_sample_early_exit on the same batch, whose
 roofline counts only the rows a request needs up to its first rejection; --op
 tree times greedy draft-tree verification (spec_verify_tree_greedy) on a
-seeded tree workload (--tree).
+seeded tree workload (--tree); --op greedy times the all-greedy entry point
+(spec_verify_greedy) on the workload with every request greedy.
 """
 from __future__ import annotations
 
@@ -70,13 +71,14 @@ def parse():
     ap.add_argument("--tree", default="tree-eagle",
                     choices=("tree-small", "tree-eagle", "tree-ragged"),
                     help="tree workload for --op tree")
-    ap.add_argument("--op", choices=("verify", "draft", "commit", "early-exit", "tree"),
+    ap.add_argument("--op", choices=("verify", "draft", "commit", "early-exit", "tree", "greedy"),
                     default="verify",
                     help="verify: the verify step (the metric); draft: the draft-side "
                          "sampler on the workload's draft rows at step 0; commit: the "
                          "commit step on the workload's verify outputs; early-exit: the "
                          "early-exit verify on the same batch; tree: greedy draft-tree "
-                         "verification on --tree")
+                         "verification on --tree; greedy: spec_verify_greedy on the "
+                         "workload with every request greedy")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -472,7 +474,8 @@ def main():
     hip = Hip()
     dev = torch.device("cuda:0")
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
-    batch = W.make_batch(args.workload, 0)
+    greedy = args.op == "greedy"
+    batch = W.make_batch(args.workload, 0, temperature_override=0.0 if greedy else None)
     d = binding.to_device_batch(batch, dev)
     B, V, K = batch.B, batch.V, batch.max_k
     n_d = batch.n_draft_rows
@@ -496,13 +499,20 @@ def main():
     vp = ctypes.c_void_p
     argsets = []
     for c in range(copies):
+        if greedy:  # the all-greedy entry point: no draft logits, temperatures or seed
+            argsets.append((vp(targets[c].data_ptr()), dtype, B, V, K, n_d,
+                            vp(d["offsets"].data_ptr()), vp(d["tokens"].data_ptr()),
+                            vp(acc.data_ptr()), vp(out.data_ptr()), vp(ws.data_ptr()), ws_n, sh))
+            continue
         argsets.append((vp(targets[c].data_ptr()), vp(drafts[c].data_ptr()), dtype, B, V, K, n_d,
                         vp(d["offsets"].data_ptr()), vp(d["tokens"].data_ptr()),
                         vp(d["temperature"].data_ptr()), ctypes.c_uint64(batch.seed),
                         vp(acc.data_ptr()), vp(out.data_ptr()), vp(pa.data_ptr()),
                         vp(qa.data_ptr()), vp(ws.data_ptr()), ws_n, sh))
-    call = lib.spec_verify_sample_early_exit if ee else lib.spec_verify_sample
-    name = "spec_verify_sample_early_exit" if ee else "spec_verify_sample"
+    call = (lib.spec_verify_sample_early_exit if ee else
+            lib.spec_verify_greedy if greedy else lib.spec_verify_sample)
+    name = ("spec_verify_sample_early_exit" if ee else
+            "spec_verify_greedy" if greedy else "spec_verify_sample")
     torch.cuda.synchronize()
     print(f"[bench] B={B} K={K} V={V} copies={copies} ({copies * per_copy / 1e9:.2f} GB); "
           f"warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -544,12 +554,13 @@ def main():
     # ---- cross-check: events the library records around each single launch
     # (each pair of event records adds its own small overhead to the figure)
     k_us = ms_per_step * 1e3
-    if ee:
+    if ee or greedy:
         # the timed region is `steps` back-to-back calls of two launches each:
         # sv_verify_ee, then the small kernel that clears its decision records
         ev_us = None
-        print(f"[bench] sv_verify_ee + ee_clear_records {k_us:.2f} us per call over the "
-              "timed region", file=sys.stderr, flush=True)
+        what = "sv_verify_ee + ee_clear_records" if ee else "sv_verify (all greedy)"
+        print(f"[bench] {what} {k_us:.2f} us per call over the timed region", file=sys.stderr,
+              flush=True)
     else:
         n_t = min(args.steps, 200)
         evs = [(hip.event(), hip.event()) for _ in range(n_t)]
@@ -614,12 +625,12 @@ def main():
         "hbm_frac_step": alg / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg,
         "bytes_per_verified_position": alg / positions,
-        "kernel_us": ({"sv_verify_ee_and_clear": k_us} if ee else
-                      {"sv_verify": k_us, "sv_verify_single_launch_events": ev_us}),
+        "kernel_us": ({"sv_verify_ee_and_clear": k_us} if ee else {"sv_verify": k_us} if greedy
+                      else {"sv_verify": k_us, "sv_verify_single_launch_events": ev_us}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": (traffic_record(args.workload, "sv_verify_ee", EE_KERNEL_SOURCES)
-                                 if ee else traffic_record(args.workload)),
+                                 if ee else None if greedy else traffic_record(args.workload)),
                      "kernel": "sv_verify_ee" if ee else "sv_verify"},
         "copy_gbs": {"value": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                      "what": "1 GiB device-to-device copy on the same stream, read + written bytes"},
