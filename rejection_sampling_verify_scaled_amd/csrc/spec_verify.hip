@@ -72,8 +72,8 @@ constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
 #ifndef SV_FOLD_SLEEP
 #define SV_FOLD_SLEEP 1
 #endif
-// Workgroups of this kernel one CU holds at once (96 VGPRs per lane: five
-// waves per SIMD, so five 4-wave workgroups per CU).
+// Workgroups of this kernel one CU holds at once (at most 96 VGPRs per lane:
+// five waves per SIMD, so five 4-wave workgroups per CU).
 constexpr int kWorkgroupsPerCu = 5;
 
 // ------------------------------------------------------------------ parameters
@@ -600,7 +600,7 @@ __device__ __forceinline__ void race_pair(const Params& p, int b, int c, const v
 
 template <bool BF16, bool VEC>
 __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceRow& rr,
-                               bool bad, bool fold_expired);
+                               bool bad, bool fold_expired, int32_t x);
 
 // Race of sampled request b over the chunks of group cg.  x holds draft token
 // t = threadIdx.x of request b for t < K (loaded at the start of the workgroup).
@@ -686,14 +686,15 @@ __device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t 
     slot_store(p.race + static_cast<int64_t>(b) * p.ngr + cg,
                pack_slot(key, expired ? kExpiredIdx : static_cast<uint32_t>(idx)));
   // the request's last race workgroup finishes it
-  if (cg == p.ngr - 1) finish_sampled<BF16, VEC>(p, b, r, rr, bad, expired);
+  if (cg == p.ngr - 1) finish_sampled<BF16, VEC>(p, b, r, rr, bad, expired, x);
 }
 
 // The last race workgroup of request b: folds the workgroup winners, writes
-// the outputs and clears the request's slots.
+// the outputs and clears the request's slots.  x is draft token t = threadIdx.x
+// (t < K), loaded when the workgroup started, so the outputs need no load.
 template <bool BF16, bool VEC>
 __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceRow& rr,
-                               bool bad, bool fold_expired) {
+                               bool bad, bool fold_expired, int32_t x) {
   __shared__ float sh_key[kWaves];
   __shared__ int sh_idx[kWaves];
   __shared__ int sh_expired;
@@ -741,10 +742,7 @@ __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceR
     block_argmax(key, idx, sh_key, sh_idx);
   }
   const int n = rr.n;
-  if (tid <= r.K) {
-    const int32_t xt = (tid < n) ? p.tokens[r.off0 + tid] : 0;
-    p.out_tokens[trow0 + tid] = (tid < n) ? xt : (tid == n ? idx : -1);
-  }
+  if (tid <= r.K) p.out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? idx : -1);
   if (tid == 0) p.accept_len[b] = n;
 }
 
