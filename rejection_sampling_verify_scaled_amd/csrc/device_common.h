@@ -214,6 +214,30 @@ __device__ __forceinline__ void dpp_merge_argmax(float& v, int& i) {
   merge_argmax(v, i, v2, i2);
 }
 
+// (max, sum) pairs through the same DPP steps.  Merging a pair with itself
+// would double its sum, so a lane without a DPP source takes the empty pair
+// (-inf, 0) instead; the sums are added in the DPP tree's order.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ void dpp_merge_stats(float& m, float& s, float cf) {
+  const float m2 = __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(-INFINITY), __float_as_int(m), CTRL, ROW_MASK, 0xf, false));
+  const float s2 = __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(0.f), __float_as_int(s), CTRL, ROW_MASK, 0xf, false));
+  merge_stats(m, s, m2, s2, cf);
+}
+
+// Every lane ends with the wave's merged (max, sum).
+__device__ __forceinline__ void wave_merge_stats(float& m, float& s, float cf) {
+  dpp_merge_stats<kDppRowShr1>(m, s, cf);
+  dpp_merge_stats<kDppRowShr2>(m, s, cf);
+  dpp_merge_stats<kDppRowShr4>(m, s, cf);
+  dpp_merge_stats<kDppRowShr8>(m, s, cf);
+  dpp_merge_stats<kDppRowBcast15, 0xa>(m, s, cf);
+  dpp_merge_stats<kDppRowBcast31, 0xc>(m, s, cf);
+  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+  s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
+}
+
 // Every lane ends with the wave's (value, lowest index) winner.
 __device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
   dpp_merge_argmax<kDppRowShr1>(v, i);

@@ -158,18 +158,12 @@ __device__ void draft_finish(const DraftParams& p, int b, float T) {
     if (!greedy) slot_store(slots[1], 0u);
   }
   if (expired) atomicOr(&sh_bad, 1);
-  // fixed-order tree over the workgroup
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64);
-    const float k2 = __shfl_xor(key, o, 64);
-    const int i2 = __shfl_xor(idx, o, 64);
-    if (greedy) {
-      merge_argmax(M, idx, m2, i2);
-    } else {
-      merge_stats(M, S, m2, s2, cf);
-      merge_argmax(key, idx, k2, i2);
-    }
+  // fixed-order DPP tree over each wave
+  if (greedy) {
+    wave_merge_argmax(M, idx);
+  } else {
+    wave_merge_stats(M, S, cf);
+    wave_merge_argmax(key, idx);
   }
   if (lane == 0) {
     sh_m[wave] = M;

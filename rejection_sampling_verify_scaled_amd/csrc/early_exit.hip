@@ -200,8 +200,8 @@ __device__ void ee_stats(const EeParams& p, int b, int s, int j, const EeReq& r)
 }
 
 // The stage's last workgroup: fold the stage's partials (wave w < nrows folds
-// row w: lane l takes chunks l, l + 64, ... in order, then a fixed shuffle
-// tree), then decide.
+// row w: lane l takes chunks l, l + 64, ... in order, then a fixed DPP tree),
+// then decide.
 template <bool BF16>
 __device__ void ee_decide(const EeParams& p, int b, int s, const EeReq& r) {
   __shared__ float sh_m[kStageRows], sh_s[kStageRows];
@@ -228,15 +228,10 @@ __device__ void ee_decide(const EeParams& p, int b, int s, const EeReq& r) {
       else
         merge_stats(M, S, slot_f(v), __uint_as_float(slot_w(v)), cf);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64);
-      const int i2 = __shfl_xor(I, o, 64);
-      if (r.greedy)
-        merge_argmax(M, I, m2, i2);
-      else
-        merge_stats(M, S, m2, s2, cf);
-    }
+    if (r.greedy)
+      wave_merge_argmax(M, I);
+    else
+      wave_merge_stats(M, S, cf);
     if (expired) atomicOr(&sh_bad, 2);
     if (lane == 0) {
       const bool finite = M > -INFINITY && M < INFINITY && (r.greedy || S < INFINITY);
