@@ -82,7 +82,7 @@ def test_draft_large_batch_f32():
 
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
-@pytest.mark.parametrize("V", [1, 3, 37, 1000, 4099, 40001, 70000])
+@pytest.mark.parametrize("V", [1, 3, 37, 1000, 4099, 40001, 70000, 262144, 300007])
 def test_draft_vocab_sizes(dtype, V):
     """Any V: vector and scalar paths, one to many chunks, ragged last chunk."""
     rng = np.random.default_rng(V * 5 + dtype)

@@ -80,11 +80,12 @@ def test_early_exit_large_workloads(cfg):
 
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
-@pytest.mark.parametrize("V", [1, 37, 4099, 70000])
+@pytest.mark.parametrize("V", [1, 37, 4099, 70000, 262144, 300007])
 def test_early_exit_ragged(dtype, V):
-    """Ragged K (including K = 0), mixed temperatures, any V."""
+    """Ragged K (including K = 0), mixed temperatures, any V (up to 256k-class
+    vocabularies, more than 64 row-chunks per row)."""
     rng = np.random.default_rng(V * 13 + dtype)
-    B = 40
+    B = 40 if V < 200000 else 12
     ks = [int(x) for x in rng.integers(0, 9, size=B)]
     temps = rng.choice([0.0, 0.5, 1.0, 1.7], size=B)
     bt = W.make_custom_batch(rng, dtype, V, ks, temps, seed=V + 3, max_k=8)

@@ -118,6 +118,23 @@ def test_uniform_k_vocab(dtype, V, K):
     compare(b, gg, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
 
 
+@pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
+@pytest.mark.parametrize("V", [262144, 300007])
+def test_large_vocab(dtype, V):
+    """256k-class vocabularies: more than 64 row-chunks per row, so the fold
+    takes several blocks of partials (and a ragged tail at 300007)."""
+    rng = np.random.default_rng(V * 13 + dtype)
+    B = 12
+    ks = [int(x) for x in rng.integers(0, 9, size=B)]
+    temps = rng.choice([0.0, 0.7, 1.0], size=B)
+    b = W.make_custom_batch(rng, dtype, V, ks, temps, seed=V + 5, max_k=8)
+    say(f"large V={V} dtype={dtype} ks={ks}")
+    gpu = run_gpu(b, "sample")
+    compare(b, gpu, oracle.verify_batch(b))
+    gg = run_gpu(b, "greedy")
+    compare(b, gg, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
+
+
 def test_plain_sampling_k0():
     """max_k = 0: every request is plain sampling from softmax(z / T)."""
     rng = np.random.default_rng(3)

@@ -150,11 +150,12 @@ def random_trees(rng, B, V, max_nodes, kinds, min_nodes=1):
 
 @pytest.mark.parametrize("V,dtype", [(1, W.DTYPE_F32), (37, W.DTYPE_BF16), (4099, W.DTYPE_F32),
                                      (4099, W.DTYPE_BF16), (70000, W.DTYPE_BF16),
-                                     (70000, W.DTYPE_F32)])
+                                     (70000, W.DTYPE_F32), (262144, W.DTYPE_F32),
+                                     (300007, W.DTYPE_BF16)])
 def test_tree_random_shapes(V, dtype):
     say("tree random shapes", V, W.DTYPE_NAMES[dtype])
     rng = np.random.default_rng(V * 7 + dtype)
-    B = 24 if V < 50000 else 12
+    B = 24 if V < 50000 else (12 if V < 200000 else 4)
     trees, z = random_trees(rng, B, V, 64, ["chain", "star", "random", "full"])
     offs, parents, tokens = pack_trees(trees)
     target = W.to_storage(z, dtype)
