@@ -135,6 +135,19 @@ def test_large_vocab(dtype, V):
     compare(b, gg, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
 
 
+@pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
+def test_temperature_range(dtype):
+    """Temperatures from 0.25 to 10 (1.5 is the lesson's exercise value): the
+    1e-5 bound on p and q holds while |z| / T stays below about 100."""
+    rng = np.random.default_rng(77 + dtype)
+    B, V = 48, 20011
+    temps = np.tile([0.25, 1.5, 3.0, 10.0], B // 4)
+    ks = [int(x) for x in rng.integers(1, 9, size=B)]
+    b = W.make_custom_batch(rng, dtype, V, ks, temps, seed=501, max_k=8)
+    say(f"temperature range dtype={dtype}")
+    compare(b, run_gpu(b, "sample"), oracle.verify_batch(b))
+
+
 def test_plain_sampling_k0():
     """max_k = 0: every request is plain sampling from softmax(z / T)."""
     rng = np.random.default_rng(3)
