@@ -20,6 +20,15 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), f"{n} declared in include/spec_verify.h but not exported"
 
 
+def test_every_declared_function_has_a_signature(lib):
+    """The binding declares argument and result types for every entry point the
+    header declares (ctypes would otherwise pass 64-bit sizes and pointers as int)."""
+    for n in binding.header_functions():
+        f = getattr(lib, n)
+        assert f.argtypes is not None, f"{n} has no argtypes in the binding"
+        assert f.restype is not None, f"{n} has no restype in the binding"
+
+
 def test_workspace_bytes(lib):
     assert lib.spec_verify_workspace_bytes(64, 128256, 4) > 0
     assert lib.spec_verify_workspace_bytes(64, 128256, 4) % 256 == 0
