@@ -890,10 +890,14 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   if (prm.flat) {
     prm.m = 1;
     prm.ng = static_cast<int32_t>(ceil_div(static_cast<int64_t>(rows) * prm.nc, kGroupItems));
-    // two chunks per race workgroup, or more when a request has fewer
-    // statistics workgroups than that leaves race workgroups
+    // race chunks per race workgroup: at least two, and enough that a
+    // request has at most half as many race workgroups as statistics
+    // workgroups.  Few rows per request (MTP, K = 1) then get wide races:
+    // fewer workgroups folding the same partials, and fewer empty ones for
+    // the greedy requests (B=512 K=1: 11 race workgroups per request -> 6,
+    // 82.0 -> 77.8 us; B=64 K=4 and B=256 K=8 keep two chunks)
     prm.mr = static_cast<int32_t>(
-        std::min<int64_t>(prm.nc, std::max<int64_t>(2, ceil_div(prm.nc, prm.ng))));
+        std::min<int64_t>(prm.nc, std::max<int64_t>(2, ceil_div(2 * prm.nc, prm.ng))));
   } else {
     prm.m = chunks_per_workgroup(rows, prm.nc);
     prm.ng = static_cast<int32_t>(ceil_div(prm.nc, prm.m));
