@@ -308,12 +308,13 @@ __device__ inline uint64_t slot_wait(const uint64_t* p) {
 // ------------------------------------------------------------------ statistics
 
 // One wave's share of a row-chunk: lane elements e0 + (u * 64 + lane) * EPV +
-// [0, EPV), u = 0..kItemVecs-1.  The vector path loads every vector from an
+// [0, EPV), u = 0..NV-1 (NV = kItemVecs for a full row-chunk; a shorter
+// chunk keeps the same layout with fewer vectors).  The vector path loads every vector from an
 // in-row address (indices clamped to the row's last vector) on one code path,
 // so the loads of several row-chunks stay in flight together; mask_tail then
 // replaces the vectors past the row end with -inf.  The scalar path reads -inf
 // past V itself.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int NV = kItemVecs>
 __device__ __forceinline__ void load_item(const void* base, int64_t row, int V, int64_t e0,
                                           uint4* out) {
   constexpr int EPV = elems_per_vec(BF16);
@@ -324,12 +325,12 @@ __device__ __forceinline__ void load_item(const void* base, int64_t row, int V, 
     const int last = V / EPV - 1;
     const int i0 = static_cast<int>(e0 / EPV) + lane;
 #pragma unroll
-    for (int u = 0; u < kItemVecs; ++u) out[u] = rowv[min(i0 + u * 64, last)];
+    for (int u = 0; u < NV; ++u) out[u] = rowv[min(i0 + u * 64, last)];
   } else {
     const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
     const int64_t rb = row * V;
 #pragma unroll
-    for (int u = 0; u < kItemVecs; ++u) {
+    for (int u = 0; u < NV; ++u) {
       const int64_t e = e0 + static_cast<int64_t>(u * 64 + lane) * EPV;
       uint32_t w[4];
 #pragma unroll
@@ -350,14 +351,14 @@ __device__ __forceinline__ void load_item(const void* base, int64_t row, int V, 
 }
 
 // Vector path, row-chunk reaching past the row end: vectors past it become -inf.
-template <bool BF16>
+template <bool BF16, int NV = kItemVecs>
 __device__ __forceinline__ void mask_tail(uint4* buf, int V, int64_t e0) {
   constexpr int EPV = elems_per_vec(BF16);
   const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
   const int last = V / EPV - 1;
   const int i0 = static_cast<int>(e0 / EPV) + (threadIdx.x & 63);
 #pragma unroll
-  for (int u = 0; u < kItemVecs; ++u)
+  for (int u = 0; u < NV; ++u)
     if (i0 + u * 64 > last) buf[u] = make_uint4(ninf, ninf, ninf, ninf);
 }
 
@@ -417,13 +418,13 @@ __device__ __forceinline__ uint64_t item_stats(const uint4* buf, float cf) {
 // The wave maximum from per-vector maxima; then each lane takes the first of
 // its vectors holding it (a backward scan keeps the last match, the lowest)
 // and the first element of that vector equal to it.  NaN never matches.
-template <bool BF16>
+template <bool BF16, int NV = kItemVecs>
 __device__ __forceinline__ uint64_t item_argmax(const uint4* buf, int64_t e0) {
   constexpr int EPV = elems_per_vec(BF16);
   const int lane = threadIdx.x & 63;
-  float vm[kItemVecs];
+  float vm[NV];
 #pragma unroll
-  for (int u = 0; u < kItemVecs; ++u) {
+  for (int u = 0; u < NV; ++u) {
     float xs[EPV];
     unpack<BF16>(buf[u], xs);
     vm[u] = xs[0];
@@ -432,12 +433,12 @@ __device__ __forceinline__ uint64_t item_argmax(const uint4* buf, int64_t e0) {
   }
   float mx = vm[0];
 #pragma unroll
-  for (int u = 1; u < kItemVecs; ++u) mx = fmaxf(mx, vm[u]);
+  for (int u = 1; u < NV; ++u) mx = fmaxf(mx, vm[u]);
   mx = wave_max(mx);
   int us = -1;
   uint4 sel = buf[0];
 #pragma unroll
-  for (int u = kItemVecs - 1; u >= 0; --u) {
+  for (int u = NV - 1; u >= 0; --u) {
     if (vm[u] == mx) {
       us = u;
       sel = buf[u];

@@ -48,93 +48,6 @@ __host__ __device__ constexpr int draft_chunk_tokens(bool bf16, int nv) {
   return 64 * nv * elems_per_vec(bf16);
 }
 
-// A chunk held by a wave: lane elements e0 + (u * 64 + lane) * EPV + [0, EPV),
-// u = 0..NV-1 (the row-chunk layout of the verify kernel; NV = kItemVecs is
-// its full length).  The vector path clamps every load into the row and masks
-// the vectors past its end with -inf afterwards; the scalar path reads -inf
-// past V.
-template <bool BF16, bool VEC, int NV>
-__device__ __forceinline__ void draft_load(const void* base, int64_t row, int V, int64_t e0,
-                                           uint4* out) {
-  constexpr int EPV = elems_per_vec(BF16);
-  const int lane = threadIdx.x & 63;
-  if constexpr (VEC) {
-    const uint4* rowv = reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
-                                                       row * V * (BF16 ? 2 : 4));
-    const int last = V / EPV - 1;
-    const int i0 = static_cast<int>(e0 / EPV) + lane;
-#pragma unroll
-    for (int u = 0; u < NV; ++u) out[u] = rowv[min(i0 + u * 64, last)];
-  } else {
-    const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
-    const int64_t rb = row * V;
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int64_t e = e0 + static_cast<int64_t>(u * 64 + lane) * EPV;
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (BF16) {
-          const uint16_t* b16 = static_cast<const uint16_t*>(base);
-          const uint32_t lo = (e + 2 * k < V) ? b16[rb + e + 2 * k] : 0xff80u;
-          const uint32_t hi = (e + 2 * k + 1 < V) ? b16[rb + e + 2 * k + 1] : 0xff80u;
-          w[k] = lo | (hi << 16);
-        } else {
-          w[k] = (e + k < V) ? __float_as_uint(static_cast<const float*>(base)[rb + e + k])
-                             : ninf;
-        }
-      }
-      out[u] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
-}
-
-template <bool BF16, int NV>
-__device__ __forceinline__ void draft_mask_tail(uint4* buf, int V, int64_t e0) {
-  constexpr int EPV = elems_per_vec(BF16);
-  const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
-  const int last = V / EPV - 1;
-  const int i0 = static_cast<int>(e0 / EPV) + (threadIdx.x & 63);
-#pragma unroll
-  for (int u = 0; u < NV; ++u)
-    if (i0 + u * 64 > last) buf[u] = make_uint4(ninf, ninf, ninf, ninf);
-}
-
-// A greedy chunk: (max, lowest index attaining it); NaN never matches.
-template <bool BF16, int NV>
-__device__ __forceinline__ uint64_t draft_argmax(const uint4* buf, int64_t e0) {
-  constexpr int EPV = elems_per_vec(BF16);
-  const int lane = threadIdx.x & 63;
-  float vm[NV];
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    float xs[EPV];
-    unpack<BF16>(buf[u], xs);
-    vm[u] = xs[0];
-#pragma unroll
-    for (int k = 1; k < EPV; ++k) vm[u] = fmaxf(vm[u], xs[k]);
-  }
-  float mx = vm[0];
-#pragma unroll
-  for (int u = 1; u < NV; ++u) mx = fmaxf(mx, vm[u]);
-  mx = wave_max(mx);
-  int idx = INT_MAX;
-#pragma unroll
-  for (int u = NV - 1; u >= 0; --u) {  // backward: the lowest match stays
-    if (vm[u] == mx) {
-      float xs[EPV];
-      unpack<BF16>(buf[u], xs);
-      int ks = 0;
-#pragma unroll
-      for (int k = EPV - 1; k >= 0; --k)
-        if (xs[k] == mx) ks = k;
-      idx = static_cast<int>(e0) + (u * 64 + lane) * EPV + ks;
-    }
-  }
-  idx = wave_min_int(idx);
-  return pack_slot(mx, static_cast<uint32_t>(idx));
-}
-
 struct DraftParams {
   const void* logits;        // [B][V]
   const float* temperature;  // [B]
@@ -155,7 +68,7 @@ __device__ __forceinline__ uint64_t* race_slot(const DraftParams& p, int b, int 
 }
 
 // Statistics and race of one sampled chunk held by a wave (lane elements as
-// in draft_load).  Returns the statistics slot (max, sum relative to fl(max c))
+// in load_item).  Returns the statistics slot (max, sum relative to fl(max c))
 // and sets the race slot (log2-domain key, index).
 template <bool BF16, int NV>
 __device__ __forceinline__ uint64_t chunk_race(const uint4* buf, int64_t e0, float cf, uint32_t b,
@@ -314,11 +227,11 @@ __global__ __launch_bounds__(kThreads) void sd_sample(DraftParams p) {
   if (c < p.nc) {
     uint4 buf[NV];
     const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
-    draft_load<BF16, VEC, NV>(p.logits, b, p.V, e0, buf);
-    if (VEC && e0 + CHUNK > p.V) draft_mask_tail<BF16, NV>(buf, p.V, e0);
+    load_item<BF16, VEC, NV>(p.logits, b, p.V, e0, buf);
+    if (VEC && e0 + CHUNK > p.V) mask_tail<BF16, NV>(buf, p.V, e0);
     const int lane = threadIdx.x & 63;
     if (T == 0.f) {
-      const uint64_t v = draft_argmax<BF16, NV>(buf, e0);
+      const uint64_t v = item_argmax<BF16, NV>(buf, e0);
       if (lane == 0) slot_store(stat_slot(p, b, c), v);
     } else {
       uint64_t race;
