@@ -40,8 +40,8 @@ namespace {
 
 constexpr uint32_t kDraftTag = 2u;  // Philox stream tag of the draft sampler
 // Half chunks below this many full-chunk waves (1024 SIMDs x 4): 64 bf16 rows
-// of V = 128256 10.58 -> 9.90 us, while 256 fp32 rows keep full chunks
-// (half: 35.4 -> 40.4 us, twice the partials to fold).
+// of V = 128256 go from 10.6 to 10.0 us, while 256 fp32 rows keep full chunks
+// (half chunks there: 35.4 -> 40.4 us, twice the partials to fold).
 constexpr int64_t kHalfChunksBelow = 4096;
 
 __host__ __device__ constexpr int draft_chunk_tokens(bool bf16, int nv) {
