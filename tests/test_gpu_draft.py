@@ -93,6 +93,19 @@ def test_draft_vocab_sizes(dtype, V):
     check(rows, dtype, temps, 1234 + V, 5)
 
 
+@pytest.mark.parametrize("B", [127, 128])
+def test_draft_chunk_length_switch(B):
+    """Either side of the batch size where the sampler moves from 4 KiB to 8 KiB
+    chunks per wave (bf16, V=128256: 127 rows x 32 full chunks stay below 4096
+    waves, 128 rows do not).  The same rows give the oracle's tokens either way."""
+    rng = np.random.default_rng(31)
+    V = 128256
+    rows = W.to_storage(rng.normal(0, 3.0, size=(128, V)), W.DTYPE_BF16)[:B]
+    temps = np.where(np.arange(128) % 3 == 0, 0.0, 0.8).astype(np.float32)[:B]
+    say(f"draft chunk switch B={B}")
+    check(rows, W.DTYPE_BF16, temps, 4321, 2)
+
+
 def test_draft_scalar_path_misaligned():
     """A base pointer off 16-byte alignment takes the scalar-load path."""
     import torch
