@@ -20,6 +20,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -109,6 +110,19 @@ def race_exponential(seed: int, b: int, pos: int, v: int, lib=None) -> float:
     return (lib or load()).oracle_race_exponential(seed, b, pos, v)
 
 
+def default_threads() -> int:
+    """Worker threads for request-parallel oracle runs: the cores this process may
+    use, at most 16 (``ORACLE_THREADS`` overrides)."""
+    env = os.environ.get("ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -124,12 +138,17 @@ def _as_logits(dtype: int, a):
 
 
 def verify(dtype: int, target, draft, offsets, tokens, temperature, seed: int, V: int,
-           max_k: int, reqs=None, lib=None, n_draft_rows=None) -> dict:
+           max_k: int, reqs=None, lib=None, n_draft_rows=None, threads=None) -> dict:
     """Run the oracle over a packed batch (see the workload module for layout).
 
     Returns numpy arrays: accept_len [B], out_tokens [sum(K_b)+B], p_at / q_at
     [sum(K_b)] (float64), flags [B], race_best / race_gap [B].  With ``reqs``
     only the listed requests are evaluated (others keep accept_len == -2).
+
+    Requests are independent, so ``threads`` > 1 (default: ``default_threads()``)
+    splits them over worker threads, each calling the same C entry point on its
+    own requests and writing their disjoint entries of the shared outputs (a
+    ctypes call releases the GIL).  The result does not depend on ``threads``.
     """
     lib = lib or load()
     if dtype == F32:
@@ -160,23 +179,36 @@ def verify(dtype: int, target, draft, offsets, tokens, temperature, seed: int, V
     r = None
     if reqs is not None:
         r = np.ascontiguousarray(reqs, dtype=np.int32)
-    rc = lib.oracle_spec_verify(dtype, _ptr(target), _ptr(draft), B, V, max_k, n_d,
-                                _ptr(offsets), _ptr(tokens), _ptr(temperature),
-                                ctypes.c_uint64(seed), _ptr(r), 0 if r is None else r.shape[0],
-                                _ptr(acc), _ptr(out), _ptr(p_at), _ptr(q_at), _ptr(flags),
-                                _ptr(best), _ptr(gap))
-    if rc != 0:
-        raise ValueError(f"oracle_spec_verify rejected its arguments (rc={rc})")
+    threads = default_threads() if threads is None else max(1, int(threads))
+
+    def run(rr):
+        return lib.oracle_spec_verify(dtype, _ptr(target), _ptr(draft), B, V, max_k, n_d,
+                                      _ptr(offsets), _ptr(tokens), _ptr(temperature),
+                                      ctypes.c_uint64(seed), _ptr(rr),
+                                      0 if rr is None else rr.shape[0], _ptr(acc), _ptr(out),
+                                      _ptr(p_at), _ptr(q_at), _ptr(flags), _ptr(best), _ptr(gap))
+
+    n_req = B if r is None else r.shape[0]
+    if threads == 1 or n_req < 2:
+        rcs = [run(r)]
+    else:
+        every = np.arange(B, dtype=np.int32) if r is None else r
+        # interleaved shards balance ragged batches (neighbouring requests differ in K_b)
+        shards = [np.ascontiguousarray(every[i::threads]) for i in range(min(threads, n_req))]
+        with ThreadPoolExecutor(len(shards)) as pool:
+            rcs = list(pool.map(run, shards))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError(f"oracle_spec_verify rejected its arguments (rc={rcs})")
     return dict(accept_len=acc, out_tokens=out, p_at=p_at[:n_d], q_at=q_at[:n_d],
                 flags=flags, race_best=best, race_gap=gap)
 
 
-def verify_batch(batch, reqs=None, greedy_only: bool = False, lib=None) -> dict:
+def verify_batch(batch, reqs=None, greedy_only: bool = False, lib=None, threads=None) -> dict:
     """Oracle over a workload ``Batch``; ``greedy_only`` forces T=0 everywhere."""
     temp = np.zeros_like(batch.temperature) if greedy_only else batch.temperature
     return verify(batch.dtype, batch.target, None if greedy_only else batch.draft,
                   batch.offsets, batch.tokens, temp, batch.seed, batch.V, batch.max_k,
-                  reqs=reqs, lib=lib, n_draft_rows=batch.n_draft_rows)
+                  reqs=reqs, lib=lib, n_draft_rows=batch.n_draft_rows, threads=threads)
 
 
 def draft_exponential(seed: int, b: int, step: int, v: int, lib=None) -> float:

@@ -28,7 +28,10 @@
  *   - sampling is an exponential race: winner = argmax_v (ln w_v - ln E_v)
  *     with E_v = -ln U_v, U_v from Philox4x32-10 keyed by the seed and
  *     counter (v >> 2, position, request, 0), word v & 3; the accept uniform
- *     r_t is word 0 of counter (0, t, request, 1);
+ *     r_t is word 0 of counter (0, t, request, 1).  w_v is a probability:
+ *     (p - q)+ after a rejection, p itself for the bonus (z_v / T - lse), so
+ *     the race keys and the near-tie window below do not move when a
+ *     constant is added to a row's logits;
  *   - U(x) = (2*(x >> 9) + 1) * 2^-24, an exact value in (0, 1).
  *
  * It also holds the draft-side sampler that precedes verification
@@ -55,7 +58,7 @@
 
 /* flags written per request */
 #define OR_FLAG_ACCEPT_NEAR_TIE 1u  /* some evaluated |r*q - p| < 1e-6 * max(p, r*q) */
-#define OR_FLAG_RACE_NEAR_TIE 2u    /* best - second < 1e-6 * max(1, |best|) */
+#define OR_FLAG_RACE_NEAR_TIE 2u    /* best - second < 1e-6 * max(1, |best|), keys ln w - ln E */
 #define OR_FLAG_RESIDUAL_EMPTY 4u   /* no token had p > q; raced on p instead */
 
 /* ---------------------------------------------------------------- Philox */
@@ -312,7 +315,7 @@ void oracle_verify_one(const oracle_inputs* in, const oracle_outputs* o, int32_t
         if (!(w > 0.0)) continue;
         key = log(w) - log(e);
       } else {
-        key = logit(in->target, in->dtype, trow0 + n, V, v) / T - log(e);
+        key = logit(in->target, in->dtype, trow0 + n, V, v) / T - lp[n] - log(e);
       }
       if (key > best) {
         second = best;
@@ -370,7 +373,7 @@ int oracle_spec_verify(int dtype, const void* target, const void* draft, int32_t
  * top token at every draft step (greedy drafting, T = 0).  Row b of `logits`
  * is the draft model's output for request b at draft step `step`.
  *   T == 0: x = lowest index attaining the row maximum;
- *   T > 0:  x = argmax_v (z_v / T - ln E_v) with E_v = -ln U_v, U_v from
+ *   T > 0:  x = argmax_v (ln q_v - ln E_v) with E_v = -ln U_v, U_v from
  *           Philox4x32-10 keyed by the seed, counter (v >> 2, step, b, 2),
  *           word v & 3 (stream tag 2, apart from the verify step's tags 0
  *           and 1); ties to the lowest index.  An exponential race, so x is
@@ -401,7 +404,8 @@ int oracle_draft_sample(int dtype, const void* logits, int32_t B, int32_t V,
     double best = -INFINITY, second = -INFINITY;
     int32_t x = -1;
     for (int32_t v = 0; v < V; ++v) {
-      double key = logit(logits, dtype, b, V, v) / T - log(oracle_draft_exponential(seed, b, step, v));
+      double key =
+          logit(logits, dtype, b, V, v) / T - lse - log(oracle_draft_exponential(seed, b, step, v));
       if (key > best) {
         second = best;
         best = key;

@@ -540,6 +540,163 @@ def pin_faults(lib):
     assert res["accept_len"][0] >= 0 and res["accept_len"][2] >= 0
 
 
+# ------------------------------------------------------------------ near ties and the empty residual
+#
+# The parity tests forgive a GPU mismatch only on a request the oracle flags,
+# so the flags are pinned like any other output: cases built so that the
+# quantity a flag measures is known by construction (independently of the
+# oracle's arithmetic) must flag inside the window and must not outside it.
+# The accept test and the race follow "Decodificacion Especulativa y EAGLE",
+# section "La Regla de Exactitud"; the window widths are the oracle's stated
+# reading (1e-6 relative).
+
+
+def _two_token_row(p):
+    """float64 logits of the two-token distribution (p, 1 - p)."""
+    return np.array([math.log(p), math.log1p(-p)])
+
+
+def pin_accept_near_tie_flag(lib, seed=31):
+    """r*q(x) placed at a known relative distance delta from p(x) (V = 2, K = 1, T = 1):
+    |delta| = 1e-9 flags, |delta| = 1e-3 does not, also for probabilities near 1e-8
+    (the window is relative); delta > 0 accepts and delta < 0 rejects."""
+    cases = [(1e-9, 0.4), (-1e-9, 0.4), (1e-3, 0.4), (-1e-3, 0.4), (1e-9, 2e-8), (1e-3, 2e-8),
+             (-1e-3, 2e-8)]
+    B = len(cases)
+    rows_t, rows_d, toks = [], [], []
+    for b, (delta, q) in enumerate(cases):
+        r = oracle.accept_uniform(seed, b, 0, lib=lib)
+        p = r * q * (1.0 + delta)
+        rows_t.append(np.stack([_two_token_row(p), np.zeros(2)]))
+        rows_d.append(_two_token_row(q)[None, :])
+        toks.append([0])
+    target, draft, offsets, tokens = pack_requests(rows_t, rows_d, toks)
+    res = oracle.verify(oracle.F64, target, draft, offsets, tokens, np.ones(B, np.float32), seed,
+                        2, 1, lib=lib)
+    for b, (delta, q) in enumerate(cases):
+        flagged = bool(res["flags"][b] & oracle.FLAG_ACCEPT_NEAR_TIE)
+        assert flagged == (abs(delta) < 1e-6), (b, delta, q, int(res["flags"][b]))
+        assert int(res["accept_len"][b]) == (1 if delta > 0 else 0), (b, delta)
+        # the reported probabilities are the constructed ones
+        assert abs(res["q_at"][b] - q) <= 1e-12 * q
+        r = oracle.accept_uniform(seed, b, 0, lib=lib)
+        assert abs(res["p_at"][b] - r * q * (1 + delta)) <= 1e-12 * q
+
+
+def pin_bonus_race_near_tie_flag(lib, seed=32):
+    """Bonus race (K = 0, V = 2): logits chosen so the two race keys differ by a known
+    eps.  |eps| = 1e-9 flags, |eps| = 1e-4 does not; the winner follows the sign of
+    eps and race_gap equals |eps|.  The same rows shifted by +1000, or at T = 0.25,
+    give the same outcome: the window does not widen with a logit offset."""
+    cases = []
+    for shift in (0.0, 1000.0):
+        for T in (1.0, 0.25):
+            for eps in (1e-9, -1e-9, 1e-4, -1e-4):
+                cases.append((eps, shift, T))
+    B = len(cases)
+    rows_t, temps = [], []
+    for b, (eps, shift, T) in enumerate(cases):
+        e0 = oracle.race_exponential(seed, b, 0, 0, lib=lib)
+        e1 = oracle.race_exponential(seed, b, 0, 1, lib=lib)
+        # key_v = z_v / T - lse - ln E_v, so key_0 - key_1 = (z_0 - z_1) / T - ln(E_0 / E_1)
+        d = (math.log(e0 / e1) + eps) * T
+        rows_t.append(np.array([[shift + d, shift]]))
+        temps.append(T)
+    target = np.concatenate(rows_t)
+    offsets = np.zeros(B + 1, np.int32)
+    res = oracle.verify(oracle.F64, target, np.zeros((0, 2)), offsets, np.zeros(0, np.int32),
+                        np.array(temps, np.float32), seed, 2, 0, lib=lib)
+    for b, (eps, shift, T) in enumerate(cases):
+        flagged = bool(res["flags"][b] & oracle.FLAG_RACE_NEAR_TIE)
+        assert flagged == (abs(eps) < 1e-6), (b, eps, shift, T, float(res["race_gap"][b]))
+        assert int(res["accept_len"][b]) == 0
+        assert int(res["out_tokens"][b]) == (0 if eps > 0 else 1), (b, eps)
+        assert abs(res["race_gap"][b] - abs(eps)) <= 1e-12 * (1 + shift) / T, (b, eps)
+
+
+def _residual_tie_case(lib, seed, b, eps, mass):
+    """Rows of one K = 1, V = 3 request whose draft x = 2 is always rejected
+    (target p_2 = 0 < r*q_2) and whose residual (p - q)+ lives on tokens 0 and 1
+    with weights w_0, w_1 (w_0 + w_1 = mass) chosen so that the residual race
+    keys ln w_v - ln E_v differ by eps."""
+    e0 = oracle.race_exponential(seed, b, 0, 0, lib=lib)
+    e1 = oracle.race_exponential(seed, b, 0, 1, lib=lib)
+    rho = (e0 / e1) * math.exp(eps)        # w_0 / w_1
+    w1 = mass / (1.0 + rho)
+    w0 = mass - w1
+    q = np.array([0.5, 0.5 - mass, mass])
+    p = np.array([q[0] + w0, q[1] + w1, 0.0])
+    with np.errstate(divide="ignore"):
+        zt = np.log(p)
+    return np.stack([zt, np.zeros(3)]), np.log(q)[None, :], [2]
+
+
+def pin_residual_race_near_tie_flag(lib, seed=33):
+    """Residual race with two positive weights whose keys differ by a known eps.
+    At residual mass 0.3: |eps| = 1e-9 flags, 1e-4 does not.  At mass 2e-9 the keys
+    sit near ln(1e-9) ~ -21, so the window 1e-6 * |best| is ~2e-5: eps = 5e-6 flags
+    there (the window scales with |best| above 1) and eps = 1e-4 does not."""
+    cases = [(1e-9, 0.3), (-1e-9, 0.3), (1e-4, 0.3), (-1e-4, 0.3), (5e-6, 2e-9), (-5e-6, 2e-9),
+             (1e-4, 2e-9)]
+    rows_t, rows_d, toks = [], [], []
+    for b, (eps, mass) in enumerate(cases):
+        t, d, x = _residual_tie_case(lib, seed, b, eps, mass)
+        rows_t.append(t)
+        rows_d.append(d)
+        toks.append(x)
+    target, draft, offsets, tokens = pack_requests(rows_t, rows_d, toks)
+    B = len(cases)
+    res = oracle.verify(oracle.F64, target, draft, offsets, tokens, np.ones(B, np.float32), seed,
+                        3, 1, lib=lib)
+    for b, (eps, mass) in enumerate(cases):
+        assert int(res["accept_len"][b]) == 0, b
+        assert not (res["flags"][b] & oracle.FLAG_RESIDUAL_EMPTY), b
+        best = float(res["race_best"][b])
+        window = 1e-6 * max(1.0, abs(best))
+        assert (abs(eps) < window) == bool(res["flags"][b] & oracle.FLAG_RACE_NEAR_TIE), \
+            (b, eps, mass, best, int(res["flags"][b]))
+        assert int(res["out_tokens"][offsets[b] + b]) == (0 if eps > 0 else 1), (b, eps)
+        # w_v = p_v - q_v loses ~1e-16 absolute to rounding, so ln w_v carries ~1e-16 / w_v
+        assert abs(res["race_gap"][b] - abs(eps)) <= 1e-7 * abs(eps) + 1e-14 + 3e-16 / mass, \
+            (b, eps)
+    # the tiny-mass cases are inside the widened window only because |best| > 1
+    assert all(abs(float(res["race_best"][b])) > 10 for b in (4, 5, 6))
+
+
+def pin_residual_empty_fallback(lib, seed=34, B=96):
+    """A rejection with an empty residual.  Target row (1, 0, -800) against draft row
+    (1, 0, -700) at T = 1, draft token 2: in float64 the target's p_2 underflows to 0
+    while q_2 ~ 1e-305 does not, p_0 = q_0 and p_1 = q_1 exactly, so (p - q)+ is
+    zero everywhere.  The request must reject at t = 0, set the residual-empty flag,
+    and draw from p_0 instead: the winner is argmax over v of ln p_v - ln E_v.  An
+    identical draft row accepts its token 0 (control).  The cases include seeds where that
+    winner differs both from the plain minimum of E (an unweighted race) and from
+    the minimum of E over tokens 0 and 1."""
+    zt = np.array([[1.0, 0.0, -800.0], [0.0, 0.0, 0.0]])
+    zq = np.array([[1.0, 0.0, -700.0]])
+    assert math.exp(-800.0 - math.log(math.e + 1)) == 0.0 and math.exp(-700.0 - 1.32) > 0.0
+    rows_t = [zt] * B + [zt]
+    rows_d = [zq] * B + [zt[:1]]
+    toks = [[2]] * B + [[0]]
+    target, draft, offsets, tokens = pack_requests(rows_t, rows_d, toks)
+    res = oracle.verify(oracle.F64, target, draft, offsets, tokens, np.ones(B + 1, np.float32),
+                        seed, 3, 1, lib=lib)
+    with np.errstate(divide="ignore"):
+        lp = np.log(scipy.special.softmax(zt[0]))
+    differs_unweighted = differs_pair = 0
+    for b in range(B):
+        assert int(res["accept_len"][b]) == 0, b
+        assert res["flags"][b] & oracle.FLAG_RESIDUAL_EMPTY, b
+        e = np.array([oracle.race_exponential(seed, b, 0, v, lib=lib) for v in range(3)])
+        with np.errstate(divide="ignore"):
+            want = int(np.argmax(lp - np.log(e)))
+        assert int(res["out_tokens"][offsets[b] + b]) == want, (b, want, e)
+        differs_unweighted += want != int(np.argmin(e))
+        differs_pair += want != int(np.argmin(e[:2]))
+    assert differs_unweighted > 0 and differs_pair > 0
+    assert int(res["accept_len"][B]) == 1 and res["flags"][B] == 0
+
+
 # ------------------------------------------------------------------ draft-side sampler
 
 
@@ -603,6 +760,26 @@ def pin_draft_faults(lib):
     res = oracle.draft_sample(oracle.F64, z, temp, 2, 0, lib=lib)
     assert list(res["tokens"][1:5]) == [-1, -1, -1, -1]
     assert 0 <= res["tokens"][0] < V and res["tokens"][5] == int(np.argmax(z[5]))
+
+
+def pin_draft_race_near_tie_flag(lib, seed=35):
+    """Draft race (V = 2) with keys built to differ by a known eps, as for the bonus
+    race: 1e-9 flags, 1e-4 does not, the winner follows the sign of eps, and a
+    +1000 logit shift or T = 0.25 changes nothing."""
+    cases = [(eps, shift, T) for shift in (0.0, 1000.0) for T in (1.0, 0.25)
+             for eps in (1e-9, -1e-9, 1e-4, -1e-4)]
+    step = 3
+    rows = []
+    for b, (eps, shift, T) in enumerate(cases):
+        e0 = oracle.draft_exponential(seed, b, step, 0, lib=lib)
+        e1 = oracle.draft_exponential(seed, b, step, 1, lib=lib)
+        rows.append([shift + (math.log(e0 / e1) + eps) * T, shift])
+    res = oracle.draft_sample(oracle.F64, np.array(rows), np.array([c[2] for c in cases],
+                              np.float32), seed, step, lib=lib)
+    for b, (eps, shift, T) in enumerate(cases):
+        assert bool(res["flags"][b] & oracle.FLAG_RACE_NEAR_TIE) == (abs(eps) < 1e-6), (b, eps)
+        assert int(res["tokens"][b]) == (0 if eps > 0 else 1), (b, eps)
+        assert abs(res["race_gap"][b] - abs(eps)) <= 1e-12 * (1 + shift) / T, (b, eps)
 
 
 # ------------------------------------------------------------------ commit step
@@ -810,7 +987,9 @@ def pin_tree_faults(lib):
 ALL_PINS = [pin_philox_kat, pin_philox_rocrand, pin_u01, pin_softmax_vs_scipy,
             pin_greedy_vs_numpy, pin_exact_enumeration, pin_plain_sampling, pin_closed_form,
             pin_temperature_invariance, pin_identical_draft_accepts, pin_disjoint_draft_rejects,
-            pin_faults, pin_draft_distribution, pin_draft_greedy, pin_draft_streams,
-            pin_draft_faults, pin_commit_example, pin_commit_after_verify,
+            pin_faults, pin_accept_near_tie_flag, pin_bonus_race_near_tie_flag,
+            pin_residual_race_near_tie_flag, pin_residual_empty_fallback,
+            pin_draft_distribution, pin_draft_greedy, pin_draft_streams,
+            pin_draft_faults, pin_draft_race_near_tie_flag, pin_commit_example, pin_commit_after_verify,
             pin_tree_page_example, pin_tree_chain_is_linear, pin_tree_brute_force,
             pin_tree_faults]

@@ -1,7 +1,7 @@
 """GPU parity of the draft-side sampler (spec_draft_sample) against the oracle.
 
 Tokens must match exactly except where the oracle flags a near tie in the
-race (flags bit 2, allowed in at most 0.1% of sampled rows, plus one); q(x)
+race (flags bit 2, allowed in at most 0.1% of sampled rows); q(x)
 within 1e-5 absolute; greedy rows and failures bit-exact.
 """
 import numpy as np
@@ -55,7 +55,7 @@ def check(rows, dtype, temps, seed, step, gpu=None):
     flagged = (ref["flags"] & oracle.FLAG_RACE_NEAR_TIE) != 0
     bad = (tok != ref["tokens"]) & ~(sampled & flagged)
     assert not bad.any(), (np.nonzero(bad)[0][:8], tok[bad][:8], ref["tokens"][bad][:8])
-    assert flagged[sampled].sum() <= 0.001 * sampled.sum() + 1
+    assert flagged[sampled].sum() <= 0.001 * sampled.sum()
     ok = (ref["tokens"] >= 0) & sampled & ~flagged
     if ok.any():
         assert np.abs(q[ok] - ref["q_at"][ok]).max() < Q_TOL

@@ -83,7 +83,8 @@ def oracle_chain(b, seq0, lens0):
                       b.max_k)
     c = oracle.commit_tokens(b.offsets, v["accept_len"], v["out_tokens"], seq0, lens0, b.max_k,
                              n_draft_rows=b.n_draft_rows)
-    flagged = draft_flag | ((b.temperature > 0) & (v["flags"] != 0))
+    near_tie = oracle.FLAG_ACCEPT_NEAR_TIE | oracle.FLAG_RACE_NEAR_TIE
+    flagged = draft_flag | ((b.temperature > 0) & ((v["flags"] & near_tie) != 0))
     return dict(draft_tokens=tokens, accept_len=v["accept_len"], out_tokens=v["out_tokens"],
                 **c), flagged
 
@@ -98,7 +99,7 @@ def test_decode_step_chain(cfg, B):
     lens0 = rng.integers(0, cap - b.max_k - 1, size=b.B).astype(np.int32)
     got = gpu_chain(b, seq0, lens0, cap)
     want, flagged = oracle_chain(b, seq0, lens0)
-    assert flagged.sum() <= 1 + b.B // 100, flagged.sum()
+    assert flagged.sum() <= 0.001 * (b.temperature > 0).sum(), flagged.sum()
     exact = ~flagged
     for q in np.flatnonzero(exact):
         o, o1 = int(b.offsets[q]), int(b.offsets[q + 1])

@@ -40,9 +40,31 @@ MUTANTS = {
     "target_row_alignment": ("const int64_t trow0 = (int64_t)off + b;",
                              "const int64_t trow0 = (int64_t)off;"),
     # bonus drawn from the last drafted position instead of the one after it
-    "bonus_wrong_row": ("key = logit(in->target, in->dtype, trow0 + n, V, v) / T - log(e);",
+    "bonus_wrong_row": ("key = logit(in->target, in->dtype, trow0 + n, V, v) / T - lp[n] - log(e);",
                         "key = logit(in->target, in->dtype, trow0 + (n > 0 ? n - 1 : 0), V, v)"
-                        " / T - log(e);"),
+                        " / T - lp[n] - log(e);"),
+    # bonus key left unnormalised (z / T - ln E): the near-tie window then grows with a
+    # constant added to the logits
+    "bonus_key_unshifted": ("/ T - lp[n] - log(e);", "/ T - log(e);"),
+    # accept near-tie window 1000 times too wide
+    "accept_flag_wide": ("fabs(r * q - p) < 1e-6 * fmax(p, r * q)",
+                         "fabs(r * q - p) < 1e-3 * fmax(p, r * q)"),
+    # accept near-tie window absolute instead of relative
+    "accept_flag_absolute": ("fabs(r * q - p) < 1e-6 * fmax(p, r * q)", "fabs(r * q - p) < 1e-6"),
+    # race near-tie window 1000 times too wide (verify step)
+    "race_flag_wide": ("if (best - second < 1e-6 * fmax(1.0, fabs(best)) && o->flags)",
+                       "if (best - second < 1e-3 * fmax(1.0, fabs(best)) && o->flags)"),
+    # race near-tie window that does not scale with |best|
+    "race_flag_unscaled": ("if (best - second < 1e-6 * fmax(1.0, fabs(best)) && o->flags)",
+                           "if (best - second < 1e-6 * fmin(1.0, fabs(best)) && o->flags)"),
+    # empty residual: the fallback race on p_n removed (nothing is drawn)
+    "fallback_removed": ("if (residual && any_positive) {", "if (residual) {"),
+    # empty residual detected with >=, so an all-zero residual counts as non-empty
+    "residual_empty_test": ("if (p - q > 0.0) any_positive = 1;", "if (p - q >= 0.0) any_positive = 1;"),
+    # empty residual: fallback races every token with equal weight
+    "fallback_unweighted": ("        key = logit(in->target, in->dtype, trow0 + n, V, v) / T - lp[n] - log(e);",
+                            "        key = residual ? -log(e) :\n"
+                            "            logit(in->target, in->dtype, trow0 + n, V, v) / T - lp[n] - log(e);"),
     # exponential race with the wrong sign on the exponential variate
     "race_sign": ("key = log(w) - log(e);", "key = log(w) + log(e);"),
     # Philox: wrong multiplier in the first lane
@@ -51,8 +73,11 @@ MUTANTS = {
     # Philox: wrong key increment
     "philox_key_schedule": ("k1 += W1;", "k1 += W0;"),
     # draft sampler: exponential variate added instead of subtracted
-    "draft_race_sign": ("/ T - log(oracle_draft_exponential(seed, b, step, v));",
-                        "/ T + log(oracle_draft_exponential(seed, b, step, v));"),
+    "draft_race_sign": ("/ T - lse - log(oracle_draft_exponential(seed, b, step, v));",
+                        "/ T - lse + log(oracle_draft_exponential(seed, b, step, v));"),
+    # draft sampler: key left unnormalised (z / T - ln E)
+    "draft_key_unshifted": ("/ T - lse - log(oracle_draft_exponential(seed, b, step, v));",
+                            "/ T - log(oracle_draft_exponential(seed, b, step, v));"),
     # draft sampler: the draft step left out of the counter
     "draft_step_ignored": ("(uint32_t)v >> 2, (uint32_t)step, (uint32_t)b, 2u",
                            "(uint32_t)v >> 2, 0u, (uint32_t)b, 2u"),
@@ -60,8 +85,8 @@ MUTANTS = {
     "draft_stream_tag": ("(uint32_t)v >> 2, (uint32_t)step, (uint32_t)b, 2u",
                          "(uint32_t)v >> 2, (uint32_t)step, (uint32_t)b, 0u"),
     # draft sampler: temperature ignored in the race key
-    "draft_untempered": ("double key = logit(logits, dtype, b, V, v) / T - log(",
-                         "double key = logit(logits, dtype, b, V, v) - log("),
+    "draft_untempered": ("logit(logits, dtype, b, V, v) / T - lse - log(",
+                         "logit(logits, dtype, b, V, v) - lse - log("),
     # commit: the emitted token left out (only the accepted drafts appended)
     "commit_drops_emitted": ("for (int32_t i = 0; i <= n; ++i)\n      seq_tokens",
                              "for (int32_t i = 0; i < n; ++i)\n      seq_tokens"),
@@ -90,9 +115,12 @@ MUTANTS = {
 # cheap pins first; the first failing pin ends a case
 ORDER = [P.pin_philox_kat, P.pin_u01, P.pin_softmax_vs_scipy, P.pin_greedy_vs_numpy,
          P.pin_temperature_invariance, P.pin_identical_draft_accepts,
-         P.pin_disjoint_draft_rejects, P.pin_faults, P.pin_plain_sampling,
+         P.pin_disjoint_draft_rejects, P.pin_faults, P.pin_accept_near_tie_flag,
+         P.pin_bonus_race_near_tie_flag, P.pin_residual_race_near_tie_flag,
+         P.pin_residual_empty_fallback, P.pin_plain_sampling,
          P.pin_exact_enumeration, P.pin_closed_form, P.pin_draft_greedy, P.pin_draft_faults,
-         P.pin_draft_distribution, P.pin_draft_streams, P.pin_commit_example,
+         P.pin_draft_distribution, P.pin_draft_streams, P.pin_draft_race_near_tie_flag,
+         P.pin_commit_example,
          P.pin_commit_after_verify, P.pin_tree_page_example, P.pin_tree_faults,
          P.pin_tree_chain_is_linear, P.pin_tree_brute_force]
 
