@@ -79,6 +79,13 @@ def parse():
                          "early-exit verify on the same batch; tree: greedy draft-tree "
                          "verification on --tree; greedy: spec_verify_greedy on the "
                          "workload with every request greedy")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs of --traffic-probe (FETCH_SIZE, "
+                         "then WRITE_SIZE, -f csv) into the traffic record of --op on "
+                         "--workload under profiles/, and print the summary")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="no GPU: per-kernel dispatch durations (count, mean, median, "
+                         "min, max) from a rocprofv3 --kernel-trace -f csv run")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -165,6 +172,115 @@ DRAFT_SLOTS_SAMPLED = 30
 DRAFT_SLOTS_GREEDY = 2
 # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: full-rate 32-bit VALU lane slots / s
 PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+
+
+def _csv_rows(directory: str, suffix: str):
+    """Rows of every rocprofv3 CSV under `directory` whose name ends in `suffix`."""
+    import csv
+    found = []
+    for dp, _, files in os.walk(directory):
+        for fn in sorted(files):
+            if fn.endswith(suffix):
+                with open(os.path.join(dp, fn), newline="") as f:
+                    found.extend(csv.DictReader(f))
+    if not found:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return found
+
+
+def kernel_base_name(name: str) -> str:
+    """`sv_verify` from `void (anonymous namespace)::sv_verify<true, true>(...)`."""
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("<")[0].split("(")[0].split("::")[-1].strip()
+
+
+def _per_dispatch(rows, counter: str):
+    """{dispatch id: (kernel name, counter value summed over its rows)} in dispatch order."""
+    out = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = out.get(d, (r["Kernel_Name"], 0.0))
+        out[d] = (name, v + float(r["Counter_Value"]))
+    return dict(sorted(out.items()))
+
+
+KERNEL_OF_OP = {"verify": "sv_verify", "early-exit": "sv_verify_ee", "greedy": "sv_verify"}
+# file-name tags of the workloads' profile summaries
+SLUG = {1: "tiny_b1_k4_f32", 2: "llama_b64_k4_bf16", 3: "large_batch_b256_k8_f32",
+        4: "mtp_b512_k1_bf16", 5: "ragged_b1024_bf16"}
+
+
+def summarize_counters(args):
+    """Traffic record of one kernel from FETCH_SIZE and WRITE_SIZE runs of
+    `bench.py --traffic-probe MIB` (KiB per dispatch).  Each counter is scaled by
+    what it reads for the probe's device copies of MIB MiB (MIB MiB read and
+    MIB MiB written per copy)."""
+    import numpy as np
+    kernel = KERNEL_OF_OP[args.op]
+    sources = EE_KERNEL_SOURCES if args.op == "early-exit" else KERNEL_SOURCES
+    lines = []
+    vals = {}
+    for counter, directory in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_counters):
+        disp = _per_dispatch(_csv_rows(directory, "counter_collection.csv"), counter)
+        copies = [v for n, v in disp.values() if "copyBuffer" in n]
+        mine = [v for n, v in disp.values() if kernel_base_name(n) == kernel]
+        if len(copies) < 3 or not mine:
+            raise SystemExit(f"{counter}: {len(copies)} copy and {len(mine)} {kernel} dispatches")
+        copy_kib = float(np.median(copies[-5:]))
+        size_kib = float(args.traffic_probe << 10)
+        scale = size_kib / copy_kib
+        mean = float(np.mean(mine))
+        vals[counter] = (mean, scale, len(mine), float(np.min(mine)), float(np.max(mine)))
+        lines.append(f"  {counter} per copy (KiB): {[round(c, 1) for c in copies[-5:]]}"
+                     f"  -> scale {scale:.4f}")
+    fetch = vals["FETCH_SIZE"][0] * vals["FETCH_SIZE"][1] * 1024
+    write = vals["WRITE_SIZE"][0] * vals["WRITE_SIZE"][1] * 1024
+    from rejection_sampling_verify_scaled_amd import workloads as W
+    batch = W.make_batch(args.workload, 0)
+    alg = algorithmic_bytes(batch)
+    rec = {"kernel": kernel, "workload": args.workload,
+           "source_sha256": kernel_source_sha256(sources),
+           "hbm_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+           "fetch_scale": vals["FETCH_SIZE"][1], "write_scale": vals["WRITE_SIZE"][1],
+           "summary": f"profiles/{kernel}_{SLUG[args.workload]}_traffic.txt"}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{kernel}_workload{args.workload}.json"),
+              "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    m, sc, n, lo, hi = vals["FETCH_SIZE"]
+    print(f"HBM traffic of {kernel}, workload {args.workload} ({W.WORKLOADS[args.workload].name})")
+    print(f"kernel source sha256: {rec['source_sha256']}")
+    print(f"reference: the probe's device copies of {args.traffic_probe} MiB")
+    print("\n".join(lines))
+    print(f"{kernel}, {n} dispatches: FETCH_SIZE mean {m:.1f} KiB (min {lo:.1f}, max {hi:.1f});"
+          f" WRITE_SIZE mean {vals['WRITE_SIZE'][0]:.1f} KiB")
+    print(f"  scaled: read {fetch / 1e6:.2f} MB + written {write / 1e6:.3f} MB = "
+          f"{(fetch + write) / 1e6:.2f} MB per launch")
+    if args.op != "early-exit":
+        print(f"  algorithmic bytes per launch: {alg / 1e6:.2f} MB; measured / algorithmic = "
+              f"{(fetch + write) / alg:.3f}")
+
+
+def summarize_trace(args):
+    """Per-kernel dispatch durations from a rocprofv3 --kernel-trace run."""
+    import numpy as np
+    rows = _csv_rows(args.summarize_trace, "kernel_trace.csv")
+    by = {}
+    for r in rows:
+        name = kernel_base_name(r["Kernel_Name"])
+        by.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"{'kernel':60s} {'calls':>6s} {'mean us':>9s} {'median':>9s} {'min':>9s} {'max':>9s}")
+    for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(d)
+        print(f"{name[:60]:60s} {a.size:6d} {a.mean():9.2f} {np.median(a):9.2f} {a.min():9.2f} "
+              f"{a.max():9.2f}")
 
 
 def bench_draft(args):
@@ -448,6 +564,12 @@ def bench_tree(args):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the verify step is per request, so several GPUs would each run it on "

@@ -157,9 +157,9 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_offsets: torch.Tensor,
                        draft_tokens: torch.Tensor, max_k: int,
                        accept_len: Optional[torch.Tensor] = None,
                        out_tokens: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None):
+                       workspace: Optional[torch.Tensor] = None, stream=None, lib=None):
     """All-greedy verify; returns (accept_len [B], out_tokens [n_draft + B])."""
-    lib = load_library()
+    lib = lib or load_library()
     B, V, n_d, accept_len, out_tokens, workspace = _prepare(
         target_logits, draft_offsets, draft_tokens, max_k, accept_len, out_tokens, workspace)
     if not target_logits.is_contiguous():
@@ -180,9 +180,9 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                        out_tokens: Optional[torch.Tensor] = None,
                        p_at_draft: Optional[torch.Tensor] = None,
                        q_at_draft: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None):
+                       workspace: Optional[torch.Tensor] = None, stream=None, lib=None):
     """Mixed sampled / greedy verify; returns (accept_len, out_tokens, p_at, q_at)."""
-    lib = load_library()
+    lib = lib or load_library()
     B, V, n_d, accept_len, out_tokens, workspace = _prepare(
         target_logits, draft_offsets, draft_tokens, max_k, accept_len, out_tokens, workspace)
     device = target_logits.device
@@ -215,11 +215,11 @@ def spec_verify_sample_early_exit(target_logits: torch.Tensor, draft_logits: tor
                                   out_tokens: Optional[torch.Tensor] = None,
                                   p_at_draft: Optional[torch.Tensor] = None,
                                   q_at_draft: Optional[torch.Tensor] = None,
-                                  workspace: Optional[torch.Tensor] = None, stream=None):
+                                  workspace: Optional[torch.Tensor] = None, stream=None, lib=None):
     """Early-exit verify (rows past each request's stop are not read); returns
     (accept_len, out_tokens, p_at, q_at) like spec_verify_sample, with p/q NaN
     past the stop."""
-    lib = load_library()
+    lib = lib or load_library()
     B = draft_offsets.shape[0] - 1
     V = target_logits.shape[1]
     n_d = draft_tokens.shape[0]
@@ -256,9 +256,9 @@ def spec_draft_sample(draft_logits: torch.Tensor, temperature: torch.Tensor, see
                       step: int, tokens: Optional[torch.Tensor] = None,
                       q_at: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, stream=None,
-                      want_q: bool = True):
+                      want_q: bool = True, lib=None):
     """Draft-side sampler over rows [B, V]; returns (tokens [B] int32, q_at [B] or None)."""
-    lib = load_library()
+    lib = lib or load_library()
     if draft_logits.dim() != 2 or not draft_logits.is_contiguous():
         raise ValueError("draft_logits must be a contiguous [B, V] tensor")
     B, V = draft_logits.shape
@@ -286,10 +286,10 @@ def spec_commit_tokens(draft_offsets: torch.Tensor, accept_len: torch.Tensor,
                        out_tokens: torch.Tensor, seq_tokens: torch.Tensor,
                        seq_len: torch.Tensor, max_k: int, capacity: Optional[int] = None,
                        next_tokens: Optional[torch.Tensor] = None,
-                       status: Optional[torch.Tensor] = None, stream=None):
+                       status: Optional[torch.Tensor] = None, stream=None, lib=None):
     """Append the verify step's emitted tokens to the histories seq_tokens [B, S]
     (in place) and advance seq_len [B]; returns (next_tokens [B], status [B])."""
-    lib = load_library()
+    lib = lib or load_library()
     B = accept_len.shape[0]
     device = accept_len.device
     _check(draft_offsets, "draft_offsets", torch.int32, (B + 1,), device)
@@ -324,10 +324,10 @@ def spec_verify_tree_greedy(target_logits: torch.Tensor, node_offsets: torch.Ten
                             out_tokens: Optional[torch.Tensor] = None,
                             accept_nodes: Optional[torch.Tensor] = None,
                             want_nodes: bool = True,
-                            workspace: Optional[torch.Tensor] = None, stream=None):
+                            workspace: Optional[torch.Tensor] = None, stream=None, lib=None):
     """Greedy draft-tree verify; returns (accept_len [B], out_tokens [n_rows],
     accept_nodes [n_rows] or None)."""
-    lib = load_library()
+    lib = lib or load_library()
     if target_logits.dim() != 2:
         raise ValueError("target_logits must be 2-D [rows, V]")
     device = target_logits.device

@@ -17,6 +17,11 @@ SRCS = [os.path.join(PKG, "csrc", name)
 SRC = SRCS[0]  # the verify kernel's source (its sha256 keys the committed traffic counters)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
+# The same sources with every bounded wait cut to a single load: a test build
+# in which waits expire, to check that the kernels then still exit and fail
+# only the requests they could not finish (never loaded by the product path).
+LIB_SPIN0 = os.path.join(PKG, "libspecverify_spin0.so")
+SPIN0_FLAGS = ("-DSV_SPIN_LIMIT=0u",)
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -50,6 +55,16 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> None:
+    """The product library and the expired-wait test build."""
+    build(verbose=verbose)
+    build(out=LIB_SPIN0, extra=SPIN0_FLAGS, verbose=verbose)
+
+
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
-    print(LIB)
+    if sys.argv[1:] == ["--all"]:
+        build_all(verbose=True)
+        print(LIB, LIB_SPIN0)
+    else:
+        build(verbose=True, extra=sys.argv[1:])
+        print(LIB)

@@ -21,7 +21,13 @@ constexpr int kItemVecs = 8;                      // 16-byte loads per lane per 
 constexpr int kItemsInFlight = 2;                 // row-chunks a wave loads before reducing
 constexpr int kGroupItems = kWaves * kItemsInFlight;  // flat grouping: row-chunks per workgroup
 constexpr int kChunkBytes = 64 * kItemVecs * 16;  // one row-chunk: 8 KiB
-constexpr unsigned kSpinLimit = 1u << 16;         // polls before a wait gives up
+// Polls before a wait gives up.  A library built with a small limit (0: one
+// load, no re-poll) makes the waits expire on purpose, so that the expired
+// paths can be exercised: every wait still ends and every kernel exits.
+#ifndef SV_SPIN_LIMIT
+#define SV_SPIN_LIMIT (1u << 16)
+#endif
+constexpr unsigned kSpinLimit = SV_SPIN_LIMIT;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ int ceil_div_dev(int a, int b) { return (a + b - 1) / b; }
