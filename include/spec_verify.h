@@ -41,7 +41,8 @@
  *   Logits are float32 (SV_F32) or bfloat16 bit patterns (SV_BF16).
  *
  * Ownership: the caller owns every buffer, the workspace included.  The library
- * allocates nothing, keeps no host state between calls, never synchronises, and
+ * allocates nothing, keeps no host state between calls (apart from the device
+ * address of spec_verify_sample_static's array), never synchronises, and
  * only enqueues one kernel on `stream` (a hipStream_t; NULL is the default
  * stream).  Outputs are valid once the stream reaches the end of the call's
  * work.  The workspace carries hand-off slots between the kernel's
@@ -53,8 +54,8 @@
  * Errors: a negative return value means nothing was enqueued (except
  * SV_ERR_LAUNCH, which reports a launch failure).  accept_len[b] = -1 with
  * tokens left unwritten would mean a bounded wait inside the kernel expired
- * (the device stopped making progress); zero the workspace again after that.  Per-request problems found
- * on the device -- K_b outside [0, max_k], a slice outside [0, n_draft_rows),
+ * (the device stopped making progress); zero the workspace again after that.
+ * Per-request problems found on the device -- K_b outside [0, max_k], a slice outside [0, n_draft_rows),
  * a draft token outside [0, V), a temperature that is negative, NaN or
  * infinite, a needed row whose maximum is not finite, or a NaN in a row that
  * a sampled request reads -- set accept_len[b] = -1 and fill request b's output
@@ -72,6 +73,7 @@ extern "C" {
 
 #define SV_KMAX 8 /* largest per-request draft length */
 #define SV_TREE_MAX_NODES 64 /* largest draft tree (root included), spec_verify_tree_greedy */
+#define SV_STATIC_SCRATCH_BYTES ((size_t)16 << 20) /* fixed array of spec_verify_sample_static */
 
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
@@ -83,7 +85,9 @@ enum sv_status {
   SV_ERR_DTYPE = -3,     /* dtype is not SV_F32 or SV_BF16 */
   SV_ERR_WORKSPACE = -4, /* workspace smaller than spec_verify_workspace_bytes() or
                             not 16-byte aligned */
-  SV_ERR_LAUNCH = -5     /* the HIP runtime rejected a kernel launch */
+  SV_ERR_LAUNCH = -5,    /* the HIP runtime rejected a kernel launch */
+  SV_ERR_SCRATCH = -6    /* spec_verify_sample_static: spec_verify_workspace_bytes(B, V,
+                            max_k) exceeds SV_STATIC_SCRATCH_BYTES */
 };
 
 /* Host function.  Bytes of device workspace a call with these sizes needs
@@ -134,6 +138,38 @@ int spec_verify_sample_timed(const void* target_logits, const void* draft_logits
                              int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* event_start, void* event_end);
+
+/* ---------------------------------------------------------------- no allocation */
+
+/* For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  spec_verify_sample with the workspace replaced by a fixed
+ * array in the library's device code: SV_STATIC_SCRATCH_BYTES (16 MiB) per
+ * device, held by every device the library runs on until the process ends.  No call allocates (no hipMalloc, hipFree or
+ * allocating library routine).  Same arguments, results and status codes as
+ * spec_verify_sample, without workspace and workspace_bytes, plus:
+ *   clear_scratch  host; nonzero enqueues a zero fill of the hand-off slots
+ *                  this call uses before its kernel.  The first call on a
+ *                  device always fills the whole array.  Every completed
+ *                  call leaves the slots zero, so 0 is the normal value;
+ *                  pass 1 after a call that returned accept_len = -1 from an
+ *                  expired wait.
+ * Sizes whose spec_verify_workspace_bytes(B, V, max_k) exceeds the array
+ * (e.g. B = 1024 requests of max_k = 8 at V = 256k) return SV_ERR_SCRATCH
+ * with nothing enqueued.  The slots start zero (the loader zero-fills the
+ * array, and the first call fills it again); each call relies on the last
+ * completed call on that device having left them zero.  All calls on one
+ * device share the array: two calls that may overlap in time on one device
+ * (different streams or host threads) race and give wrong results.  The
+ * first call on a device looks up the array's device address with
+ * hipGetSymbolAddress (with that device current) and keeps it for later
+ * calls. */
+int spec_verify_sample_static(const void* target_logits, const void* draft_logits, int32_t dtype,
+                              int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows,
+                              const int32_t* draft_offsets, const int32_t* draft_tokens,
+                              const float* temperature, uint64_t seed, int32_t* accept_len,
+                              int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                              int32_t clear_scratch, void* stream);
 
 /* ---------------------------------------------------------------- early exit */
 

@@ -22,8 +22,9 @@ SV_F32 = 0
 SV_BF16 = 1
 SV_KMAX = 8
 SV_TREE_MAX_NODES = 64
+SV_STATIC_SCRATCH_BYTES = 16 << 20
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
-          -4: "SV_ERR_WORKSPACE", -5: "SV_ERR_LAUNCH"}
+          -4: "SV_ERR_WORKSPACE", -5: "SV_ERR_LAUNCH", -6: "SV_ERR_SCRATCH"}
 
 
 class SpecVerifyError(RuntimeError):
@@ -53,6 +54,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_sample.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, u64, vp, vp,
                                        vp, vp, vp, sz, vp]
     lib.spec_verify_sample.restype = ctypes.c_int
+    lib.spec_verify_sample_static.argtypes = list(lib.spec_verify_sample.argtypes[:15]) + [i32, vp]
+    lib.spec_verify_sample_static.restype = ctypes.c_int
     lib.spec_verify_sample_timed.argtypes = list(lib.spec_verify_sample.argtypes) + [vp, vp]
     lib.spec_verify_sample_timed.restype = ctypes.c_int
     lib.spec_verify_early_exit_workspace_bytes.argtypes = [i32, i32, i32]
@@ -201,6 +204,48 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if rc != 0:
         raise SpecVerifyError("spec_verify_sample", rc, lib.spec_verify_status_string(rc).decode())
+    return accept_len, out_tokens, p_at_draft, q_at_draft
+
+
+def spec_verify_sample_static(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                              draft_offsets: torch.Tensor, draft_tokens: torch.Tensor,
+                              temperature: torch.Tensor, seed: int, max_k: int,
+                              accept_len: torch.Tensor, out_tokens: torch.Tensor,
+                              p_at_draft: Optional[torch.Tensor] = None,
+                              q_at_draft: Optional[torch.Tensor] = None,
+                              clear_scratch: bool = False, stream=None, lib=None):
+    """spec_verify_sample on the library's fixed device array instead of a
+    workspace: allocates nothing, so every output is passed in.  Returns
+    (accept_len, out_tokens, p_at, q_at)."""
+    lib = lib or load_library()
+    if target_logits.dim() != 2 or target_logits.device.type != "cuda":
+        raise ValueError("target_logits must be a 2-D tensor on a HIP device")
+    device = target_logits.device
+    B = draft_offsets.shape[0] - 1
+    V = target_logits.shape[1]
+    n_d = draft_tokens.shape[0]
+    if B < 1:
+        raise ValueError("need at least one request (offsets has B+1 entries)")
+    if not 0 <= max_k <= SV_KMAX:
+        raise ValueError(f"max_k must be in [0, {SV_KMAX}]")
+    _check(draft_offsets, "draft_offsets", torch.int32, (B + 1,), device)
+    _check(draft_tokens, "draft_tokens", torch.int32, (n_d,), device)
+    _check(target_logits, "target_logits", target_logits.dtype, (n_d + B, V), device)
+    _check(draft_logits, "draft_logits", target_logits.dtype, (n_d, V), device)
+    _check(temperature, "temperature", torch.float32, (B,), device)
+    _check(accept_len, "accept_len", torch.int32, (B,), device)
+    _check(out_tokens, "out_tokens", torch.int32, (n_d + B,), device)
+    for name, t in (("p_at_draft", p_at_draft), ("q_at_draft", q_at_draft)):
+        if t is not None:
+            _check(t, name, torch.float32, (n_d,), device)
+    rc = lib.spec_verify_sample_static(
+        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), B, V, max_k, n_d,
+        _ptr(draft_offsets), _ptr(draft_tokens), _ptr(temperature),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(accept_len), _ptr(out_tokens),
+        _ptr(p_at_draft), _ptr(q_at_draft), 1 if clear_scratch else 0, _stream_handle(stream))
+    if rc != 0:
+        raise SpecVerifyError("spec_verify_sample_static", rc,
+                              lib.spec_verify_status_string(rc).decode())
     return accept_len, out_tokens, p_at_draft, q_at_draft
 
 

@@ -55,6 +55,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 #include <cmath>
 #include <cstdint>
@@ -941,6 +942,57 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
              : launch<false, false>(prm, grid, s, ev0, ev1);
 }
 
+// ------------------------------------------------------------------ static scratch
+//
+// Hand-off slots of spec_verify_sample_static, the variant for callers that
+// cannot allocate device memory.  The array lives in the code object: every
+// device the library runs on holds one copy of kScratchBytes until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = SV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / sizeof(uint64_t)];
+
+__global__ __launch_bounds__(kThreads) void sv_zero_fill(uint4* p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchSlot {
+  void* ptr = nullptr;   // device address of `scratch` on this device
+  bool cleared = false;  // a zero fill of the whole array has been enqueued
+};
+
+// Looks up (once per device, with that device current) the device address of
+// `scratch`; enqueues a zero fill of the whole array on the first call on a
+// device, or of the first `clear_bytes` bytes when `clear_bytes` > 0.
+int static_scratch(hipStream_t stream, size_t clear_bytes, void** out) {
+  constexpr int kMaxDevices = 64;
+  static ScratchSlot slots[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(mu);
+  ScratchSlot& sl = slots[dev];
+  if (!sl.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_ERR_LAUNCH;
+    sl.ptr = p;
+  }
+  if (!sl.cleared) clear_bytes = kScratchBytes;
+  if (clear_bytes > 0) {
+    const int64_t n = static_cast<int64_t>(round256(std::min(clear_bytes, kScratchBytes)) / 16);
+    const int64_t grid = std::min<int64_t>(ceil_div(n, kThreads), 4 * compute_units());
+    hipLaunchKernelGGL(sv_zero_fill, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+                       static_cast<uint4*>(sl.ptr), n);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    sl.cleared = true;
+  }
+  *out = sl.ptr;
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -983,6 +1035,28 @@ int spec_verify_sample_timed(const void* target_logits, const void* draft_logits
                   q_at_draft, workspace, workspace_bytes, stream, false, event_start, event_end);
 }
 
+int spec_verify_sample_static(const void* target_logits, const void* draft_logits, int32_t dtype,
+                              int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows,
+                              const int32_t* draft_offsets, const int32_t* draft_tokens,
+                              const float* temperature, uint64_t seed, int32_t* accept_len,
+                              int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                              int32_t clear_scratch, void* stream) {
+  if (!target_logits || !draft_offsets || !accept_len || !out_tokens || !temperature ||
+      (n_draft_rows > 0 && (!draft_logits || !draft_tokens)))
+    return SV_ERR_NULL;
+  if (!shape_ok(B, V, max_k, n_draft_rows)) return SV_ERR_SHAPE;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  const size_t need = spec_verify_workspace_bytes(B, V, max_k);
+  if (need == 0 || need > kScratchBytes) return SV_ERR_SCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int rc = static_scratch(s, clear_scratch ? need : 0, &ws);
+  if (rc != SV_OK) return rc;
+  return dispatch(target_logits, draft_logits, dtype, B, V, max_k, n_draft_rows, draft_offsets,
+                  draft_tokens, temperature, seed, accept_len, out_tokens, p_at_draft,
+                  q_at_draft, ws, kScratchBytes, stream, false, nullptr, nullptr);
+}
+
 const char* spec_verify_status_string(int status) {
   switch (status) {
     case SV_OK: return "ok";
@@ -991,6 +1065,9 @@ const char* spec_verify_status_string(int status) {
     case SV_ERR_DTYPE: return "unknown dtype";
     case SV_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
     case SV_ERR_LAUNCH: return "kernel launch failed";
+    case SV_ERR_SCRATCH:
+      return "sizes need more hand-off slots than the static scratch holds "
+             "(SV_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
