@@ -1,6 +1,7 @@
 """C ABI checks that need no GPU: the library loads, exports what the header
 declares, sizes workspaces, and rejects bad arguments before any HIP call."""
 import ctypes
+import os
 
 import pytest
 
@@ -9,7 +10,10 @@ from rejection_sampling_verify_scaled_amd import binding
 
 @pytest.fixture(scope="module")
 def lib():
-    return binding.load_library()
+    # SPECVERIFY_HOST_TEST_LIB: another build of the same sources (the sanitizer
+    # test points it at a host-side AddressSanitizer build)
+    path = os.environ.get("SPECVERIFY_HOST_TEST_LIB")
+    return binding.load_library(path) if path else binding.load_library()
 
 
 def test_exports_every_declared_function(lib):
