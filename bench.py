@@ -174,6 +174,24 @@ DRAFT_SLOTS_GREEDY = 2
 PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
 
 
+def host_description() -> dict:
+    """CPU model and core counts of the host the CPU baseline ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
 # ------------------------------------------------------------------ rocprofv3 summaries
 
 
@@ -763,15 +781,20 @@ def main():
         print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
               flush=True)
         olib = oracle.load()
-        t0 = time.perf_counter()
-        passes = 0
+        threads = oracle.default_threads()
+        legs = {}
         res = None
-        while True:
-            res = oracle.verify_batch(batch, lib=olib)
-            passes += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        cpu_s = time.perf_counter() - t0
+        # the same oracle single-threaded, then with its requests split over
+        # `threads` worker threads; half the CPU time each
+        for n_thr in (1, threads):
+            t0 = time.perf_counter()
+            passes = 0
+            while True:
+                res = oracle.verify_batch(batch, lib=olib, threads=n_thr)
+                passes += 1
+                if time.perf_counter() - t0 >= args.cpu_seconds / 2:
+                    break
+            legs[n_thr] = (passes, time.perf_counter() - t0)
         greedy = batch.temperature == 0
         mism = 0
         for b in range(B):
@@ -782,11 +805,15 @@ def main():
             flagged = (not greedy[b]) and res["flags"][b] != 0
             if not same and not flagged:
                 mism += 1
+        (p1, s1), (pn, sn) = legs[1], legs[threads]
         line["cpu_baseline"] = {
-            "value": positions * passes / cpu_s, "unit": "positions/s", "cores": 1,
+            "value": positions * pn / sn, "unit": "positions/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{passes} passes over the full {B}-request batch of the same workload "
-                      f"(single-threaded float64 C oracle, {cpu_s:.1f} s)"}
+            "sample": f"{pn} passes over the full {B}-request batch of the same workload "
+                      f"(float64 C oracle, requests split over {threads} threads, {sn:.1f} s)",
+            "single_core": {"value": positions * p1 / s1, "cores": 1,
+                            "sample": f"{p1} passes, one thread, {s1:.1f} s"},
+            "host": host_description()}
         line["parity_check"] = {"requests": B, "unflagged_mismatches": int(mism),
                                 "flagged": int((res["flags"] != 0).sum())}
     else:

@@ -127,10 +127,11 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, int3
                        int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* spec_verify_sample, plus two HIP events (hipEvent_t handles created by the
- * caller) recorded on `stream` immediately before and after the library's
- * kernel, so a caller can time the kernel on the stream it runs on.  Both
- * events must be valid.  Same results as spec_verify_sample. */
+/* Measurement hook (not needed to serve): spec_verify_sample, plus two HIP
+ * events (hipEvent_t handles created by the caller) recorded on `stream`
+ * immediately before and after the library's kernel, so a benchmark can time
+ * the kernel on the stream it runs on.  Both events must be valid.  Same
+ * results as spec_verify_sample. */
 int spec_verify_sample_timed(const void* target_logits, const void* draft_logits, int32_t dtype,
                              int32_t B, int32_t V, int32_t max_k, int32_t n_draft_rows,
                              const int32_t* draft_offsets, const int32_t* draft_tokens,
@@ -175,7 +176,8 @@ int spec_verify_sample_static(const void* target_logits, const void* draft_logit
 
 /* Host function.  Workspace bytes spec_verify_sample_early_exit needs (either
  * dtype); 0 for a bad shape.  The workspace must be zero-filled once when
- * allocated; calls keep it usable without further clearing. */
+ * allocated; completed calls keep it usable without further clearing (zero it
+ * again after a call that reported accept_len = -1 from an expired wait). */
 size_t spec_verify_early_exit_workspace_bytes(int32_t B, int32_t V, int32_t max_k);
 
 /* Early-exit verify: the decision of spec_verify_sample without reading the
@@ -200,7 +202,12 @@ size_t spec_verify_early_exit_workspace_bytes(int32_t B, int32_t V, int32_t max_
  *     K = 8 fp32 from 64 requests of V = 128256, ragged K <= 8 bf16 from
  *     256 requests of V = 152064; at K = 1 the two are within a few us.
  * The workspace is the one sized by spec_verify_early_exit_workspace_bytes.
- * Calls that overlap in time need separate workspaces. */
+ * Unlike spec_verify_sample, each call enqueues two kernels on `stream`: the
+ * verify kernel, then a small kernel that clears its decision records.  As
+ * for the other entry points, accept_len[b] = -1 with no fault found in the
+ * request means a bounded wait expired; the workspace may then hold stale
+ * hand-off slots, so zero it again before the next call.  Calls that overlap
+ * in time need separate workspaces. */
 int spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits,
                                   int32_t dtype, int32_t B, int32_t V, int32_t max_k,
                                   int32_t n_draft_rows, const int32_t* draft_offsets,
