@@ -13,12 +13,13 @@
 // arithmetic-bound pass.  Workgroup g serves request b = g / ng and the 4
 // chunks cg * 4 + wave (cg = g mod ng, one chunk per wave).  A wave of a sampled request makes one pass over its chunk for the
 // maximum, then a second pass that, per token, forms the weight
-// w = 2^(z c - fl(m c)) (c = log2(e) / T, m the chunk maximum), adds it to
+// w = 2^((z - m) c) (c = log2(e) / T, m the chunk maximum), adds it to
 // the chunk's softmax sum and runs the exponential race: the token with the
 // largest w / e wins, e = -log2 U from Philox4x32-10 on stream tag 2,
 // counter (v >> 2, step, b, 2), word v & 3.  Candidates are compared by
 // cross-multiplication; the chunk's winner becomes the log2-domain key
-// log2(w / e) + fl(m c), which is comparable across chunks.  A greedy wave
+// log2(w / e), relative to the chunk maximum; the finisher moves each key to
+// the row maximum M by adding (m - M) c before comparing.  A greedy wave
 // reduces its chunk to (max, lowest argmax).  Each chunk leaves one or two
 // 8-byte slots in the workspace; the request's last workgroup in grid order
 // folds them (larger key, then lower index; softmax sums rescaled to the
@@ -68,8 +69,8 @@ __device__ __forceinline__ uint64_t* race_slot(const DraftParams& p, int b, int 
 }
 
 // Statistics and race of one sampled chunk held by a wave (lane elements as
-// in load_item).  Returns the statistics slot (max, sum relative to fl(max c))
-// and sets the race slot (log2-domain key, index).
+// in load_item).  Returns the statistics slot (max, sum relative to max) and
+// sets the race slot (log2-domain key relative to the chunk maximum, index).
 template <bool BF16, int NV>
 __device__ __forceinline__ uint64_t chunk_race(const uint4* buf, int64_t e0, float cf, uint32_t b,
                                                uint32_t step, uint32_t k0, uint32_t k1,
@@ -86,7 +87,7 @@ __device__ __forceinline__ uint64_t chunk_race(const uint4* buf, int64_t e0, flo
   }
   mx = wave_max(mx);
   // offset 0 when there is no finite max keeps a NaN visible in the sum
-  const float mc = (mx == -INFINITY) ? 0.f : scaled_max(mx, cf);
+  const float mc = weight_ref(mx);
   float s = 0.f, bw = 0.f, be = 1.f;
   int bi = INT_MAX;
 #pragma unroll
@@ -99,7 +100,7 @@ __device__ __forceinline__ uint64_t chunk_race(const uint4* buf, int64_t e0, flo
       const Philox4 r = philox_race(static_cast<uint32_t>((v0 >> 2) + h), step, b, kDraftTag, k0, k1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float w = fast_exp2(scaled_logit(xs[4 * h + k], cf, mc));
+        const float w = fast_exp2(log2_weight(xs[4 * h + k], cf, mc));
         s += w;
         const float e = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
         if (w * be > bw * e) {
@@ -111,7 +112,7 @@ __device__ __forceinline__ uint64_t chunk_race(const uint4* buf, int64_t e0, flo
     }
   }
   s = wave_sum(s);
-  float key = bi == INT_MAX ? -INFINITY : fast_log2(bw / be) + mc;
+  float key = bi == INT_MAX ? -INFINITY : fast_log2(bw / be);
   wave_merge_argmax(key, bi);
   race = pack_slot(key, static_cast<uint32_t>(bi));
   return pack_slot(mx, __float_as_uint(s));
@@ -151,6 +152,11 @@ __device__ void draft_finish(const DraftParams& p, int b, float T) {
   float M = -INFINITY, S = 0.f, key = -INFINITY;
   int idx = INT_MAX;
   bool expired = false;
+  // pass 1: the statistics (and a greedy row's argmax).  A sampled row's race
+  // keys are relative to their chunk maximum, so they are merged in pass 2,
+  // once the row maximum is known; the thread's first chunk keeps its slots
+  // in registers, later chunks (V above 256 chunks) are read again.
+  uint64_t first_s = 0u, first_r = 0u;
   for (int c = tid; c < p.nc; c += kThreads) {
     uint64_t* slots[2] = {stat_slot(p, b, c), race_slot(p, b, c)};
     uint64_t v[2];
@@ -160,41 +166,58 @@ __device__ void draft_finish(const DraftParams& p, int b, float T) {
     }
     if (greedy) {
       merge_argmax(M, idx, slot_f(v[0]), static_cast<int>(slot_w(v[0])));
+      slot_store(slots[0], 0u);
     } else {
       merge_stats(M, S, slot_f(v[0]), __uint_as_float(slot_w(v[0])), cf);
-      merge_argmax(key, idx, slot_f(v[1]), static_cast<int>(slot_w(v[1])));
+      if (c == tid) {
+        first_s = v[0];
+        first_r = v[1];
+        slot_store(slots[0], 0u);
+        slot_store(slots[1], 0u);
+      }
     }
-    slot_store(slots[0], 0u);
-    if (!greedy) slot_store(slots[1], 0u);
   }
   if (expired) atomicOr(&sh_bad, 1);
-  // fixed-order DPP tree over each wave
-  if (greedy) {
+  // fixed-order DPP tree over each wave, then the waves in order
+  if (greedy)
     wave_merge_argmax(M, idx);
-  } else {
+  else
     wave_merge_stats(M, S, cf);
-    wave_merge_argmax(key, idx);
-  }
   if (lane == 0) {
     sh_m[wave] = M;
     sh_s[wave] = S;
-    sh_k[wave] = key;
     sh_i[wave] = idx;
   }
   __syncthreads();
-  if (tid != 0) return;
   M = sh_m[0];
   S = sh_s[0];
-  key = sh_k[0];
   idx = sh_i[0];
   for (int w = 1; w < kWaves; ++w) {
-    if (greedy) {
+    if (greedy)
       merge_argmax(M, idx, sh_m[w], sh_i[w]);
-    } else {
+    else
       merge_stats(M, S, sh_m[w], sh_s[w], cf);
-      merge_argmax(key, idx, sh_k[w], sh_i[w]);
-    }
   }
+  if (!greedy) {
+    // pass 2: each chunk's key log2(w / e) + (m - M) c, relative to the row maximum
+    idx = INT_MAX;
+    for (int c = tid; c < p.nc; c += kThreads) {
+      uint64_t vs = first_s, vr = first_r;
+      if (c != tid) {
+        vs = slot_load(stat_slot(p, b, c));
+        vr = slot_load(race_slot(p, b, c));
+        if (vs != 0u) {
+          slot_store(stat_slot(p, b, c), 0u);
+          slot_store(race_slot(p, b, c), 0u);
+        }
+      }
+      if (vs == 0u || vr == 0u) continue;  // an expired wait (already reported)
+      const float kc = slot_f(vr) + (slot_f(vs) - M) * cf;
+      merge_argmax(key, idx, kc, static_cast<int>(slot_w(vr)));
+    }
+    block_argmax(key, idx, sh_k, sh_i);
+  }
+  if (tid != 0) return;
   const bool finite_max = M > -INFINITY && M < INFINITY;
   const bool ok = !sh_bad && finite_max && idx != INT_MAX && (greedy || S < INFINITY);
   p.tokens[b] = ok ? idx : -1;
@@ -202,7 +225,7 @@ __device__ void draft_finish(const DraftParams& p, int b, float T) {
     float q = NAN;
     if (ok && !greedy) {
       const float zx = load_logit<BF16>(p.logits, static_cast<int64_t>(b) * p.V + idx);
-      q = fast_exp2(scaled_logit(zx, cf, scaled_max(M, cf)) - fast_log2(S));
+      q = fast_exp2(log2_weight(zx, cf, M) - fast_log2(S));
     }
     p.q_at[b] = q;
   }

@@ -61,7 +61,7 @@ constexpr int kRaceChunks = 8;
 constexpr int kRaceChunksNarrow = 4;
 constexpr int64_t kNarrowRaceBelow = 512;
 constexpr int kStageRows = 2;      // a stage streams target row s and draft row s
-constexpr int kDecSlots = 5;       // decision record: code, fl(m_p c), log2 S_p, fl(m_q c), log2 S_q
+constexpr int kDecSlots = 5;       // decision record: code, m_p, log2 S_p, m_q, log2 S_q
 constexpr uint32_t kCont = 1u, kRej = 2u, kDone = 3u;  // decision codes (low byte)
 
 struct EeParams {
@@ -272,13 +272,13 @@ __device__ void ee_decide(const EeParams& p, int b, int s, const EeReq& r) {
   // sampled: ratio test at position s
   __shared__ int sh_rej;
   if (tid == 0) {
-    const float mcp = scaled_max(sh_m[0], cf), lsp = fast_log2(sh_s[0]);
-    const float mcq = scaled_max(sh_m[1], cf), lsq = fast_log2(sh_s[1]);
+    const float mp = sh_m[0], lsp = fast_log2(sh_s[0]);
+    const float mq = sh_m[1], lsq = fast_log2(sh_s[1]);
     const int32_t x = p.tokens[r.off0 + s];
     const float zp = load_logit<BF16>(p.target, (static_cast<int64_t>(r.off0) + b + s) * p.V + x);
     const float zq = load_logit<BF16>(p.draft, (static_cast<int64_t>(r.off0) + s) * p.V + x);
-    const float pp = fast_exp2(scaled_logit(zp, cf, mcp) - lsp);
-    const float qq = fast_exp2(scaled_logit(zq, cf, mcq) - lsq);
+    const float pp = fast_exp2(log2_weight(zp, cf, mp) - lsp);
+    const float qq = fast_exp2(log2_weight(zq, cf, mq) - lsq);
     const float u = uniform_open01(philox4x32_10(0u, s, b, 1u, p.k0, p.k1).w[0]);
     if (p.p_at) p.p_at[r.off0 + s] = pp;
     if (p.q_at) p.q_at[r.off0 + s] = qq;
@@ -286,9 +286,9 @@ __device__ void ee_decide(const EeParams& p, int b, int s, const EeReq& r) {
     if (!sh_rej) {
       dec_store(p, b, s, 0, kCont);
     } else {
-      dec_store(p, b, s, 1, __float_as_uint(mcp));
+      dec_store(p, b, s, 1, __float_as_uint(mp));
       dec_store(p, b, s, 2, __float_as_uint(lsp));
-      dec_store(p, b, s, 3, __float_as_uint(mcq));
+      dec_store(p, b, s, 3, __float_as_uint(mq));
       dec_store(p, b, s, 4, __float_as_uint(lsq));
       dec_store(p, b, s, 0, kRej | (static_cast<uint32_t>(s) << 8));
     }
@@ -302,7 +302,7 @@ __device__ void ee_decide(const EeParams& p, int b, int s, const EeReq& r) {
 // ------------------------------------------------------------------ races
 
 struct EeRace {
-  float cf, mcp, lsp, mcq, lsq;
+  float cf, mp, lsp, mq, lsq;
   int n;
   bool residual;
 };
@@ -328,7 +328,7 @@ __device__ __forceinline__ void ee_race_chunk(const uint4* bp, const uint4* bq, 
       for (int k = 0; k < EPV; ++k) mx = fmaxf(mx, xs[k]);
     }
     mx = wave_max(mx);
-    shift = (mx == -INFINITY) ? 0.f : scaled_max(mx, rr.cf);
+    shift = weight_ref(mx);
   }
   float bw = 0.f, be = 1.f;
   int bi = INT_MAX;
@@ -346,10 +346,10 @@ __device__ __forceinline__ void ee_race_chunk(const uint4* bp, const uint4* bq, 
       for (int k = 0; k < 4; ++k) {
         float w;
         if constexpr (RESIDUAL) {
-          w = fast_exp2(scaled_logit(zp[4 * h + k], rr.cf, rr.mcp) - rr.lsp) -
-              fast_exp2(scaled_logit(zq[4 * h + k], rr.cf, rr.mcq) - rr.lsq);
+          w = fast_exp2(log2_weight(zp[4 * h + k], rr.cf, rr.mp) - rr.lsp) -
+              fast_exp2(log2_weight(zq[4 * h + k], rr.cf, rr.mq) - rr.lsq);
         } else {
-          w = fast_exp2(scaled_logit(zp[4 * h + k], rr.cf, shift));
+          w = fast_exp2(log2_weight(zp[4 * h + k], rr.cf, shift));
         }
         const float e = -fast_log2(uniform_open01(ph.w[k]));  // E / ln 2
         if (w * be > bw * e) {
@@ -360,7 +360,8 @@ __device__ __forceinline__ void ee_race_chunk(const uint4* bp, const uint4* bq, 
       }
     }
   }
-  float kk = bi == INT_MAX ? -INFINITY : fast_log2(bw / be) + shift;
+  // (log2 keys over an absolute offset: chunks of one race share no reference)
+  float kk = bi == INT_MAX ? -INFINITY : fast_log2(bw / be) + shift * rr.cf;
   wave_merge_argmax(kk, bi);
   merge_argmax(key, idx, kk, bi);
 }
@@ -417,9 +418,9 @@ __device__ void ee_race(const EeParams& p, int b, int s, int rc, const EeReq& r)
         if (rc == p.ngr - 1 && tid == 0) p.accept_len[b] = -1;
         return;
       }
-      rr.mcp = __uint_as_float(v[0]);
+      rr.mp = __uint_as_float(v[0]);
       rr.lsp = __uint_as_float(v[1]);
-      rr.mcq = __uint_as_float(v[2]);
+      rr.mq = __uint_as_float(v[2]);
       rr.lsq = __uint_as_float(v[3]);
     } else if (kind == kCont && s == r.K) {
       rr.n = s;

@@ -10,7 +10,7 @@
 //      row-major order when every request has max_k drafts, else one column
 //      of m chunks across the request's rows): each wave streams whole
 //      row-chunks (8 16-byte loads per lane, two row-chunks in flight) and
-//      reduces each to one 8-byte partial: (max, sum of 2^(z c - fl(max c))),
+//      reduces each to one 8-byte partial: (max, sum of 2^((z - max) c)),
 //      c = log2(e) / T, for the K+1 target and K draft rows of a sampled
 //      request, or (max, lowest argmax index) for the K+1 target rows of a
 //      greedy one;
@@ -47,9 +47,9 @@
 // thread's best in a chunk becomes the float key w / e, and keys merge
 // across threads, chunks and workgroups by (larger key, then lower index),
 // an order-independent rule, so the winner does not depend on how chunks are
-// grouped.  Weights are 2^(z c - fl(m c)) with fl(m c) the rounded product
-// for the row maximum m; the same rounded offset is used when the row's sum
-// is formed, so it cancels exactly from p = w / sum.
+// grouped.  Weights are 2^((z - m) c) with m the row maximum, the exponent
+// formed from the exact difference z - m (device_common.h), and the row's sum
+// is formed relative to the same m, so m cancels exactly from p = w / sum.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -335,7 +335,7 @@ __device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, Fo
         const uint64_t x = rs[c];
         if (x != 0u) bm = fmaxf(bm, slot_f(x));
       }
-      const float bmc = (bm == -INFINITY) ? 0.f : scaled_max(bm, cf);
+      const float bmc = weight_ref(bm);
       S *= rescale(M, cf, bmc);
       for (int c = cb; c < ce; ++c) {
         const uint64_t x = rs[c];
@@ -412,7 +412,7 @@ __device__ void finish_greedy(const Params& p, int b, const Req& r) {
 // ------------------------------------------------------------------ race
 
 struct RaceRow {
-  float mcp, lsp, mcq, lsq, cf;
+  float mp, lsp, mq, lsq, cf;
   int n;
 };
 
@@ -454,10 +454,10 @@ __device__ __forceinline__ void race_group(const float zp[4], const float zq[4],
     const float e = -fast_log2(uniform_open01(r.w[k]));  // E / ln 2
     float w;
     if constexpr (RESIDUAL) {
-      w = fast_exp2(scaled_logit(zp[k], rr.cf, rr.mcp) - rr.lsp) -
-          fast_exp2(scaled_logit(zq[k], rr.cf, rr.mcq) - rr.lsq);
+      w = fast_exp2(log2_weight(zp[k], rr.cf, rr.mp) - rr.lsp) -
+          fast_exp2(log2_weight(zq[k], rr.cf, rr.mq) - rr.lsq);
     } else {
-      w = fast_exp2(scaled_logit(zp[k], rr.cf, rr.mcp));
+      w = fast_exp2(log2_weight(zp[k], rr.cf, rr.mp));
     }
     if (w * be > bw * e) {
       bw = w;
@@ -643,8 +643,8 @@ __device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t 
     bool reject = false;
     if (tid < K) {
       const float pp =
-          fast_exp2(scaled_logit(zp, cf, scaled_max(sh.row_m[tid], cf)) - sh.row_ls[tid]);
-      const float qq = fast_exp2(scaled_logit(zq, cf, scaled_max(sh.row_m[K + 1 + tid], cf)) -
+          fast_exp2(log2_weight(zp, cf, sh.row_m[tid]) - sh.row_ls[tid]);
+      const float qq = fast_exp2(log2_weight(zq, cf, sh.row_m[K + 1 + tid]) -
                                  sh.row_ls[K + 1 + tid]);
       const float u = uniform_open01(philox4x32_10(0u, tid, b, 1u, p.k0, p.k1).w[0]);
       reject = !(u * qq < pp);
@@ -658,10 +658,10 @@ __device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t 
     __syncthreads();
     // workgroup-uniform values read from LDS: keep them in scalar registers
     rr.n = uniform_int(sh_n);
-    rr.mcp = uniform_float(scaled_max(sh.row_m[rr.n], cf));
+    rr.mp = uniform_float(sh.row_m[rr.n]);
     rr.lsp = uniform_float(sh.row_ls[rr.n]);
     if (rr.n < K) {
-      rr.mcq = uniform_float(scaled_max(sh.row_m[K + 1 + rr.n], cf));
+      rr.mq = uniform_float(sh.row_m[K + 1 + rr.n]);
       rr.lsq = uniform_float(sh.row_ls[K + 1 + rr.n]);
     }
     const void* prow = static_cast<const char*>(p.target) + (trow0 + rr.n) * p.V * esz;

@@ -93,6 +93,21 @@ def test_draft_vocab_sizes(dtype, V):
     check(rows, dtype, temps, 1234 + V, 5)
 
 
+@pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
+def test_draft_temperature_range(dtype):
+    """Temperatures from 0.05 to 10 on N(0, 9) logits with 200 tokens raised by 8
+    (row maxima near 20, |z| / T up to about 400): tokens exact and q(x) within
+    1e-5 at every temperature."""
+    rng = np.random.default_rng(55 + dtype)
+    B, V = 48, 20011
+    z = rng.normal(0, 3.0, size=(B, V))
+    z[:, rng.choice(V, size=200, replace=False)] += 8.0
+    rows = W.to_storage(z, dtype)
+    temps = np.tile([0.05, 0.1, 0.25, 1.5, 3.0, 10.0], B // 6).astype(np.float32)
+    say(f"draft temperature range dtype={dtype}")
+    check(rows, dtype, temps, 777, 1)
+
+
 @pytest.mark.parametrize("B", [127, 128])
 def test_draft_chunk_length_switch(B):
     """Either side of the batch size where the sampler moves from 4 KiB to 8 KiB

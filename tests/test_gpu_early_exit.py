@@ -92,6 +92,18 @@ def test_early_exit_ragged(dtype, V):
     check(bt, run_ee(bt), oracle.verify_batch(bt))
 
 
+@pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
+def test_early_exit_temperature_range(dtype):
+    """Temperatures from 0.05 to 10 on N(0, 9) logits, |z| / T up to about 250."""
+    rng = np.random.default_rng(91 + dtype)
+    B, V = 48, 20011
+    temps = np.tile([0.05, 0.1, 0.25, 1.5, 3.0, 10.0], B // 6)
+    ks = [int(x) for x in rng.integers(1, 9, size=B)]
+    bt = W.make_custom_batch(rng, dtype, V, ks, temps, seed=502, max_k=8)
+    say(f"early exit temperature range dtype={dtype}")
+    check(bt, run_ee(bt), oracle.verify_batch(bt))
+
+
 def test_early_exit_faults():
     """Bad offsets, tokens and temperatures, and a bad row at position 0, fail alone."""
     rng = np.random.default_rng(19)

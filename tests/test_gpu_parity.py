@@ -134,11 +134,12 @@ def test_large_vocab(dtype, V):
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
 def test_temperature_range(dtype):
-    """Temperatures from 0.25 to 10 (1.5 is the lesson's exercise value): the
-    1e-5 bound on p and q holds while |z| / T stays below about 100."""
+    """Temperatures from 0.05 to 10 (1.5 is the lesson's exercise value) on
+    N(0, 9) logits (row maxima near 12, so |z| / T reaches about 250): the 1e-5
+    bound on p and q holds throughout (exponents are formed from z - max)."""
     rng = np.random.default_rng(77 + dtype)
     B, V = 48, 20011
-    temps = np.tile([0.25, 1.5, 3.0, 10.0], B // 4)
+    temps = np.tile([0.05, 0.1, 0.25, 1.5, 3.0, 10.0], B // 6)
     ks = [int(x) for x in rng.integers(1, 9, size=B)]
     b = W.make_custom_batch(rng, dtype, V, ks, temps, seed=501, max_k=8)
     say(f"temperature range dtype={dtype}")
