@@ -86,6 +86,10 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="no GPU: per-kernel dispatch durations (count, mean, median, "
                          "min, max) from a rocprofv3 --kernel-trace -f csv run")
+    ap.add_argument("--stage-trace", action="store_true",
+                    help="per-stage timeline of the verify kernel on --workload, from its "
+                         "stage-trace build (libspecverify_trace.so): --steps traced calls "
+                         "after --warmup untraced ones; prints a summary, no JSON line")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -299,6 +303,149 @@ def summarize_trace(args):
         a = np.array(d)
         print(f"{name[:60]:60s} {a.size:6d} {a.mean():9.2f} {np.median(a):9.2f} {a.min():9.2f} "
               f"{a.max():9.2f}")
+
+
+def stage_trace(args):
+    """Per-stage timeline of sv_verify from the stage-trace build.
+
+    Each workgroup of the trace build records its role and the wall clock at
+    numbered stages (spec_verify.hip, SV_STAMP): statistics workgroups at
+    start, scalars loaded, partials stored (and, for a greedy request's
+    finisher, partials folded and outputs written); race workgroups at start,
+    scalars loaded, last partial seen, partials folded, ratio tests done,
+    chunks raced, winner stored, and the finisher at winners collected and
+    outputs written.  Times are per call, from the first workgroup's start,
+    averaged over the traced calls; a sampled request's chain is measured from
+    the last store of its partials."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_scaled_amd import binding
+    from rejection_sampling_verify_scaled_amd import build as hip_build
+    from rejection_sampling_verify_scaled_amd import workloads as W
+
+    if not os.path.exists(hip_build.LIB_TRACE):
+        raise SystemExit(f"{hip_build.LIB_TRACE} is missing: build it with "
+                         "`python -m rejection_sampling_verify_scaled_amd.build --all`")
+    lib = binding.load_library(hip_build.LIB_TRACE)
+    lib.spec_verify_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.spec_verify_trace_copy.restype = ctypes.c_int
+    lib.spec_verify_trace_reset.restype = ctypes.c_int
+    lib.spec_verify_trace_points.restype = ctypes.c_int
+    npts = lib.spec_verify_trace_points()
+    hip = Hip()
+    khz = ctypes.c_int()
+    hip.lib.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                              ctypes.c_int]
+    HIP_ATTR_WALL_CLOCK_RATE = 10017  # hipDeviceAttributeWallClockRate (hip_runtime_api.h)
+    if hip.lib.hipDeviceGetAttribute(ctypes.byref(khz), HIP_ATTR_WALL_CLOCK_RATE, 0) != 0:
+        raise SystemExit("hipDeviceGetAttribute(wall clock rate) failed")
+    us_per_tick = 1e3 / khz.value
+    dev = torch.device("cuda:0")
+    batch = W.make_batch(args.workload, 0)
+    d = binding.to_device_batch(batch, dev)
+    per_copy = d["target"].numel() * d["target"].element_size() + \
+        d["draft"].numel() * d["draft"].element_size()
+    copies = args.copies or max(1, math.ceil(1.25e9 / per_copy))
+    targets = [d["target"]] + [d["target"].clone() for _ in range(copies - 1)]
+    drafts = [d["draft"]] + [d["draft"].clone() for _ in range(copies - 1)]
+    ws = binding.new_workspace(batch.B, batch.V, batch.max_k)
+
+    def call(c):
+        binding.spec_verify_sample(targets[c], drafts[c], d["offsets"], d["tokens"],
+                                   d["temperature"], batch.seed, batch.max_k, workspace=ws,
+                                   lib=lib)
+
+    for i in range(args.warmup):
+        call(i % copies)
+    torch.cuda.synchronize()
+    n_words = (1 << 16) * npts
+    buf = np.zeros(n_words, dtype=np.uint64)
+    rows = []
+    for i in range(args.steps):
+        if lib.spec_verify_trace_reset() != 0:
+            raise SystemExit("trace reset failed")
+        call(i % copies)
+        torch.cuda.synchronize()
+        if lib.spec_verify_trace_copy(buf.ctypes.data_as(ctypes.c_void_p), n_words) != 0:
+            raise SystemExit("trace copy failed")
+        rows.append(trace_summary(buf.reshape(-1, npts).copy(), batch, us_per_tick))
+    keys = rows[0].keys()
+    print(f"stage timeline of sv_verify, workload {args.workload} ({W.WORKLOADS[args.workload].name}),"
+          f" {args.steps} traced calls after {args.warmup} untraced; trace build "
+          f"(-DSV_TRACE); us, mean over calls")
+    for k in keys:
+        vals = [r[k] for r in rows if r.get(k) is not None]
+        if vals:
+            print(f"  {k:58s} {np.mean(vals):8.2f}   (min {np.min(vals):7.2f}, max {np.max(vals):7.2f})")
+
+
+def trace_summary(rec, batch, us_per_tick) -> dict:
+    """One traced call's stage figures (see stage_trace)."""
+    import numpy as np
+    head = rec[:, 0]
+    live = head != 0
+    rec, head = rec[live], head[live]
+    kind = (head & 0xFF).astype(int)
+    req = ((head >> 8) & 0xFFFFFF).astype(int)
+    st = rec.astype(np.int64)
+    t0 = st[:, 1][st[:, 1] > 0].min()
+
+    def us(x):
+        return (x - t0) * us_per_tick
+
+    out = {}
+    ends = st[:, 1:].max(axis=1)
+    out["kernel span (first start to last stamp)"] = us(ends.max())
+    s_m = kind == 1
+    out["statistics workgroup: scalars loaded after start"] = float(
+        np.mean((st[s_m, 2] - st[s_m, 1]) * us_per_tick)) if s_m.any() else None
+    out["statistics workgroup: partials stored after start"] = float(
+        np.mean((st[s_m & (st[:, 3] > 0), 3] - st[s_m & (st[:, 3] > 0), 1]) * us_per_tick))
+    out["last partial stored (all requests)"] = us(st[s_m, 3].max())
+    chain = {k: [] for k in ("seen", "fold", "ratio", "race", "winners", "collected", "outputs",
+                             "race_start", "last_stats")}
+    greedy_tail = []
+    for b in range(batch.B):
+        sb = s_m & (req == b)
+        if not sb.any():
+            continue
+        last = st[sb, 3].max()
+        rb = (kind == 2) & (req == b)
+        if batch.temperature[b] > 0 and rb.any():
+            r = st[rb]
+            fin = r[r[:, 9] > 0]
+            if len(fin) == 0:
+                continue
+            chain["last_stats"].append(us(last))
+            chain["race_start"].append(float(np.median(r[:, 1]) - last) * us_per_tick)
+            chain["seen"].append(float(np.median(r[:, 3]) - last) * us_per_tick)
+            chain["fold"].append(float(np.median(r[:, 4]) - np.median(r[:, 3])) * us_per_tick)
+            chain["ratio"].append(float(np.median(r[:, 5]) - np.median(r[:, 4])) * us_per_tick)
+            chain["race"].append(float(r[:, 6].max() - np.median(r[:, 5])) * us_per_tick)
+            chain["winners"].append(float(r[:, 7].max() - r[:, 6].max()) * us_per_tick)
+            chain["collected"].append(float(fin[0, 8] - r[:, 7].max()) * us_per_tick)
+            chain["outputs"].append(float(fin[0, 9] - fin[0, 8]) * us_per_tick)
+        elif batch.temperature[b] == 0:
+            f = st[sb & (st[:, 5] > 0)]
+            if len(f):
+                greedy_tail.append((f[0, 5] - last) * us_per_tick)
+    if chain["seen"]:
+        out["sampled: last partial stored (mean over requests)"] = float(np.mean(chain["last_stats"]))
+        out["sampled: race workgroup start, from the last partial"] = float(np.mean(chain["race_start"]))
+        out["sampled: last partial seen by the race workgroups"] = float(np.mean(chain["seen"]))
+        out["sampled: partials folded"] = float(np.mean(chain["fold"]))
+        out["sampled: ratio tests done (z(x_t) gathers)"] = float(np.mean(chain["ratio"]))
+        out["sampled: row n loaded and raced (slowest workgroup)"] = float(np.mean(chain["race"]))
+        out["sampled: winners stored"] = float(np.mean(chain["winners"]))
+        out["sampled: finisher collected the winners"] = float(np.mean(chain["collected"]))
+        out["sampled: outputs written"] = float(np.mean(chain["outputs"]))
+        total = [sum(x) for x in zip(chain["seen"], chain["fold"], chain["ratio"], chain["race"],
+                                     chain["winners"], chain["collected"], chain["outputs"])]
+        out["sampled: chain, last partial to outputs"] = float(np.mean(total))
+    if greedy_tail:
+        out["greedy: last partial to outputs (finisher)"] = float(np.mean(greedy_tail))
+    return out
 
 
 def bench_draft(args):
@@ -587,6 +734,11 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.stage_trace:
+        if args.gpus != 1:
+            raise SystemExit("bench.py measures one GPU")
+        stage_trace(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

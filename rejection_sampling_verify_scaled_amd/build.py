@@ -22,6 +22,10 @@ LIB = os.path.join(PKG, "libspecverify.so")
 # only the requests they could not finish (never loaded by the product path).
 LIB_SPIN0 = os.path.join(PKG, "libspecverify_spin0.so")
 SPIN0_FLAGS = ("-DSV_SPIN_LIMIT=0u",)
+# The same sources with the verify kernel's stage timestamps compiled in
+# (SV_TRACE): a measurement build for `bench.py --stage-trace`.
+LIB_TRACE = os.path.join(PKG, "libspecverify_trace.so")
+TRACE_FLAGS = ("-DSV_TRACE",)
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -56,15 +60,16 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
 
 
 def build_all(verbose: bool = False) -> None:
-    """The product library and the expired-wait test build."""
+    """The product library, the expired-wait test build and the stage-trace build."""
     build(verbose=verbose)
     build(out=LIB_SPIN0, extra=SPIN0_FLAGS, verbose=verbose)
+    build(out=LIB_TRACE, extra=TRACE_FLAGS, verbose=verbose)
 
 
 if __name__ == "__main__":
     if sys.argv[1:] == ["--all"]:
         build_all(verbose=True)
-        print(LIB, LIB_SPIN0)
+        print(LIB, LIB_SPIN0, LIB_TRACE)
     else:
         build(verbose=True, extra=sys.argv[1:])
         print(LIB)

@@ -77,6 +77,35 @@ constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
 // five waves per SIMD, so five 4-wave workgroups per CU).
 constexpr int kWorkgroupsPerCu = 5;
 
+// Stage timestamps (a build with SV_TRACE defined only; the product build
+// compiles them out).  Workgroup g records its role in word 0 of its record
+// (kind | request << 8 | group << 32; kind 1: statistics, 2: race) and the
+// wall clock (hipDeviceAttributeWallClockRate) at numbered stages in words
+// 1..kTracePoints - 1; spec_verify_trace_copy reads the records back.
+#ifdef SV_TRACE
+constexpr int kTraceWgs = 1 << 16, kTracePoints = 10;
+__device__ uint64_t sv_trace[kTraceWgs * kTracePoints];
+#define SV_TRACE_HEAD(kind, b, grp)                                                      \
+  do {                                                                                   \
+    if (threadIdx.x == 0 && blockIdx.x < kTraceWgs)                                      \
+      sv_trace[blockIdx.x * kTracePoints] = static_cast<uint64_t>(kind) |                \
+                                            (static_cast<uint64_t>(b) << 8) |            \
+                                            (static_cast<uint64_t>(grp) << 32);          \
+  } while (0)
+#define SV_STAMP(i)                                                                      \
+  do {                                                                                   \
+    if (threadIdx.x == 0 && blockIdx.x < kTraceWgs)                                      \
+      sv_trace[blockIdx.x * kTracePoints + (i)] = wall_clock64();                        \
+  } while (0)
+#else
+#define SV_TRACE_HEAD(kind, b, grp) \
+  do {                              \
+  } while (0)
+#define SV_STAMP(i) \
+  do {              \
+  } while (0)
+#endif
+
 // ------------------------------------------------------------------ parameters
 
 struct Params {
@@ -222,7 +251,9 @@ __device__ void stats_items(const Params& p, int b, const Req& r, int cg, float 
 // Statistics of request b over the chunks of group cg.
 template <bool BF16, bool VEC>
 __device__ void stats_part(const Params& p, int b, int cg) {
+  SV_TRACE_HEAD(1, b, cg);
   const Req r = load_req(p, b);
+  SV_STAMP(2);  // the request's scalars loaded
   const int tid = threadIdx.x;
   if (!r.valid()) {
     if (cg == 0) {
@@ -235,6 +266,7 @@ __device__ void stats_part(const Params& p, int b, int cg) {
   }
   if (r.greedy) {
     stats_items<BF16, VEC, true>(p, b, r, cg, 0.f);
+    SV_STAMP(3);  // partials stored
     // the request's last workgroup with items finishes it (flat grouping
     // leaves the groups past a greedy request's (K+1) nc items empty)
     const int last = p.flat ? static_cast<int>(ceil_div_dev((r.K + 1) * p.nc, kGroupItems)) - 1
@@ -242,6 +274,7 @@ __device__ void stats_part(const Params& p, int b, int cg) {
     if (cg == last) finish_greedy(p, b, r);
   } else {
     stats_items<BF16, VEC, false>(p, b, r, cg, kLog2e / r.T);
+    SV_STAMP(3);  // partials stored
   }
 }
 
@@ -279,6 +312,7 @@ __device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, Fo
     // re-polling all their partials would load the memory system that the
     // statistics stream through.
     if (tid == 0) slot_wait(part_slot(p, b, row_slot(p, K, nrows - 1), p.nc - 1));
+    SV_STAMP(3);  // race: the request's last partial seen
   }
   for (int cblk = 0; cblk < p.nc; cblk += kFoldChunks) {
     const int ncb = min(kFoldChunks, p.nc - cblk);
@@ -382,6 +416,7 @@ __device__ void finish_greedy(const Params& p, int b, const Req& r) {
     bad_token = x < 0 || x >= p.V;
   }
   fold_rows<true>(p, b, K, K + 1, 0.f, sh);
+  SV_STAMP(4);  // greedy finisher: partials folded
   const bool any_bad_token = __syncthreads_or(bad_token);
   clear_request(p, b, K, K + 1);
   if (sh.bad & 2) {
@@ -407,6 +442,7 @@ __device__ void finish_greedy(const Params& p, int b, const Req& r) {
     if (p.q_at) p.q_at[r.off0 + tid] = NAN;
   }
   if (tid == 0) p.accept_len[b] = n;
+  SV_STAMP(5);  // greedy outputs written
 }
 
 // ------------------------------------------------------------------ race
@@ -630,6 +666,7 @@ __device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t 
     }
   }
   fold_rows<false>(p, b, K, 2 * K + 1, cf, sh);
+  SV_STAMP(4);  // race: partials folded
   const bool any_bad_token = __syncthreads_or(bad_token) != 0;
   const bool bad = (sh.bad & 1) || any_bad_token;
   const bool expired = (sh.bad & 2) != 0;
@@ -658,6 +695,7 @@ __device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t 
     __syncthreads();
     // workgroup-uniform values read from LDS: keep them in scalar registers
     rr.n = uniform_int(sh_n);
+    SV_STAMP(5);  // race: ratio tests done, n known
     rr.mp = uniform_float(sh.row_m[rr.n]);
     rr.lsp = uniform_float(sh.row_ls[rr.n]);
     if (rr.n < K) {
@@ -682,10 +720,12 @@ __device__ void race_part(const Params& p, int b, int cg, const Req& r, int32_t 
       for (; c < c_end; ++c) race_chunk<BF16, VEC, false>(p, b, c, prow, nullptr, rr, key, idx);
     }
   }
+  SV_STAMP(6);  // race: this workgroup's chunks raced
   block_argmax(key, idx, sh_key, sh_idx);
   if (tid == 0)
     slot_store(p.race + static_cast<int64_t>(b) * p.ngr + cg,
                pack_slot(key, expired ? kExpiredIdx : static_cast<uint32_t>(idx)));
+  SV_STAMP(7);  // race: winner stored
   // the request's last race workgroup finishes it
   if (cg == p.ngr - 1) finish_sampled<BF16, VEC>(p, b, r, rr, bad, expired, x);
 }
@@ -715,6 +755,7 @@ __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceR
     merge_argmax(key, idx, slot_f(v), static_cast<int>(slot_w(v)));
   }
   block_argmax(key, idx, sh_key, sh_idx);  // its barriers also publish sh_expired
+  SV_STAMP(8);  // finisher: every winner collected
   clear_request(p, b, r.K, 2 * r.K + 1);
   if (sh_expired) {
     if (tid == 0) p.accept_len[b] = -1;
@@ -745,6 +786,7 @@ __device__ void finish_sampled(const Params& p, int b, const Req& r, const RaceR
   const int n = rr.n;
   if (tid <= r.K) p.out_tokens[trow0 + tid] = (tid < n) ? x : (tid == n ? idx : -1);
   if (tid == 0) p.accept_len[b] = n;
+  SV_STAMP(9);  // finisher: outputs written
 }
 
 // ------------------------------------------------------------------ kernel
@@ -778,12 +820,15 @@ __global__ __launch_bounds__(kThreads) void sv_verify(Params p) {
     b2 = p.B - L + t / p.ngr;
     rc = t - (b2 - (p.B - L)) * p.ngr;
   }
+  SV_STAMP(1);  // workgroup started
   // the race request's draft tokens, loaded before anything waits
   Req r2{};
   bool race = false;
   int32_t x = 0;
   if (b2 >= 0 && b2 < p.B) {
+    SV_TRACE_HEAD(2, b2, rc);
     r2 = load_req(p, b2);
+    SV_STAMP(2);  // the request's scalars loaded
     race = r2.sampled();
     if (race && static_cast<int>(threadIdx.x) < r2.K) x = p.tokens[r2.off0 + threadIdx.x];
   }
@@ -1056,6 +1101,24 @@ int spec_verify_sample_static(const void* target_logits, const void* draft_logit
                   draft_tokens, temperature, seed, accept_len, out_tokens, p_at_draft,
                   q_at_draft, ws, kScratchBytes, stream, false, nullptr, nullptr);
 }
+
+#ifdef SV_TRACE
+// Trace build only (not part of the product ABI): copy the first n_words
+// words of the stage records to host memory, or zero them all (reset).
+int spec_verify_trace_copy(uint64_t* host, size_t n_words) {
+  n_words = std::min(n_words, static_cast<size_t>(kTraceWgs) * kTracePoints);
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(sv_trace), n_words * sizeof(uint64_t)) ==
+                 hipSuccess
+             ? 0
+             : -1;
+}
+int spec_verify_trace_reset(void) {
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(sv_trace)) != hipSuccess) return -1;
+  return hipMemset(ptr, 0, sizeof(uint64_t) * kTraceWgs * kTracePoints) == hipSuccess ? 0 : -1;
+}
+int spec_verify_trace_points(void) { return kTracePoints; }
+#endif
 
 const char* spec_verify_status_string(int status) {
   switch (status) {
