@@ -83,6 +83,9 @@ def parse():
                     help="no GPU: turn two rocprofv3 --pmc runs of --traffic-probe (FETCH_SIZE, "
                          "then WRITE_SIZE, -f csv) into the traffic record of --op on "
                          "--workload under profiles/, and print the summary")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="no GPU: per-kernel mean of every counter per dispatch in a "
+                         "rocprofv3 --pmc -f csv run")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="no GPU: per-kernel dispatch durations (count, mean, median, "
                          "min, max) from a rocprofv3 --kernel-trace -f csv run")
@@ -165,15 +168,15 @@ def traffic_record(workload: int, kernel: str = "sv_verify", sources=None):
     return rec.get("hbm_bytes_per_launch")
 
 
-# VALU issue slots per token of the draft sampler (quarter-rate exp / log count
-# 4, a full-rate op 1), from its formulation: a sampled token costs a quarter
-# of a Philox4x32-10 call (10 rounds of two 32x32->64 products and two
-# three-input xors: 10 slots), the uniform map (2), -log2 U (4), the weight's
-# fma and exp2 (5), the sum (1), the cross-multiplied comparison with its
-# three selects (6) and unpack + max (2): 30.  A greedy token: unpack + max
-# and its share of the argmax search: 2.
-DRAFT_SLOTS_SAMPLED = 30
-DRAFT_SLOTS_GREEDY = 2
+# VALU lane slots per token of the draft sampler, from the instructions the
+# kernel issues (SQ_INSTS_VALU x 64 per dispatch, profiles/sd_sample_*_valu.txt):
+# a sampled token takes 36.5 (bf16) or 31.7 (fp32) -- a quarter Philox4x32-10
+# call, the uniform map, -log2 U, the weight's exponent and exp2, the sum, the
+# cross-multiplied comparison, unpacking and the maximum, plus loop and
+# reduction overhead -- and a greedy token about 1.5 (unpack, maximum and its
+# share of the argmax search).
+DRAFT_SLOTS_SAMPLED = {True: 36.5, False: 31.7}  # keyed by "rows are bf16"
+DRAFT_SLOTS_GREEDY = 1.5
 # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: full-rate 32-bit VALU lane slots / s
 PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
 
@@ -288,6 +291,24 @@ def summarize_counters(args):
     if args.op != "early-exit":
         print(f"  algorithmic bytes per launch: {alg / 1e6:.2f} MB; measured / algorithmic = "
               f"{(fetch + write) / alg:.3f}")
+
+
+def summarize_pmc(args):
+    """Per-kernel mean of each counter per dispatch (values summed over the
+    counter's dimensions within a dispatch)."""
+    import numpy as np
+    rows = _csv_rows(args.summarize_pmc, "counter_collection.csv")
+    per = {}
+    for r in rows:
+        key = (int(r["Dispatch_Id"]), kernel_base_name(r["Kernel_Name"]), r["Counter_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by = {}
+    for (_, name, counter), v in per.items():
+        by.setdefault((name, counter), []).append(v)
+    print(f"{'kernel':32s} {'counter':28s} {'dispatches':>10s} {'mean':>16s} {'median':>16s}")
+    for (name, counter), v in sorted(by.items()):
+        a = np.array(v)
+        print(f"{name[:32]:32s} {counter[:28]:28s} {a.size:10d} {a.mean():16.1f} {np.median(a):16.1f}")
 
 
 def summarize_trace(args):
@@ -499,7 +520,8 @@ def bench_draft(args):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / args.steps * 1e3
     n_s = int((batch.temperature > 0).sum())
-    slots = (n_s * DRAFT_SLOTS_SAMPLED + (B - n_s) * DRAFT_SLOTS_GREEDY) * V
+    slots = (n_s * DRAFT_SLOTS_SAMPLED[batch.dtype == W.DTYPE_BF16] +
+             (B - n_s) * DRAFT_SLOTS_GREEDY) * V
     achieved = slots / (us * 1e-6)
     call(0)
     torch.cuda.synchronize()
@@ -734,6 +756,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args)
         return
     if args.stage_trace:
         if args.gpus != 1:
