@@ -451,6 +451,15 @@ def trace_summary(rec, batch, us_per_tick) -> dict:
             f = st[sb & (st[:, 5] > 0)]
             if len(f):
                 greedy_tail.append((f[0, 5] - last) * us_per_tick)
+    # what ends the kernel: the latest sampled outputs against the latest greedy outputs
+    s_out = st[(kind == 2) & (st[:, 9] > 0), 9]
+    g_out = st[(kind == 1) & (st[:, 5] > 0), 5]
+    if len(s_out):
+        out["sampled: last request's outputs written"] = us(s_out.max())
+        out["sampled: last request's statistics complete"] = float(np.max(chain["last_stats"])) \
+            if chain["last_stats"] else None
+    if len(g_out):
+        out["greedy: last request's outputs written"] = us(g_out.max())
     if chain["seen"]:
         out["sampled: last partial stored (mean over requests)"] = float(np.mean(chain["last_stats"]))
         out["sampled: race workgroup start, from the last partial"] = float(np.mean(chain["race_start"]))
