@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="no GPU: per-kernel dispatch durations (count, mean, median, "
                          "min, max) from a rocprofv3 --kernel-trace -f csv run")
+    ap.add_argument("--valu-rates", action="store_true",
+                    help="issue cycles per wave64 instruction of the VALU classes the "
+                         "samplers use, from libspecverify_rates.so; prints a summary")
     ap.add_argument("--stage-trace", action="store_true",
                     help="per-stage timeline of the verify kernel on --workload, from its "
                          "stage-trace build (libspecverify_trace.so): --steps traced calls "
@@ -168,17 +171,36 @@ def traffic_record(workload: int, kernel: str = "sv_verify", sources=None):
     return rec.get("hbm_bytes_per_launch")
 
 
-# VALU lane slots per token of the draft sampler, from the instructions the
-# kernel issues (SQ_INSTS_VALU x 64 per dispatch, profiles/sd_sample_*_valu.txt):
-# a sampled token takes 36.5 (bf16) or 31.7 (fp32) -- a quarter Philox4x32-10
-# call, the uniform map, -log2 U, the weight's exponent and exp2, the sum, the
-# cross-multiplied comparison, unpacking and the maximum, plus loop and
-# reduction overhead -- and a greedy token about 1.5 (unpack, maximum and its
-# share of the argmax search).
-DRAFT_SLOTS_SAMPLED = {True: 36.5, False: 31.7}  # keyed by "rows are bf16"
+# VALU issue of the draft sampler.  A gfx950 SIMD issues a full-rate 32-bit
+# wave64 instruction (fma, add, xor, compare, select) in 2 cycles: 32 lanes per
+# cycle, the rate behind the published 157.3 TFLOP/s fp32.  `bench.py
+# --valu-rates` measures (profiles/valu_issue_rates.txt) 2.34 cycles for such
+# an instruction, 8.8 for a transcendental (v_exp_f32, v_log_f32) and 5.4 for
+# v_mad_u64_u32 (Philox's 32 x 32 -> 64 product, counted in SQ_INSTS_VALU_INT64).
+# Costs below are in full-rate lane slots: 1 for a full-rate instruction, 3.8
+# for a transcendental and 2.3 for a 64-bit integer instruction.
+VALU_SLOTS_TRANS = 3.8
+VALU_SLOTS_INT64 = 2.3
+# Per sampled token the kernel issues (counters SQ_INSTS_VALU,
+# SQ_INSTS_VALU_TRANS_F32 and SQ_INSTS_VALU_INT64 per dispatch, over the
+# tokens; profiles/sd_sample_*_valu.txt) 36.5 (bf16) or 31.7 (fp32) VALU
+# instructions per lane, of which 2.2 are transcendental (the exp2 of the
+# weight, the log2 of -log2 U, and a share of the finisher's) and 4.84 are
+# 64-bit integer (a Philox4x32-10 call has 18.1 v_mad_u64_u32 for 4 tokens:
+# the first round's product of a uniform counter word is scalar).  The rest
+# are full rate: the uniform map, the weight's exponent, the sum, the
+# cross-multiplied comparison, unpacking and the maximum, loop and reduction
+# overhead.  A greedy token takes about 1.5 full-rate instructions (unpack,
+# maximum and its share of the argmax search).
+DRAFT_INSTS_SAMPLED = {True: 36.5, False: 31.7}  # keyed by "rows are bf16"
+DRAFT_TRANS_PER_TOKEN = 2.2
+DRAFT_INT64_PER_TOKEN = 4.84
+DRAFT_SLOTS_SAMPLED = {
+    bf: n - DRAFT_TRANS_PER_TOKEN - DRAFT_INT64_PER_TOKEN + DRAFT_TRANS_PER_TOKEN * VALU_SLOTS_TRANS
+    + DRAFT_INT64_PER_TOKEN * VALU_SLOTS_INT64 for bf, n in DRAFT_INSTS_SAMPLED.items()}
 DRAFT_SLOTS_GREEDY = 1.5
-# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: full-rate 32-bit VALU lane slots / s
-PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
+# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz: full-rate 32-bit VALU lane slots / s
+PEAK_VALU_SLOTS = 256 * 4 * 32 * 2.4e9
 
 
 def host_description() -> dict:
@@ -324,6 +346,65 @@ def summarize_trace(args):
         a = np.array(d)
         print(f"{name[:60]:60s} {a.size:6d} {a.mean():9.2f} {np.median(a):9.2f} {a.min():9.2f} "
               f"{a.max():9.2f}")
+
+
+VALU_RATE_OPS = (  # (label, VALU instructions per loop body, the body)
+    ("fma", 1, "v_fma_f32"),
+    ("exp2", 1, "v_exp_f32"),
+    ("log2", 1, "v_log_f32"),
+    ("mad64", 2, "v_mad_u64_u32 + v_add_u32"),
+    ("mul_lo", 2, "v_mul_lo_u32 + v_add_u32"),
+    ("xor_add", 2, "v_xor_b32 + v_add_u32"),
+)
+
+
+def valu_rates():
+    """Issue cycles per wave64 instruction on one SIMD for the VALU classes the
+    samplers use (csrc/valu_rates.hip): each probe runs 16 independent chains
+    of one operation per thread, 8 workgroups of 256 threads per CU; its rate
+    is stated per SIMD and shader clock cycle, with the shader clock read by
+    the probe itself.  The add that completes the two-instruction bodies is
+    taken at the xor + add probe's cost per instruction."""
+    import torch
+
+    from rejection_sampling_verify_scaled_amd import build as hip_build
+    if not torch.cuda.is_available():
+        raise SystemExit("--valu-rates needs a HIP GPU")
+    if not os.path.exists(hip_build.LIB_RATES):
+        raise SystemExit(f"{hip_build.LIB_RATES} is missing: build it with "
+                         "`python -m rejection_sampling_verify_scaled_amd.build --all`")
+    lib = ctypes.CDLL(hip_build.LIB_RATES)
+    lib.sv_valu_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                 ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double)]
+    lib.sv_valu_rate.restype = ctypes.c_int
+    hip = Hip()
+    khz = ctypes.c_int()
+    hip.lib.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                              ctypes.c_int]
+    HIP_ATTR_WALL_CLOCK_RATE = 10017  # hipDeviceAttributeWallClockRate (hip_runtime_api.h)
+    if hip.lib.hipDeviceGetAttribute(ctypes.byref(khz), HIP_ATTR_WALL_CLOCK_RATE, 0) != 0:
+        raise SystemExit("hipDeviceGetAttribute(wall clock rate) failed")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    simds = 4 * cus
+    res = {}
+    for op, (label, n_inst, body) in enumerate(VALU_RATE_OPS):
+        ms, bodies, mhz = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
+        if lib.sv_valu_rate(op, cus, khz.value / 1e3, ctypes.byref(ms), ctypes.byref(bodies),
+                            ctypes.byref(mhz)) != 0:
+            raise SystemExit(f"sv_valu_rate({op}) failed")
+        rate = bodies.value / (ms.value * 1e-3)                  # loop bodies per second
+        per_simd_cycle = rate / (simds * mhz.value * 1e6)       # lane bodies per SIMD cycle
+        res[label] = (n_inst, body, ms.value, rate, mhz.value, 64.0 / per_simd_cycle)
+    add_cycles = res["xor_add"][5] / 2
+    print(f"VALU issue rates on {cus} CUs ({simds} SIMDs); cycles per wave64 instruction "
+          f"on one SIMD at the shader clock the probe saw")
+    print(f"  {'probe':8s} {'loop body':28s} {'ms':>7s} {'T bodies/s':>11s} {'MHz':>6s} "
+          f"{'cycles/body':>11s} {'cycles/instr':>12s}")
+    for label, (n_inst, body, ms, rate, mhz, cyc) in res.items():
+        own = cyc if n_inst == 1 else (cyc / 2 if label == "xor_add" else cyc - add_cycles)
+        print(f"  {label:8s} {body:28s} {ms:7.3f} {rate / 1e12:11.2f} {mhz:6.0f} {cyc:11.2f} "
+              f"{own:12.2f}")
 
 
 def stage_trace(args):
@@ -545,7 +626,7 @@ def bench_draft(args):
                    "sampled_rows": n_s, "greedy_rows": B - n_s, "input_copies_rotated": copies},
         "kernel_us": {"sd_sample": us},
         "roofline": {"bound": "alu", "achieved": achieved / 1e12, "peak": PEAK_VALU_SLOTS / 1e12,
-                     "unit": "T VALU lane-slots/s", "frac": achieved / PEAK_VALU_SLOTS,
+                     "unit": "T full-rate VALU lane-slots/s", "frac": achieved / PEAK_VALU_SLOTS,
                      "traffic": None, "kernel": "sd_sample"},
         "hbm_gbs": per_copy / (us * 1e-6) / 1e9,
         "hbm_frac": per_copy / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
@@ -768,6 +849,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.valu_rates:
+        valu_rates()
         return
     if args.stage_trace:
         if args.gpus != 1:

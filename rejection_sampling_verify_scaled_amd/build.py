@@ -26,6 +26,10 @@ SPIN0_FLAGS = ("-DSV_SPIN_LIMIT=0u",)
 # (SV_TRACE): a measurement build for `bench.py --stage-trace`.
 LIB_TRACE = os.path.join(PKG, "libspecverify_trace.so")
 TRACE_FLAGS = ("-DSV_TRACE",)
+# Issue rates of the VALU instruction classes the samplers use: a measurement
+# library of its own for `bench.py --valu-rates` (not part of the verify path).
+LIB_RATES = os.path.join(PKG, "libspecverify_rates.so")
+RATES_SRC = os.path.join(PKG, "csrc", "valu_rates.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -48,10 +52,10 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
+def build(out: str = LIB, extra=(), verbose: bool = False, srcs=None) -> str:
     """Compile the HIP sources to ``out`` (a fresh temp file renamed into place)."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", "-o", tmp, *SRCS]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", "-o", tmp, *(srcs or SRCS)]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -60,16 +64,18 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
 
 
 def build_all(verbose: bool = False) -> None:
-    """The product library, the expired-wait test build and the stage-trace build."""
+    """The product library, the expired-wait test build, the stage-trace build
+    and the VALU issue-rate library."""
     build(verbose=verbose)
     build(out=LIB_SPIN0, extra=SPIN0_FLAGS, verbose=verbose)
     build(out=LIB_TRACE, extra=TRACE_FLAGS, verbose=verbose)
+    build(out=LIB_RATES, verbose=verbose, srcs=[RATES_SRC])
 
 
 if __name__ == "__main__":
     if sys.argv[1:] == ["--all"]:
         build_all(verbose=True)
-        print(LIB, LIB_SPIN0, LIB_TRACE)
+        print(LIB, LIB_SPIN0, LIB_TRACE, LIB_RATES)
     else:
         build(verbose=True, extra=sys.argv[1:])
         print(LIB)

@@ -208,3 +208,22 @@ def test_tree_rejects_bad_arguments(lib, case):
                                      a["offs"], a["par"], a["tok"], a["acc"], a["out"], None,
                                      a["ws"], a["ws_n"], None)
     assert rc == expect
+
+
+def test_valu_rate_probe_rejects_bad_arguments():
+    """The issue-rate probe library (a measurement build) loads and refuses bad
+    arguments before any HIP call."""
+    from rejection_sampling_verify_scaled_amd import build as hip_build
+    if not os.path.exists(hip_build.LIB_RATES):
+        pytest.skip("libspecverify_rates.so is not built (build.py --all)")
+    rl = ctypes.CDLL(hip_build.LIB_RATES)
+    f = rl.sv_valu_rate
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_float),
+                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    f.restype = ctypes.c_int
+    ms, bodies, mhz = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
+    refs = (ctypes.byref(ms), ctypes.byref(bodies), ctypes.byref(mhz))
+    assert f(-1, 256, 100.0, *refs) == -1
+    assert f(6, 256, 100.0, *refs) == -1
+    assert f(0, 0, 100.0, *refs) == -1
+    assert f(0, 256, 100.0, None, None, None) == -1
