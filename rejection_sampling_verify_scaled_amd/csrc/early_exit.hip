@@ -63,6 +63,10 @@ constexpr int64_t kNarrowRaceBelow = 512;
 constexpr int kStageRows = 2;      // a stage streams target row s and draft row s
 constexpr int kDecSlots = 5;       // decision record: code, m_p, log2 S_p, m_q, log2 S_q
 constexpr uint32_t kCont = 1u, kRej = 2u, kDone = 3u;  // decision codes (low byte)
+// race slot index word of a bonus race that found its row non-finite (a NaN,
+// a +inf maximum): the request fails, as the verify step fails a row whose
+// softmax is not finite
+constexpr uint32_t kBadRowIdx = 0xFFFFFFFEu;
 
 struct EeParams {
   const void* target;
@@ -309,34 +313,42 @@ struct EeRace {
 
 // One chunk of the race held in registers (target chunk bp, draft chunk bq
 // for the residual), folded into (key, idx): keys are log2(w / e) plus the
-// chunk's weight offset, comparable across chunks.
-template <bool BF16, bool RESIDUAL>
+// weight reference, comparable across lanes and chunks.  The residual race's
+// weights use the row statistics its decision carried.  The bonus race's row
+// has no statistics pass: each lane keeps a running reference, the largest
+// logit it has seen, and moves its best weight to a new reference when that
+// grows (recomputed from the best logit, so the exponent stays an exact
+// difference); the chunk is read once.  Its chunks are checked here as well:
+// bad is set when the chunk holds a NaN or a +inf (the residual race's rows
+// were checked by their stage's statistics).
+template <bool BF16, bool RESIDUAL, int NV>
 __device__ __forceinline__ void ee_race_chunk(const uint4* bp, const uint4* bq, int64_t e0,
                                               const EeRace& rr, uint32_t b, uint32_t k0,
-                                              uint32_t k1, float& key, int& idx) {
+                                              uint32_t k1, float& key, int& idx, bool& bad) {
   constexpr int EPV = elems_per_vec(BF16);
   const int lane = threadIdx.x & 63;
-  float shift = 0.f;
-  if constexpr (!RESIDUAL) {
-    // bonus weights relative to the chunk maximum
-    float mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kItemVecs; ++u) {
-      float xs[EPV];
-      unpack<BF16>(bp[u], xs);
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) mx = fmaxf(mx, xs[k]);
-    }
-    mx = wave_max(mx);
-    shift = weight_ref(mx);
-  }
-  float bw = 0.f, be = 1.f;
+  float ref = 0.f, run = -INFINITY;  // bonus: weight reference, running maximum
+  bool nan = false;
+  float bw = 0.f, be = 1.f, bz = -INFINITY;
   int bi = INT_MAX;
 #pragma unroll
-  for (int u = 0; u < kItemVecs; ++u) {
+  for (int u = 0; u < NV; ++u) {
     float zp[EPV], zq[EPV];
     unpack<BF16>(bp[u], zp);
-    if constexpr (RESIDUAL) unpack<BF16>(bq[u], zq);
+    if constexpr (RESIDUAL) {
+      unpack<BF16>(bq[u], zq);
+    } else {
+      // (a NaN-propagating maximum: NaN if the vector holds one)
+      float vm = zp[0];
+#pragma unroll
+      for (int k = 1; k < EPV; ++k) vm = __builtin_elementwise_maximum(vm, zp[k]);
+      nan = nan || vm != vm;
+      if (vm > run) {
+        run = vm;
+        ref = weight_ref(vm);
+        bw = fast_exp2(log2_weight(bz, rr.cf, ref));  // 0 while there is no best
+      }
+    }
     const int64_t v0 = e0 + static_cast<int64_t>(u * 64 + lane) * EPV;
 #pragma unroll
     for (int h = 0; h < EPV / 4; ++h) {
@@ -349,43 +361,74 @@ __device__ __forceinline__ void ee_race_chunk(const uint4* bp, const uint4* bq, 
           w = fast_exp2(log2_weight(zp[4 * h + k], rr.cf, rr.mp) - rr.lsp) -
               fast_exp2(log2_weight(zq[4 * h + k], rr.cf, rr.mq) - rr.lsq);
         } else {
-          w = fast_exp2(log2_weight(zp[4 * h + k], rr.cf, shift));
+          w = fast_exp2(log2_weight(zp[4 * h + k], rr.cf, ref));
         }
         const float e = -fast_log2(uniform_open01(ph.w[k]));  // E / ln 2
         if (w * be > bw * e) {
           bw = w;
           be = e;
           bi = static_cast<int>(v0) + 4 * h + k;
+          if constexpr (!RESIDUAL) bz = zp[4 * h + k];
         }
       }
     }
   }
-  // (log2 keys over an absolute offset: chunks of one race share no reference)
-  float kk = bi == INT_MAX ? -INFINITY : fast_log2(bw / be) + shift * rr.cf;
+  if constexpr (!RESIDUAL) bad = bad || __ballot(nan || run == INFINITY) != 0;
+  // (log2 keys over an absolute offset: lanes and chunks share no reference)
+  float kk = bi == INT_MAX ? -INFINITY : fast_log2(bw / be) + ref * rr.cf;
   wave_merge_argmax(kk, bi);
   merge_argmax(key, idx, kk, bi);
 }
 
 template <bool BF16, bool VEC>
 __device__ void ee_race_range(const EeParams& p, int b, const EeReq& r, const EeRace& rr,
-                              int c_lo, int c_hi, float& key, int& idx) {
+                              int c_lo, int c_hi, float& key, int& idx, bool& bad) {
   constexpr int CHUNK = chunk_tokens(BF16);
   const int wave = wave_id();
   const int64_t prow = static_cast<int64_t>(r.off0) + b + rr.n;
   const int64_t qrow = static_cast<int64_t>(r.off0) + rr.n;
-  for (int c = c_lo + wave; c < c_hi; c += kWaves) {
-    uint4 bp[kItemVecs], bq[kItemVecs];
-    const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
-    load_item<BF16, VEC>(p.target, prow, p.V, e0, bp);
-    if (rr.residual) load_item<BF16, VEC>(p.draft, qrow, p.V, e0, bq);
-    if (VEC && e0 + CHUNK > p.V) {
-      mask_tail<BF16>(bp, p.V, e0);
-      if (rr.residual) mask_tail<BF16>(bq, p.V, e0);
+  if constexpr (VEC && BF16) {
+    for (int c = c_lo + wave; c < c_hi; c += kWaves) {
+      uint4 bp[kItemVecs], bq[kItemVecs];
+      const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
+      load_item<BF16, true>(p.target, prow, p.V, e0, bp);
+      if (rr.residual) load_item<BF16, true>(p.draft, qrow, p.V, e0, bq);
+      if (e0 + CHUNK > p.V) {
+        mask_tail<BF16>(bp, p.V, e0);
+        if (rr.residual) mask_tail<BF16>(bq, p.V, e0);
+      }
+      if (rr.residual)
+        ee_race_chunk<BF16, true, kItemVecs>(bp, bq, e0, rr, static_cast<uint32_t>(b), p.k0, p.k1,
+                                             key, idx, bad);
+      else
+        ee_race_chunk<BF16, false, kItemVecs>(bp, bp, e0, rr, static_cast<uint32_t>(b), p.k0,
+                                              p.k1, key, idx, bad);
     }
-    if (rr.residual)
-      ee_race_chunk<BF16, true>(bp, bq, e0, rr, static_cast<uint32_t>(b), p.k0, p.k1, key, idx);
-    else
-      ee_race_chunk<BF16, false>(bp, bp, e0, rr, static_cast<uint32_t>(b), p.k0, p.k1, key, idx);
+  } else {
+    // float32 rows and the scalar-load path take half a chunk at a time: a
+    // float32 residual race then fits five waves per SIMD (B=256 K=8: 237 ->
+    // 223 us), and the scalar path's element loads need many more registers
+    // in flight than vector loads
+    constexpr int NV = kItemVecs / 2, HALF = CHUNK / 2;
+    for (int c = c_lo + wave; c < c_hi; c += kWaves) {
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e0 = static_cast<int64_t>(c) * CHUNK + h * HALF;
+        if (e0 >= p.V) break;
+        uint4 bp[NV], bq[NV];
+        load_item<BF16, VEC, NV>(p.target, prow, p.V, e0, bp);
+        if (rr.residual) load_item<BF16, VEC, NV>(p.draft, qrow, p.V, e0, bq);
+        if (VEC && e0 + HALF > p.V) {
+          mask_tail<BF16, NV>(bp, p.V, e0);
+          if (rr.residual) mask_tail<BF16, NV>(bq, p.V, e0);
+        }
+        if (rr.residual)
+          ee_race_chunk<BF16, true, NV>(bp, bq, e0, rr, static_cast<uint32_t>(b), p.k0, p.k1, key,
+                                        idx, bad);
+        else
+          ee_race_chunk<BF16, false, NV>(bp, bp, e0, rr, static_cast<uint32_t>(b), p.k0, p.k1,
+                                         key, idx, bad);
+      }
+    }
   }
 }
 
@@ -431,10 +474,14 @@ __device__ void ee_race(const EeParams& p, int b, int s, int rc, const EeReq& r)
   }
   float key = -INFINITY;
   int idx = INT_MAX;
+  bool bad = false;
   const int c_lo = rc * p.rcw, c_hi = min(c_lo + p.rcw, p.nc);
-  ee_race_range<BF16, VEC>(p, b, r, rr, c_lo, c_hi, key, idx);
+  ee_race_range<BF16, VEC>(p, b, r, rr, c_lo, c_hi, key, idx, bad);
   block_argmax(key, idx, sh_k, sh_i);
-  if (tid == 0) slot_store(p.race + static_cast<int64_t>(b) * p.ngr + rc, pack_slot(key, static_cast<uint32_t>(idx)));
+  bad = __syncthreads_or(bad) != 0;
+  if (tid == 0)
+    slot_store(p.race + static_cast<int64_t>(b) * p.ngr + rc,
+               pack_slot(bad ? -INFINITY : key, bad ? kBadRowIdx : static_cast<uint32_t>(idx)));
   if (rc != p.ngr - 1) return;
   // the request's last race workgroup: fold the winners, write the outputs
   if (tid == 0) sh_expired = 0;
@@ -449,11 +496,21 @@ __device__ void ee_race(const EeParams& p, int b, int s, int rc, const EeReq& r)
       atomicOr(&sh_expired, 1);
       continue;
     }
+    if (slot_w(v) == kBadRowIdx) {
+      atomicOr(&sh_expired, 2);
+      continue;
+    }
     merge_argmax(key, idx, slot_f(v), static_cast<int>(slot_w(v)));
   }
-  block_argmax(key, idx, sh_k, sh_i);
-  if (sh_expired) {
+  block_argmax(key, idx, sh_k, sh_i);  // its barriers also publish sh_expired
+  if (sh_expired & 1) {
     if (tid == 0) p.accept_len[b] = -1;
+    return;
+  }
+  // a bonus row with a NaN or a +inf maximum, or with no finite maximum (no
+  // token has a positive weight), fails the request
+  if ((sh_expired & 2) || (!rr.residual && idx == INT_MAX)) {
+    ee_fault(p, b, r, true);
     return;
   }
   if (idx == INT_MAX) {
@@ -461,7 +518,8 @@ __device__ void ee_race(const EeParams& p, int b, int s, int rc, const EeReq& r)
     EeRace rb = rr;
     rb.residual = false;
     key = -INFINITY;
-    ee_race_range<BF16, VEC>(p, b, r, rb, 0, p.nc, key, idx);
+    bool unused = false;
+    ee_race_range<BF16, VEC>(p, b, r, rb, 0, p.nc, key, idx, unused);
     block_argmax(key, idx, sh_k, sh_i);
   }
   ee_outputs(p, b, r, rr.n, idx);
@@ -469,9 +527,10 @@ __device__ void ee_race(const EeParams& p, int b, int s, int rc, const EeReq& r)
 
 // ------------------------------------------------------------------ kernel
 
-// at most 128 VGPRs: four waves per SIMD (four workgroups per CU)
+// bfloat16 rows: at most 128 VGPRs, four waves per SIMD; float32 rows: at
+// most 96, five waves per SIMD (their races take half chunks)
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_verify_ee(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 5))) void sv_verify_ee(
     EeParams p) {
   const int g = blockIdx.x;
   const int per_req = p.ngs + p.ngr;

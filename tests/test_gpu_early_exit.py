@@ -123,6 +123,50 @@ def test_early_exit_faults():
     check(bt, gpu, orc)
 
 
+def test_early_exit_bad_bonus_row():
+    """A sampled request that reaches the bonus race reads target row K_b with
+    no statistics pass before it.  A NaN, a +inf or an all -inf row there fails
+    the request, as in the oracle and the full verify.  Requests 0-2 have
+    K = 0 (plain sampling from row 0).  In requests 4-6 the draft rows equal
+    the target rows, so every draft is accepted (r q < p for r < 1).
+    Requests 3 and 7 are the controls."""
+    import torch
+    from rejection_sampling_verify_scaled_amd import binding
+    rng = np.random.default_rng(23)
+    V, K = 3000, 3
+    ks = [0, 0, 0, 0, K, K, K, K]
+    for dtype in (W.DTYPE_F32, W.DTYPE_BF16):
+        bt = W.make_custom_batch(rng, dtype, V, ks, [1.0] * 8, seed=9, max_k=K)
+        for b in range(4, 8):
+            o0 = int(bt.offsets[b])
+            for t in range(K):
+                bt.draft[o0 + t] = bt.target[o0 + b + t]
+        bad = {0: ("nan", 17), 1: ("inf", 5), 2: ("ninf", None),
+               4: ("nan", 2999), 5: ("inf", 0), 6: ("ninf", None)}
+        for b, (kind, v) in bad.items():
+            row = int(bt.offsets[b]) + b + ks[b]
+            val = W.to_storage(np.array([{"nan": np.nan, "inf": np.inf}.get(kind, -np.inf)]),
+                               dtype)[0]
+            if kind == "ninf":
+                bt.target[row, :] = val
+            else:
+                bt.target[row, v] = val
+        say(f"early exit bad bonus rows dtype={dtype}")
+        orc = oracle.verify_batch(bt)
+        gpu = run_ee(bt)
+        full = binding.spec_verify_sample(*[binding.to_device_batch(bt, "cuda")[k] for k in
+                                            ("target", "draft", "offsets", "tokens",
+                                             "temperature")], bt.seed, bt.max_k)
+        torch.cuda.synchronize()
+        for b in bad:
+            assert orc["accept_len"][b] == -1, b
+            assert gpu["accept_len"][b] == -1, (b, gpu["accept_len"][b])
+            assert int(full[0][b].item()) == -1, b
+        assert orc["accept_len"][7] == K and gpu["accept_len"][7] == K
+        assert orc["accept_len"][3] == 0 and gpu["accept_len"][3] == 0
+        check(bt, gpu, orc)
+
+
 def test_early_exit_workspace_reuse():
     """Calls sharing one workspace across batch shapes give the same results, and
     every call leaves the workspace all-zero."""
