@@ -96,12 +96,11 @@ struct EeReq {
 };
 
 // Request b's scalars, checked as the verify step checks them (slice inside
-// the packed layout, K_b <= max_k, a finite non-negative temperature, draft
-// tokens inside the vocabulary); uniform, so the loads are scalar.  With
-// stage >= 0, a request whose drafts end before that stage is returned as
-// not valid without loading its tokens (its workgroups of that region only
-// exit).
-__device__ EeReq ee_req(const EeParams& p, int b, int stage = -1) {
+// the packed layout, K_b <= max_k, a finite non-negative temperature), then
+// its draft tokens (inside the vocabulary); uniform, so the loads are scalar.
+// A request whose drafts end before `stage` is not valid for that stage, and
+// its tokens are not loaded (its workgroups of that region only exit).
+__device__ EeReq ee_req_scalars(const EeParams& p, int b, int stage) {
   EeReq r;
   r.off0 = p.offsets[b];
   const int32_t off1 = p.offsets[b + 1];
@@ -110,7 +109,11 @@ __device__ EeReq ee_req(const EeParams& p, int b, int stage = -1) {
   r.greedy = r.T == 0.f;
   const bool slice_ok =
       r.off0 >= 0 && off1 <= p.n_draft_rows && off1 >= r.off0 && r.K <= p.max_k;
-  bool ok = slice_ok && r.T >= 0.f && r.T < INFINITY && stage <= r.K;
+  r.valid = slice_ok && r.T >= 0.f && r.T < INFINITY && stage <= r.K;
+  return r;
+}
+__device__ void ee_req_tokens(const EeParams& p, EeReq& r) {
+  bool ok = r.valid;
   if (ok) {
     for (int t = 0; t < r.K; ++t) {
       const int32_t x = p.tokens[r.off0 + t];
@@ -118,7 +121,6 @@ __device__ EeReq ee_req(const EeParams& p, int b, int stage = -1) {
     }
   }
   r.valid = ok;
-  return r;
 }
 
 __device__ __forceinline__ uint64_t* ee_part(const EeParams& p, int b, int s, int row, int c) {
@@ -539,7 +541,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   const int t = g - s * region;
   const int b = t / per_req;
   const int j = t - b * per_req;
-  const EeReq r = ee_req(p, b, s);
+  // A request that stopped before stage s has a stop in the record of stage
+  // s - 1 (its own decision, or one copied by publish_stop), so the
+  // workgroups of its later stages exit on that one load, issued beside the
+  // request's scalars, rather than after the token check (which waits for
+  // each token in turn).  A race workgroup still runs after a rejection at
+  // s - 1 itself.
+  const uint64_t d = s > 0 ? slot_load(ee_dec(p, b, s - 1, 0)) : 0u;
+  EeReq r = ee_req_scalars(p, b, s);
+  {
+    const uint32_t code = static_cast<uint32_t>(d), kind = code & 0xFFu;
+    const bool rejected_here = kind == kRej && static_cast<int>(code >> 8) == s - 1;
+    if (d != 0u && kind != kCont && !(j >= p.ngs && rejected_here)) return;
+  }
+  ee_req_tokens(p, r);
   if (!r.valid) {
     // (s = 0 never exceeds K_b, so region 0 sees every genuine failure)
     if (s == 0 && j == 0) {
