@@ -177,14 +177,14 @@ __device__ void ee_outputs(const EeParams& p, int b, const EeReq& r, int n, int3
 
 // ------------------------------------------------------------------ statistics of a stage
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool GREEDY>
 __device__ void ee_stats(const EeParams& p, int b, int s, int j, const EeReq& r) {
   constexpr int CHUNK = chunk_tokens(BF16);
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int nrows = r.greedy ? 1 : kStageRows;
+  const int nrows = GREEDY ? 1 : kStageRows;
   const int i_lo = j * kGroupItems;
   const int i_hi = min(i_lo + kGroupItems, nrows * p.nc);
-  const float cf = r.greedy ? 0.f : kLog2e / r.T;
+  const float cf = GREEDY ? 0.f : kLog2e / r.T;
   constexpr int IN_FLIGHT = VEC ? kItemsInFlight : 1;
   for (int i0 = i_lo + wave * IN_FLIGHT; i0 < i_hi; i0 += kWaves * IN_FLIGHT) {
     uint4 buf[IN_FLIGHT][kItemVecs];
@@ -206,8 +206,8 @@ __device__ void ee_stats(const EeParams& p, int b, int s, int j, const EeReq& r)
         const int c = i - row * p.nc;
         if (VEC && static_cast<int64_t>(c + 1) * CHUNK > p.V)
           mask_tail<BF16>(buf[k], p.V, static_cast<int64_t>(c) * CHUNK);
-        const uint64_t v = r.greedy ? item_argmax<BF16>(buf[k], static_cast<int64_t>(c) * CHUNK)
-                                    : item_stats<BF16>(buf[k], cf);
+        const uint64_t v = GREEDY ? item_argmax<BF16>(buf[k], static_cast<int64_t>(c) * CHUNK)
+                                  : item_stats<BF16>(buf[k], cf);
         if (lane == 0) slot_store(ee_part(p, b, s, row, c), v);
       }
     }
@@ -549,10 +549,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   // s - 1 itself.
   const uint64_t d = s > 0 ? slot_load(ee_dec(p, b, s - 1, 0)) : 0u;
   EeReq r = ee_req_scalars(p, b, s);
+  bool cont_prev = false;  // stage s - 1 is decided and accepted
   {
     const uint32_t code = static_cast<uint32_t>(d), kind = code & 0xFFu;
     const bool rejected_here = kind == kRej && static_cast<int>(code >> 8) == s - 1;
     if (d != 0u && kind != kCont && !(j >= p.ngs && rejected_here)) return;
+    cont_prev = d != 0u && kind == kCont;
+  }
+  // Workgroups with nothing to do for this request also exit before its
+  // token check.  (The request's faults are reported by workgroup 0 of
+  // region 0, which always checks.)
+  if (r.valid) {
+    if (j < p.ngs) {
+      // a sampled request has no statistics at s = K; groups past the items
+      if (!r.greedy && s == r.K) return;
+      const int n_items = (r.greedy ? 1 : kStageRows) * p.nc;
+      if (j > (n_items + kGroupItems - 1) / kGroupItems - 1) return;
+    } else {
+      // a greedy request has no races; region 0 races only K = 0 requests;
+      // after an acceptance at s - 1 only the bonus stage s = K races
+      if (r.greedy || (s == 0 && r.K != 0) || (cont_prev && s < r.K)) return;
+    }
   }
   ee_req_tokens(p, r);
   if (!r.valid) {
@@ -580,7 +597,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       }
       if ((code & 0xFFu) != kCont) return;
     }
-    ee_stats<BF16, VEC>(p, b, s, j, r);
+    if (r.greedy)
+      ee_stats<BF16, VEC, true>(p, b, s, j, r);
+    else
+      ee_stats<BF16, VEC, false>(p, b, s, j, r);
     if (j == last) {
       __syncthreads();
       ee_decide<BF16>(p, b, s, r);
