@@ -66,8 +66,8 @@
 namespace {
 
 constexpr int kRowsMax = 2 * SV_KMAX + 1;         // row slots per request
-constexpr int kFoldChunks = 64;                   // chunks per block of a fold
-constexpr int kFoldSlotsPerThread = (kRowsMax * kFoldChunks + 255) / 256;  // slots a thread loads per block
+constexpr int kFoldBlocks = 8;  // canonical blocks of a row per round of a fold
+constexpr int kFoldSlotsPerThread = (kRowsMax * kFoldBlocks * kGroupItems + 255) / 256;
 constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
 // s_sleep units (64 clocks each) between polling rounds of a fold
 #ifndef SV_FOLD_SLEEP
@@ -117,13 +117,13 @@ struct Params {
   uint32_t k0, k1;           // Philox key
   int32_t B, V, max_k, n_draft_rows;
   int32_t nc;   // row-chunks per row
-  int32_t flat; // 1: flat item grouping (8 items per workgroup), 0: column grouping
+  int32_t flat; // 1: flat grouping (one 8-chunk block of one row per workgroup), 0: column
   int32_t m;    // column grouping: chunks per workgroup
-  int32_t ng;   // workgroups per request: ceil(nc / m), or ceil(rows nc / 8) when flat
+  int32_t ng;   // workgroups per request: ceil(nc / m), or rows ceil(nc / 8) when flat
   int32_t mr;   // race chunks per race workgroup
   int32_t ngr;  // race workgroups per request, ceil(nc / mr) <= ng
   int32_t lag;  // request b's race workgroups follow the statistics of request b + lag
-  uint64_t* part;    // [B][2 max_k + 1][nc] row-chunk partials
+  uint64_t* part;    // [B][2 max_k + 1][nc] block (flat) or row-chunk (column) partials
   uint64_t* race;    // [B][ngr] race winner of each race workgroup
   int32_t* accept_len;
   int32_t* out_tokens;
@@ -171,17 +171,49 @@ __device__ __forceinline__ int row_slot(const Params& p, int K, int r) {
   return r <= K ? r : p.max_k + r - K;
 }
 
-__device__ __forceinline__ uint64_t* part_slot(const Params& p, int b, int j, int c) {
-  return p.part + (static_cast<int64_t>(b) * (2 * p.max_k + 1) + j) * p.nc + c;
+// A row's statistics are folded over canonical blocks: chunks [8k, 8k + 8)
+// of the row.  With flat grouping a statistics workgroup covers one block
+// and leaves its merged partial in slot k of the row; with column grouping
+// workgroups leave one partial per row-chunk (slot c) and the fold forms the
+// blocks.  Both give the same floats, so results do not depend on the grid.
+__device__ __forceinline__ int blocks_per_row(const Params& p) {
+  return (p.nc + kGroupItems - 1) / kGroupItems;
+}
+__device__ __forceinline__ int slots_per_row(const Params& p) {
+  return p.flat ? blocks_per_row(p) : p.nc;
 }
 
-// Zeroes the row-chunk partials of rows 0..nrows-1 of request b (the
-// finishing workgroup, once every reader of them is done).
+__device__ __forceinline__ uint64_t* part_slot(const Params& p, int b, int j, int u) {
+  return p.part + (static_cast<int64_t>(b) * (2 * p.max_k + 1) + j) * p.nc + u;
+}
+
+// Zeroes the partials of rows 0..nrows-1 of request b (the finishing
+// workgroup, once every reader of them is done).
 __device__ void clear_request(const Params& p, int b, int K, int nrows) {
-  const int n = nrows * p.nc;
+  const int ns = slots_per_row(p);
+  const int n = nrows * ns;
   for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int r = i / p.nc;
-    slot_store(part_slot(p, b, row_slot(p, K, r), i - r * p.nc), 0u);
+    const int r = i / ns;
+    slot_store(part_slot(p, b, row_slot(p, K, r), i - r * ns), 0u);
+  }
+}
+
+// The canonical block merge of n chunk partials in order: the largest
+// maximum, then the sums moved to it and added in order (sampled); the larger
+// maximum, then the lower index (greedy, exact in any order).
+template <bool GREEDY>
+__device__ __forceinline__ uint64_t merge_block(const uint64_t* part, int n, float cf) {
+  float M = -INFINITY;
+  int I = INT_MAX;
+  if constexpr (GREEDY) {
+    for (int i = 0; i < n; ++i) merge_argmax(M, I, slot_f(part[i]), static_cast<int>(slot_w(part[i])));
+    return pack_slot(M, static_cast<uint32_t>(I));
+  } else {
+    for (int i = 0; i < n; ++i) M = fmaxf(M, slot_f(part[i]));
+    const float mc = weight_ref(M);
+    float S = 0.f;
+    for (int i = 0; i < n; ++i) S += __uint_as_float(slot_w(part[i])) * rescale(slot_f(part[i]), cf, mc);
+    return pack_slot(M, __float_as_uint(S));
   }
 }
 
@@ -191,21 +223,25 @@ __device__ void finish_greedy(const Params& p, int b, const Req& r);
 // partials for a sampled request or (max, argmax) for a greedy one.
 template <bool BF16, bool VEC, bool GREEDY>
 __device__ void stats_items(const Params& p, int b, const Req& r, int cg, float cf) {
+  __shared__ uint64_t sh_block[kGroupItems];  // flat grouping: the block's chunk partials
   constexpr int CHUNK = chunk_tokens(BF16);
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int K = r.K;
   const int nrows = GREEDY ? K + 1 : 2 * K + 1;
   // The request's (row, chunk) items are numbered row-major over the chunks
   // a group covers; item i is row i / span, chunk c0 + i % span.  Flat
-  // grouping: every group covers all nc chunks and takes the 8 items
-  // [8 cg, 8 cg + 8).  Column grouping: group cg covers m chunks from cg m and
-  // takes all its rows x m items.
+  // grouping: group cg covers block k = cg mod (blocks per row) of row
+  // cg / (blocks per row), chunks [8k, 8k + 8).  Column grouping: group cg
+  // covers m chunks from cg m and takes all its rows x m items.
   int span, c0, i_lo, i_hi;
   if (p.flat) {
-    span = p.nc;
-    c0 = 0;
-    i_lo = cg * kGroupItems;
-    i_hi = min(i_lo + kGroupItems, nrows * p.nc);
+    const int bpr = blocks_per_row(p);
+    const int row = cg / bpr;
+    if (row >= nrows) return;  // (a greedy request's groups past its rows)
+    c0 = (cg - row * bpr) * kGroupItems;
+    span = min(kGroupItems, p.nc - c0);
+    i_lo = row * span;
+    i_hi = i_lo + span;
   } else {
     c0 = cg * p.m;
     span = min(p.m, p.nc - c0);
@@ -242,8 +278,21 @@ __device__ void stats_items(const Params& p, int b, const Req& r, int cg, float 
           mask_tail<BF16>(buf[k], p.V, static_cast<int64_t>(c) * CHUNK);
         const uint64_t v = GREEDY ? item_argmax<BF16>(buf[k], static_cast<int64_t>(c) * CHUNK)
                                   : item_stats<BF16>(buf[k], cf);
-        if (lane == 0) slot_store(part_slot(p, b, row_slot(p, K, row), c), v);
+        if (lane == 0) {
+          if (p.flat)
+            sh_block[i - i_lo] = v;
+          else
+            slot_store(part_slot(p, b, row_slot(p, K, row), c), v);
+        }
       }
+    }
+  }
+  if (p.flat) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int row = i_lo / span;
+      slot_store(part_slot(p, b, row_slot(p, K, row), c0 / kGroupItems),
+                 merge_block<GREEDY>(sh_block, span, cf));
     }
   }
 }
@@ -269,8 +318,7 @@ __device__ void stats_part(const Params& p, int b, int cg) {
     SV_STAMP(3);  // partials stored
     // the request's last workgroup with items finishes it (flat grouping
     // leaves the groups past a greedy request's (K+1) nc items empty)
-    const int last = p.flat ? static_cast<int>(ceil_div_dev((r.K + 1) * p.nc, kGroupItems)) - 1
-                            : p.ng - 1;
+    const int last = p.flat ? (r.K + 1) * blocks_per_row(p) - 1 : p.ng - 1;
     if (cg == last) finish_greedy(p, b, r);
   } else {
     stats_items<BF16, VEC, false>(p, b, r, cg, kLog2e / r.T);
@@ -281,7 +329,7 @@ __device__ void stats_part(const Params& p, int b, int cg) {
 // ------------------------------------------------------------------ folding
 
 struct FoldShared {
-  uint64_t slots[kRowsMax * kFoldChunks];  // one block of the request's partials, [row][chunk]
+  uint64_t slots[kRowsMax * kFoldBlocks * kGroupItems];  // one round of partials, [row][slot]
   float m[kWaves][kRowsMax];
   float s[kWaves][kRowsMax];  // greedy: argmax index bits
   float row_m[kRowsMax];      // folded row maximum
@@ -289,93 +337,133 @@ struct FoldShared {
   int bad;                    // 1: a row is not finite, 2: a wait expired
 };
 
-// Folds the partials of rows 0..nrows-1 of request b.  The partials are
-// taken in blocks of kFoldChunks chunks: the workgroup loads a block with
-// adjacent threads on adjacent slots (few memory transactions), re-polls the
-// slots still missing, and stages the block in LDS.  Then lane = row, and
-// wave w merges its quarter of the block's chunks in order into its running
-// row statistics; at the end wave 0 merges the waves in order.  Every
-// workgroup that folds the same request gets the same floats.
+// One round of a fold: row = lane takes blocks blk0 + 2w, blk0 + 2w + 1
+// (wave w) from the round's slots in LDS (nsr per row, spb per block; a
+// block of chunk partials is merged with merge_block) into its running row
+// statistics (M, S) or argmax (M, I).
+template <bool GREEDY>
+__device__ __forceinline__ void fold_round(const uint64_t* rs, int blk0, int nb, int nsr,
+                                           int spb, float cf, float& M, float& S, int& I) {
+  const int wave = wave_id();
+  uint64_t bv[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = 2 * wave + h;  // block within the round
+    if (blk0 + j >= nb) continue;
+    const int a = j * spb, n = min(spb, nsr - a);
+    if (n <= 0) continue;
+    bool have = true;
+    for (int i = 0; i < n; ++i) have = have && rs[a + i] != 0u;
+    if (have) bv[h] = spb == 1 ? rs[a] : merge_block<GREEDY>(rs + a, n, cf);
+  }
+  if constexpr (GREEDY) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (bv[h] != 0u) merge_argmax(M, I, slot_f(bv[h]), static_cast<int>(slot_w(bv[h])));
+  } else {
+    float bm = M;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (bv[h] != 0u) bm = fmaxf(bm, slot_f(bv[h]));
+    const float bmc = weight_ref(bm);
+    S *= rescale(M, cf, bmc);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (bv[h] != 0u) S += __uint_as_float(slot_w(bv[h])) * rescale(slot_f(bv[h]), cf, bmc);
+    M = bm;
+  }
+}
+
+// Folds the partials of rows 0..nrows-1 of request b, in rounds of
+// kFoldBlocks canonical blocks per row (fold_round).  When the request has
+// at most 64 slots (one round), wave 0 polls them all, one per lane, and
+// stages them in LDS as they arrive.  Otherwise the workgroup first waits
+// for the request's last slot (sampled), then per round loads the round's
+// slots with adjacent threads on adjacent slots (few memory transactions),
+// re-polls the slots still missing, and stages them in LDS.  At the end
+// wave 0 merges the waves in order.  The order of every operation depends on
+// nc only, so every workgroup that folds the same request, and every grid,
+// gets the same floats.
 template <bool GREEDY>
 __device__ void fold_rows(const Params& p, int b, int K, int nrows, float cf, FoldShared& sh) {
+  static_assert(kFoldBlocks == 2 * kWaves, "two blocks per wave per round");
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   if (tid == 0) sh.bad = 0;
   const bool active = lane < nrows;
+  const int nb = blocks_per_row(p), ns = slots_per_row(p);
+  const int spb = p.flat ? 1 : kGroupItems;  // slots per block
   float M = -INFINITY, S = 0.f;
   int I = INT_MAX;
   bool expired = false;
-  if constexpr (!GREEDY) {
-    // A race workgroup may start long before the request's statistics are
-    // in.  It first waits, with one lane, for the slot of the request's last
-    // row-chunk, which the last statistics workgroup in grid order writes,
-    // and only then loads every slot: hundreds of racing workgroups each
-    // re-polling all their partials would load the memory system that the
-    // statistics stream through.
-    if (tid == 0) slot_wait(part_slot(p, b, row_slot(p, K, nrows - 1), p.nc - 1));
-    SV_STAMP(3);  // race: the request's last partial seen
-  }
-  for (int cblk = 0; cblk < p.nc; cblk += kFoldChunks) {
-    const int ncb = min(kFoldChunks, p.nc - cblk);
-    const int n_slots = nrows * ncb;
-    __syncthreads();  // the previous block's LDS reads are done
-    uint64_t v[kFoldSlotsPerThread];
-#pragma unroll
-    for (int i = 0; i < kFoldSlotsPerThread; ++i) {  // issue every load before waiting on any
-      // on one code path: past the block's last slot a thread loads that slot again
-      const int q = min(tid + i * kThreads, n_slots - 1);
-      const int row = q / ncb;
-      v[i] = slot_load(part_slot(p, b, row_slot(p, K, row), cblk + q - row * ncb));
-    }
-    // re-poll every slot still missing together, one round trip per round
-    uint32_t missing = 0u;
-#pragma unroll
-    for (int i = 0; i < kFoldSlotsPerThread; ++i)
-      if (tid + i * kThreads < n_slots && v[i] == 0u) missing |= 1u << i;
-    for (unsigned it = 0; missing != 0u && it < kSpinLimit; ++it) {
-      __builtin_amdgcn_s_sleep(SV_FOLD_SLEEP);
-#pragma unroll
-      for (int i = 0; i < kFoldSlotsPerThread; ++i) {
-        if (missing & (1u << i)) {
-          const int q = tid + i * kThreads;
-          const int row = q / ncb;
-          v[i] = slot_load(part_slot(p, b, row_slot(p, K, row), cblk + q - row * ncb));
-        }
+  if (nb <= kFoldBlocks && nrows * ns <= 64) {
+    // one round: wave 0 polls every slot directly (a lane per slot)
+    if (wave == 0) {
+      const int n_slots = nrows * ns;
+      const int q = min(lane, n_slots - 1);
+      const int row = q / ns;
+      uint64_t* slot = part_slot(p, b, row_slot(p, K, row), q - row * ns);
+      uint64_t v = slot_load(slot);
+      for (unsigned it = 0; __ballot(v == 0u) != 0u && it < kSpinLimit; ++it) {
+        __builtin_amdgcn_s_sleep(SV_FOLD_SLEEP);
+        if (v == 0u) v = slot_load(slot);
       }
+      expired = __ballot(v == 0u) != 0u;
+      if (lane < n_slots) sh.slots[lane] = v;
+    }
+    if constexpr (!GREEDY) SV_STAMP(3);  // race: the request's last partial seen
+    __syncthreads();
+    if (active) fold_round<GREEDY>(sh.slots + lane * ns, 0, nb, ns, spb, cf, M, S, I);
+  } else {
+    if constexpr (!GREEDY) {
+      // A race workgroup may start long before the request's statistics are
+      // in.  It first waits, with one lane, for the request's last slot,
+      // which the last statistics workgroup in grid order writes, and only
+      // then loads every slot: hundreds of racing workgroups each re-polling
+      // hundreds of partials would load the memory system that the
+      // statistics stream through.
+      if (tid == 0) slot_wait(part_slot(p, b, row_slot(p, K, nrows - 1), ns - 1));
+      SV_STAMP(3);  // race: the request's last partial seen
+    }
+    for (int blk0 = 0; blk0 < nb; blk0 += kFoldBlocks) {
+      const int u0 = blk0 * spb;                       // the round's first slot
+      const int nsr = min(kFoldBlocks * spb, ns - u0);  // slots per row this round
+      const int n_slots = nrows * nsr;
+      __syncthreads();  // the previous round's LDS reads are done
+      uint64_t v[kFoldSlotsPerThread];
+#pragma unroll
+      for (int i = 0; i < kFoldSlotsPerThread; ++i) {  // issue every load before waiting on any
+        // on one code path: past the round's last slot a thread loads that slot again
+        const int q = min(tid + i * kThreads, n_slots - 1);
+        const int row = q / nsr;
+        v[i] = slot_load(part_slot(p, b, row_slot(p, K, row), u0 + q - row * nsr));
+      }
+      // re-poll every slot still missing together, one round trip per round
+      uint32_t missing = 0u;
 #pragma unroll
       for (int i = 0; i < kFoldSlotsPerThread; ++i)
-        if ((missing & (1u << i)) && v[i] != 0u) missing &= ~(1u << i);
-    }
-    if (missing != 0u) expired = true;
+        if (tid + i * kThreads < n_slots && v[i] == 0u) missing |= 1u << i;
+      for (unsigned it = 0; missing != 0u && it < kSpinLimit; ++it) {
+        __builtin_amdgcn_s_sleep(SV_FOLD_SLEEP);
 #pragma unroll
-    for (int i = 0; i < kFoldSlotsPerThread; ++i) {
-      const int q = tid + i * kThreads;
-      if (q < n_slots) sh.slots[q] = v[i];
-    }
-    __syncthreads();
-    if (!active) continue;
-    // wave w merges chunks [cb, ce) of the block for row = lane
-    const int cpw = (ncb + kWaves - 1) / kWaves;
-    const int cb = wave * cpw;
-    const int ce = min(cb + cpw, ncb);
-    const uint64_t* rs = sh.slots + lane * ncb;
-    if constexpr (GREEDY) {
-      for (int c = cb; c < ce; ++c) {
-        const uint64_t x = rs[c];
-        if (x != 0u) merge_argmax(M, I, slot_f(x), static_cast<int>(slot_w(x)));
+        for (int i = 0; i < kFoldSlotsPerThread; ++i) {
+          if (missing & (1u << i)) {
+            const int q = tid + i * kThreads;
+            const int row = q / nsr;
+            v[i] = slot_load(part_slot(p, b, row_slot(p, K, row), u0 + q - row * nsr));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kFoldSlotsPerThread; ++i)
+          if ((missing & (1u << i)) && v[i] != 0u) missing &= ~(1u << i);
       }
-    } else {
-      float bm = M;
-      for (int c = cb; c < ce; ++c) {
-        const uint64_t x = rs[c];
-        if (x != 0u) bm = fmaxf(bm, slot_f(x));
+      if (missing != 0u) expired = true;
+#pragma unroll
+      for (int i = 0; i < kFoldSlotsPerThread; ++i) {
+        const int q = tid + i * kThreads;
+        if (q < n_slots) sh.slots[q] = v[i];
       }
-      const float bmc = weight_ref(bm);
-      S *= rescale(M, cf, bmc);
-      for (int c = cb; c < ce; ++c) {
-        const uint64_t x = rs[c];
-        if (x != 0u) S += __uint_as_float(slot_w(x)) * rescale(slot_f(x), cf, bmc);
-      }
-      M = bm;
+      __syncthreads();
+      if (active) fold_round<GREEDY>(sh.slots + lane * nsr, blk0, nb, nsr, spb, cf, M, S, I);
     }
   }
   __syncthreads();  // sh.bad initialised
@@ -935,7 +1023,8 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   prm.flat = static_cast<int64_t>(n_draft_rows) == static_cast<int64_t>(B) * max_k;
   if (prm.flat) {
     prm.m = 1;
-    prm.ng = static_cast<int32_t>(ceil_div(static_cast<int64_t>(rows) * prm.nc, kGroupItems));
+    // one canonical block (8 chunks of one row) per statistics workgroup
+    prm.ng = static_cast<int32_t>(static_cast<int64_t>(rows) * ceil_div(prm.nc, kGroupItems));
     // race chunks per race workgroup: at least two, and enough that a
     // request has at most half as many race workgroups as statistics
     // workgroups.  Few rows per request (MTP, K = 1) then get wide races:
