@@ -1045,12 +1045,14 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   // request's statistics are in; placed too early it idles a slot the stream
   // needs, too late it starts the request's dependent chain late.  The lag,
   // in workgroups between a request's statistics and its races, was tuned
-  // on MI355X: about 0.45 of a resident generation (5 workgroups per CU)
-  // with flat grouping, 1.2 with column grouping (ragged batches).  An
+  // on MI355X: about 0.55 of a resident generation (5 workgroups per CU)
+  // with flat grouping (0.45 -> 0.55 once the fold reads merged block
+  // partials: B=64 K=4 29.35 -> 28.93 us, B=512 K=1 78.2 -> 77.5 us),
+  // 1.2 with column grouping (ragged batches).  An
   // all-greedy call has no races: lag = B puts every statistics workgroup
   // first and the grid ends there.
   const int64_t resident = kWorkgroupsPerCu * compute_units();
-  const int64_t lag_wgs = prm.flat ? resident * 9 / 20 : resident * 6 / 5;
+  const int64_t lag_wgs = prm.flat ? resident * 11 / 20 : resident * 6 / 5;
   prm.lag = all_greedy ? B
                        : static_cast<int32_t>(std::min<int64_t>(
                              B, std::max<int64_t>(1, ceil_div(lag_wgs, prm.ng))));
