@@ -185,7 +185,10 @@ size_t spec_verify_early_exit_workspace_bytes(int32_t B, int32_t V, int32_t max_
  * at the first rejection ("Decodificación Especulativa y EAGLE", section "La
  * Regla de Exactitud"; "El Concepto", steps 3-4), so target and draft rows
  * after the stop position cannot change the outcome; this entry point
- * streams a request's rows one position at a time and skips the rest.
+ * streams a request's rows one position (stage) at a time and skips the
+ * stages that start after the request's stop is decided.  A stage whose
+ * previous decision is still pending when it starts streams anyway (on
+ * speculation), so small batches stream their stages together.
  * Arguments, layout, ownership and status codes as for spec_verify_sample,
  * with these differences:
  *   - accept_len and out_tokens equal spec_verify_sample's (same Philox
@@ -197,13 +200,15 @@ size_t spec_verify_early_exit_workspace_bytes(int32_t B, int32_t V, int32_t max_
  *     request (spec_verify_sample reads every row and fails it);
  *   - it trades parallelism inside a request for bytes: worthwhile for large
  *     batches whose requests mostly stop well before K_b, slower than
- *     spec_verify_sample for small ones (it waits stage by stage).  On
- *     MI355X it pays once the full verify takes more than about 100 us:
+ *     spec_verify_sample for small ones (its stage decisions form a chain).
+ *     On MI355X it pays once the full verify takes more than about 60 us:
  *     K = 8 fp32 from 64 requests of V = 128256, ragged K <= 8 bf16 from
- *     256 requests of V = 152064; at K = 1 the two are within a few us.
+ *     256 requests of V = 152064 (even from 64 to 128); at K = 1 the two
+ *     are within a few us.
  * The workspace is the one sized by spec_verify_early_exit_workspace_bytes.
  * Unlike spec_verify_sample, each call enqueues two kernels on `stream`: the
- * verify kernel, then a small kernel that clears its decision records.  As
+ * verify kernel, then a small kernel that clears its decision records and
+ * the partials of stages streamed on speculation past a stop.  As
  * for the other entry points, accept_len[b] = -1 with no fault found in the
  * request means a bounded wait expired; the workspace may then hold stale
  * hand-off slots, so zero it again before the next call.  Calls that overlap
