@@ -8,9 +8,10 @@
 // draft-target scheme).
 //
 // One launch.  Row b is cut into chunks of NV 16-byte vectors per lane: 8 KiB
-// (NV = 8, the verify kernel's row-chunk), or 4 KiB (NV = 4) when full chunks
+// (NV = 8, the verify kernel's row-chunk), 4 KiB (NV = 4) when full chunks
 // would give the batch fewer than about four waves per SIMD for this
-// arithmetic-bound pass.  Workgroup g serves request b = g / ng and the 4
+// arithmetic-bound pass, and 2 KiB (NV = 2) when half chunks would give it
+// fewer than one.  Workgroup g serves request b = g / ng and the 4
 // chunks cg * 4 + wave (cg = g mod ng, one chunk per wave).  A wave of a sampled request makes one pass over its chunk for the
 // maximum, then a second pass that, per token, forms the weight
 // w = 2^((z - m) c) (c = log2(e) / T, m the chunk maximum), adds it to
@@ -44,6 +45,10 @@ constexpr uint32_t kDraftTag = 2u;  // Philox stream tag of the draft sampler
 // of V = 128256 go from 10.6 to 10.0 us, while 256 fp32 rows keep full chunks
 // (half chunks there: 35.4 -> 40.4 us, twice the partials to fold).
 constexpr int64_t kHalfChunksBelow = 4096;
+// Quarter chunks below this many half-chunk waves (one per SIMD): one sampled
+// bf16 row of V = 128256 7.1 -> 6.4 us, eight 7.6 -> 6.8 us; from 32 rows on
+// quarter chunks gain nothing.
+constexpr int64_t kQuarterChunksBelow = 1024;
 
 __host__ __device__ constexpr int draft_chunk_tokens(bool bf16, int nv) {
   return 64 * nv * elems_per_vec(bf16);
@@ -271,9 +276,9 @@ __global__ __launch_bounds__(kThreads) void sd_sample(DraftParams p) {
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Sized with the smallest chunk (float32, half length), so any launch fits.
+// Sized with the smallest chunk (float32, quarter length), so any launch fits.
 size_t draft_workspace(int32_t B, int32_t V) {
-  const int64_t nc = ceil_div64(V, draft_chunk_tokens(false, kItemVecs / 2));
+  const int64_t nc = ceil_div64(V, draft_chunk_tokens(false, kItemVecs / 4));
   return static_cast<size_t>(B) * static_cast<size_t>(nc) * 2 * sizeof(uint64_t);
 }
 
@@ -285,9 +290,10 @@ int draft_launch(const DraftParams& prm, int64_t grid, hipStream_t stream) {
 }
 
 template <bool BF16, bool VEC>
-int draft_launch_nv(const DraftParams& prm, int64_t grid, bool half, hipStream_t stream) {
-  return half ? draft_launch<BF16, VEC, kItemVecs / 2>(prm, grid, stream)
-              : draft_launch<BF16, VEC, kItemVecs>(prm, grid, stream);
+int draft_launch_nv(const DraftParams& prm, int64_t grid, int nv, hipStream_t stream) {
+  if (nv == kItemVecs / 4) return draft_launch<BF16, VEC, kItemVecs / 4>(prm, grid, stream);
+  if (nv == kItemVecs / 2) return draft_launch<BF16, VEC, kItemVecs / 2>(prm, grid, stream);
+  return draft_launch<BF16, VEC, kItemVecs>(prm, grid, stream);
 }
 
 }  // namespace
@@ -317,10 +323,13 @@ int spec_draft_sample(const void* draft_logits, int32_t dtype, int32_t B, int32_
   prm.B = B;
   prm.V = V;
   prm.step = step;
-  const int64_t full_waves = static_cast<int64_t>(B) * ceil_div64(V, chunk_tokens(bf16));
-  const bool half = full_waves < kHalfChunksBelow;
-  prm.nc = static_cast<int32_t>(
-      ceil_div64(V, draft_chunk_tokens(bf16, half ? kItemVecs / 2 : kItemVecs)));
+  int nv = kItemVecs;
+  if (static_cast<int64_t>(B) * ceil_div64(V, draft_chunk_tokens(bf16, nv)) < kHalfChunksBelow)
+    nv = kItemVecs / 2;
+  if (nv == kItemVecs / 2 &&
+      static_cast<int64_t>(B) * ceil_div64(V, draft_chunk_tokens(bf16, nv)) < kQuarterChunksBelow)
+    nv = kItemVecs / 4;
+  prm.nc = static_cast<int32_t>(ceil_div64(V, draft_chunk_tokens(bf16, nv)));
   prm.ng = static_cast<int32_t>(ceil_div64(prm.nc, kWaves));
   prm.part = static_cast<uint64_t*>(workspace);
   prm.tokens = tokens;
@@ -331,10 +340,10 @@ int spec_draft_sample(const void* draft_logits, int32_t dtype, int32_t B, int32_
   const bool vec = row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(draft_logits) & 15u) == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (bf16)
-    return vec ? draft_launch_nv<true, true>(prm, grid, half, s)
-               : draft_launch_nv<true, false>(prm, grid, half, s);
-  return vec ? draft_launch_nv<false, true>(prm, grid, half, s)
-             : draft_launch_nv<false, false>(prm, grid, half, s);
+    return vec ? draft_launch_nv<true, true>(prm, grid, nv, s)
+               : draft_launch_nv<true, false>(prm, grid, nv, s);
+  return vec ? draft_launch_nv<false, true>(prm, grid, nv, s)
+             : draft_launch_nv<false, false>(prm, grid, nv, s);
 }
 
 }  // extern "C"

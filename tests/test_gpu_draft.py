@@ -108,11 +108,13 @@ def test_draft_temperature_range(dtype):
     check(rows, dtype, temps, 777, 1)
 
 
-@pytest.mark.parametrize("B", [127, 128])
+@pytest.mark.parametrize("B", [16, 17, 127, 128])
 def test_draft_chunk_length_switch(B):
-    """Either side of the batch size where the sampler moves from 4 KiB to 8 KiB
-    chunks per wave (bf16, V=128256: 127 rows x 32 full chunks stay below 4096
-    waves, 128 rows do not).  The same rows give the oracle's tokens either way."""
+    """Either side of the batch sizes where the sampler changes its chunk per
+    wave (bf16, V=128256): 2 KiB up to 16 rows (16 x 63 half chunks stay below
+    1024 waves, 17 rows do not), 4 KiB up to 127 rows (127 x 32 full chunks
+    stay below 4096 waves, 128 rows do not), 8 KiB from 128.  The same rows
+    give the oracle's tokens either way."""
     rng = np.random.default_rng(31)
     V = 128256
     rows = W.to_storage(rng.normal(0, 3.0, size=(128, V)), W.DTYPE_BF16)[:B]
