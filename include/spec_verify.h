@@ -201,10 +201,9 @@ size_t spec_verify_early_exit_workspace_bytes(int32_t B, int32_t V, int32_t max_
  *   - it trades parallelism inside a request for bytes: worthwhile for large
  *     batches whose requests mostly stop well before K_b, slower than
  *     spec_verify_sample for small ones (its stage decisions form a chain).
- *     On MI355X it pays once the full verify takes more than about 60 us:
- *     K = 8 fp32 from 64 requests of V = 128256, ragged K <= 8 bf16 from
- *     256 requests of V = 152064 (even from 64 to 128); at K = 1 the two
- *     are within a few us.
+ *     On MI355X it pays once the full verify takes more than about 50 us:
+ *     K = 8 fp32 from 32 requests of V = 128256, ragged K <= 8 bf16 from
+ *     64 requests of V = 152064; at K = 1 the two are within a few us.
  * The workspace is the one sized by spec_verify_early_exit_workspace_bytes.
  * Unlike spec_verify_sample, each call enqueues two kernels on `stream`: the
  * verify kernel, then a small kernel that clears its decision records and

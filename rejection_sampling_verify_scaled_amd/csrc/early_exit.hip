@@ -8,9 +8,9 @@
 // position (stage) at a time, and later stages are skipped once a stage
 // rejects (sampled) or mismatches (greedy).
 //
-// One launch, stage-major.  The grid is max_k + 1 regions; region s holds,
-// for every request b, ngs statistics workgroups for stage s and ngr race
-// workgroups:
+// One launch, stage-major.  The grid is max_k + 1 regions of ngs statistics
+// workgroups per request, one region per stage s, and ngr race workgroups
+// per request, in one of two layouts (below):
 //   statistics (b, s), s < K_b: unless stage s - 1 is already decided and
 //     stopped, stream target row s and, for a sampled request, draft row s
 //     (8 row-chunks per workgroup, two in flight per wave), one 8-byte
@@ -32,9 +32,18 @@
 //     (keys in the log2 domain relative to each chunk's maximum, so it needs
 //     no statistics of that row).  The last race workgroup folds the chunk
 //     winners and writes the outputs.
-// A region's workgroups find the previous stage's decisions ready when the
-// regions are large (many requests); with small batches only the deciding
-// workgroups and the races wait on them.
+// Layouts.  Races at the end (the default): the race workgroups of every
+// request follow all statistics regions, and each finds its request's stop in
+// the record of the request's last draft position (a stop is copied there).
+// Races per region: region s also holds ngr race workgroups per request that
+// race a rejection at s - 1 (or the bonus at s = K_b).  Most of these find
+// nothing to do, and while a decision is pending they hold slots the stream
+// needs; but when the batch's races are many and mostly bonus races (K = 1,
+// more race workgroups than one resident generation), interleaving them with
+// the last stage's statistics keeps their arithmetic beside streaming instead
+// of in a tail of its own.  A region's workgroups find the previous stage's
+// decisions ready when the regions are large (many requests); with small
+// batches only the deciding workgroups and the races wait on them.
 //
 // Hand-offs use the zero-slot protocol of the verify kernel: a slot is
 // written once per call and is all-zero until then.  Partials and race
@@ -50,6 +59,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -91,6 +101,7 @@ struct EeParams {
   uint64_t* part;  // [B][max_k + 1][2][nc] stage partials
   uint64_t* race;  // [B][ngr] race winners
   uint64_t* dec;   // [B][max_k + 1][kDecSlots] decision records
+  int32_t endrace; // 1: the race workgroups follow all statistics regions
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_at;
@@ -543,12 +554,31 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 5))) void sv_verify_ee(
     EeParams p) {
   const int g = blockIdx.x;
-  const int per_req = p.ngs + p.ngr;
-  const int region = p.B * per_req;
-  const int s = g / region;
-  const int t = g - s * region;
-  const int b = t / per_req;
-  const int j = t - b * per_req;
+  int s, b, j;            // stage, request, group (j >= ngs: race group j - ngs)
+  bool end_race = false;  // a race workgroup of the end region (s = 0 stands in)
+  if (p.endrace) {
+    const int region = p.B * p.ngs;
+    const int n_stats = (p.max_k + 1) * region;
+    if (g < n_stats) {
+      s = g / region;
+      const int t = g - s * region;
+      b = t / p.ngs;
+      j = t - b * p.ngs;
+    } else {
+      const int t = g - n_stats;
+      s = 0;
+      b = t / p.ngr;
+      j = p.ngs + (t - b * p.ngr);
+      end_race = true;
+    }
+  } else {
+    const int per_req = p.ngs + p.ngr;
+    const int region = p.B * per_req;
+    s = g / region;
+    const int t = g - s * region;
+    b = t / per_req;
+    j = t - b * per_req;
+  }
   // A request that stopped before stage s has a stop in the record of stage
   // s - 1 (its own decision, or one copied by publish_stop), so the
   // workgroups of its later stages exit on that one load, issued beside the
@@ -574,9 +604,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const int n_items = (r.greedy ? 1 : kStageRows) * p.nc;
       if (j > (n_items + kGroupItems - 1) / kGroupItems - 1) return;
     } else {
-      // a greedy request has no races; region 0 races only K = 0 requests;
-      // after an acceptance at s - 1 only the bonus stage s = K races
-      if (r.greedy || (s == 0 && r.K != 0) || (cont_prev && s < r.K)) return;
+      // a greedy request has no races; with races per region, region 0 races
+      // only K = 0 requests, and after an acceptance at s - 1 only the bonus
+      // stage s = K races
+      if (r.greedy || (!end_race && ((s == 0 && r.K != 0) || (cont_prev && s < r.K)))) return;
     }
   }
   ee_req_tokens(p, r);
@@ -620,13 +651,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       ee_decide<BF16>(p, b, s, r);
     }
   } else if (!r.greedy) {
-    ee_race<BF16, VEC>(p, b, s, j - p.ngs, r);
+    int sr = s;  // the race's stage: a rejection at sr - 1, or the bonus at sr = K
+    if (end_race && r.K > 0) {
+      // the request's stop, copied into the record of its last draft position
+      uint32_t code = 0;
+      if (!dec_wait(p, b, r.K - 1, 0, code)) {
+        if (j - p.ngs == p.ngr - 1 && threadIdx.x == 0) p.accept_len[b] = -1;
+        return;
+      }
+      const uint32_t kind = code & 0xFFu;
+      if (kind == kCont)
+        sr = r.K;
+      else if (kind == kRej)
+        sr = static_cast<int>(code >> 8) + 1;
+      else
+        return;  // stopped without a race (a failure)
+    }
+    ee_race<BF16, VEC>(p, b, sr, j - p.ngs, r);
   }
 }
 
 // ------------------------------------------------------------------ host side
 
 int64_t ee_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device, looked up once per device.
+int64_t ee_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 struct EeLayout {
   size_t part_off, race_off, dec_off, total;
@@ -726,7 +789,15 @@ int spec_verify_sample_early_exit(const void* target_logits, const void* draft_l
   prm.out_tokens = out_tokens;
   prm.p_at = p_at_draft;
   prm.q_at = q_at_draft;
-  const int64_t grid = static_cast<int64_t>(max_k + 1) * B * (prm.ngs + prm.ngr);
+  // Races at the end unless they are mostly bonus races (K = 1) and more than
+  // one resident generation: B=512 K=1 bf16 77.9 us per region against 93.5
+  // at the end, while at the end B=1024 ragged K <= 8 runs 402 -> 355 us,
+  // B=64 K=4 44.3 -> 40.3 us and B=64 K=1 31.8 -> 26.9 us.
+  const int64_t resident = static_cast<int64_t>(bf16 ? 4 : 5) * ee_compute_units();
+  prm.endrace = max_k > 1 || static_cast<int64_t>(B) * prm.ngr <= resident;
+  const int64_t grid =
+      prm.endrace ? static_cast<int64_t>(max_k + 1) * B * prm.ngs + static_cast<int64_t>(B) * prm.ngr
+                  : static_cast<int64_t>(max_k + 1) * B * (prm.ngs + prm.ngr);
   if (grid > INT32_MAX) return SV_ERR_SHAPE;
   const int64_t row_bytes = static_cast<int64_t>(V) * (bf16 ? 2 : 4);
   const bool vec = row_bytes % 16 == 0 &&
