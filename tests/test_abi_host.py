@@ -169,8 +169,9 @@ def test_commit_rejects_bad_arguments(lib, case):
 def test_tree_workspace_bytes(lib):
     n = lib.spec_verify_tree_workspace_bytes(16, 128256, 41)
     assert n > 0 and n % 256 == 0
-    # float32 chunks (2048 tokens): 16 requests x 41 nodes x 63 chunks x 8 bytes
-    assert n >= 16 * 41 * 63 * 8
+    # one partial per block of 8 float32 chunks (2048 tokens each):
+    # 16 requests x 41 nodes x ceil(63 / 8) blocks x 8 bytes
+    assert n >= 16 * 41 * 8 * 8
     for bad in ((0, 10, 1), (1, 0, 1), (1, 10, 0), (1, 10, binding.SV_TREE_MAX_NODES + 1)):
         assert lib.spec_verify_tree_workspace_bytes(*bad) == 0
     assert binding.SV_TREE_MAX_NODES == 64
