@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -474,6 +475,25 @@ __device__ __forceinline__ uint64_t item_argmax(const uint4* buf, int64_t e0) {
   }
   idx = wave_min_int(idx);
   return pack_slot(mx, static_cast<uint32_t>(idx));
+}
+
+// ------------------------------------------------------------------ host helpers
+
+// Compute units of the current device, looked up once per device (launch
+// shapes are sized from it: a resident generation is a few workgroups per CU).
+inline int64_t device_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 }  // namespace

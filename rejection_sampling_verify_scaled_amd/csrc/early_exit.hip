@@ -59,7 +59,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -74,7 +73,9 @@ namespace {
 // kNarrowRaceBelow workgroups): a small batch then gets more race
 // parallelism on its dependent chain (B=64 K=4 bf16: 57.3 -> 49.1 us), while
 // large batches keep the wider races (B=256 K=8 fp32 at 4 chunks: 236 ->
-// 293 us).
+// 293 us).  bf16 rows with max_k > 1 always race 4 chunks (16K tokens, as 8
+// fp32 chunks): with the races after all statistics, ragged K <= 8 batches
+// of B=128 run 79.5 -> 67.6 us and of B=1024 359 -> 355 us.
 constexpr int kRaceChunks = 8;
 constexpr int kRaceChunksNarrow = 4;
 constexpr int64_t kNarrowRaceBelow = 512;
@@ -675,21 +676,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
 
 int64_t ee_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Compute units of the current device, looked up once per device.
-int64_t ee_compute_units() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 struct EeLayout {
   size_t part_off, race_off, dec_off, total;
@@ -778,7 +764,8 @@ int spec_verify_sample_early_exit(const void* target_logits, const void* draft_l
   prm.n_draft_rows = n_draft_rows;
   prm.nc = static_cast<int32_t>(ee_ceil_div(V, chunk_tokens(bf16)));
   prm.ngs = static_cast<int32_t>(ee_ceil_div(static_cast<int64_t>(kStageRows) * prm.nc, kGroupItems));
-  prm.rcw = static_cast<int64_t>(B) * ee_ceil_div(prm.nc, kRaceChunks) < kNarrowRaceBelow
+  prm.rcw = static_cast<int64_t>(B) * ee_ceil_div(prm.nc, kRaceChunks) < kNarrowRaceBelow ||
+                    (bf16 && max_k > 1)
                 ? kRaceChunksNarrow
                 : kRaceChunks;
   prm.ngr = static_cast<int32_t>(ee_ceil_div(prm.nc, prm.rcw));
@@ -793,7 +780,7 @@ int spec_verify_sample_early_exit(const void* target_logits, const void* draft_l
   // one resident generation: B=512 K=1 bf16 77.9 us per region against 93.5
   // at the end, while at the end B=1024 ragged K <= 8 runs 402 -> 355 us,
   // B=64 K=4 44.3 -> 40.3 us and B=64 K=1 31.8 -> 26.9 us.
-  const int64_t resident = static_cast<int64_t>(bf16 ? 4 : 5) * ee_compute_units();
+  const int64_t resident = static_cast<int64_t>(bf16 ? 4 : 5) * device_compute_units();
   prm.endrace = max_k > 1 || static_cast<int64_t>(B) * prm.ngr <= resident;
   const int64_t grid =
       prm.endrace ? static_cast<int64_t>(max_k + 1) * B * prm.ngs + static_cast<int64_t>(B) * prm.ngr

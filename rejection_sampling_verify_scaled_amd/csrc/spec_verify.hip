@@ -934,21 +934,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Compute units of the current device, looked up once per device.
-int64_t compute_units() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -1051,7 +1036,7 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
   // 1.2 with column grouping (ragged batches).  An
   // all-greedy call has no races: lag = B puts every statistics workgroup
   // first and the grid ends there.
-  const int64_t resident = kWorkgroupsPerCu * compute_units();
+  const int64_t resident = kWorkgroupsPerCu * device_compute_units();
   const int64_t lag_wgs = prm.flat ? resident * 11 / 20 : resident * 6 / 5;
   prm.lag = all_greedy ? B
                        : static_cast<int32_t>(std::min<int64_t>(
@@ -1119,7 +1104,7 @@ int static_scratch(hipStream_t stream, size_t clear_bytes, void** out) {
   if (!sl.cleared) clear_bytes = kScratchBytes;
   if (clear_bytes > 0) {
     const int64_t n = static_cast<int64_t>(round256(std::min(clear_bytes, kScratchBytes)) / 16);
-    const int64_t grid = std::min<int64_t>(ceil_div(n, kThreads), 4 * compute_units());
+    const int64_t grid = std::min<int64_t>(ceil_div(n, kThreads), 4 * device_compute_units());
     hipLaunchKernelGGL(sv_zero_fill, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<uint4*>(sl.ptr), n);
     if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
