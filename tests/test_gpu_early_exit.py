@@ -69,6 +69,19 @@ def test_early_exit_full_workloads(cfg):
     print(tally)
 
 
+@pytest.mark.parametrize("B", [64, 256])
+def test_early_exit_mtp_race_layouts(B):
+    """K = 1 (MTP) batches of B=64 and B=256 take the layout with the race
+    workgroups after all statistics regions (their races fit in one resident
+    generation of an MI355X); the full B=512 batch above takes races per
+    region.  Both against the oracle, every request."""
+    b = W.subset_requests(W.make_batch(4, 0), range(B))
+    say(f"early exit MTP B={B}")
+    tally = check(b, run_ee(b), oracle.verify_batch(b))
+    print(tally)
+    assert tally.sampled + tally.greedy + tally.failed == b.B
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_early_exit_large_workloads(cfg):
     b = W.make_batch(cfg, 0)
