@@ -463,7 +463,7 @@ def stage_trace(args):
     torch.cuda.synchronize()
     n_words = (1 << 16) * npts
     buf = np.zeros(n_words, dtype=np.uint64)
-    rows = []
+    rows, streams = [], []
     for i in range(args.steps):
         if lib.spec_verify_trace_reset() != 0:
             raise SystemExit("trace reset failed")
@@ -471,7 +471,9 @@ def stage_trace(args):
         torch.cuda.synchronize()
         if lib.spec_verify_trace_copy(buf.ctypes.data_as(ctypes.c_void_p), n_words) != 0:
             raise SystemExit("trace copy failed")
-        rows.append(trace_summary(buf.reshape(-1, npts).copy(), batch, us_per_tick))
+        rec = buf.reshape(-1, npts).copy()
+        rows.append(trace_summary(rec, batch, us_per_tick))
+        streams.append(stream_profile(rec, batch, us_per_tick))
     keys = rows[0].keys()
     print(f"stage timeline of sv_verify, workload {args.workload} ({W.WORKLOADS[args.workload].name}),"
           f" {args.steps} traced calls after {args.warmup} untraced; trace build "
@@ -480,6 +482,70 @@ def stage_trace(args):
         vals = [r[k] for r in rows if r.get(k) is not None]
         if vals:
             print(f"  {k:58s} {np.mean(vals):8.2f}   (min {np.min(vals):7.2f}, max {np.max(vals):7.2f})")
+    if streams[0] is not None:
+        prof = np.mean(np.stack(streams), axis=0)
+        print("stream over time (flat grouping; mean over calls; t from the first workgroup's start):")
+        print("  window (us)   blocks done (TB/s)   bytes in flight at t (MB)   "
+              "race wgs resident at t   statistics wgs waiting for scalars at t")
+        for i, (rate, infl, races, waiting) in enumerate(prof):
+            if i > 0 and rate == 0 and infl == 0 and races < 0.5:
+                break
+            t = i * STREAM_WINDOW_US
+            print(f"  [{t:4.0f},{t + STREAM_WINDOW_US:4.0f})   {rate:18.2f}   {infl:25.1f}   "
+                  f"{races:22.0f}   {waiting:38.0f}")
+
+
+STREAM_WINDOW_US = 2.0
+
+
+def stream_profile(rec, batch, us_per_tick, n_windows=80):
+    """One traced call's stream over time, for flat grouping (every request
+    has max_k drafts; None otherwise): per window of STREAM_WINDOW_US from the
+    first workgroup's start, the row bytes of the statistics blocks whose
+    partial was stored in it (as TB/s), and at the window's start the bytes
+    of blocks whose scalars had arrived but whose partial was not yet stored,
+    the race workgroups started and not yet done, and the statistics
+    workgroups started but still waiting for their request's scalars.  A
+    block's bytes are its chunks of its row (8 KiB each, the row's last one
+    shorter); a greedy request's groups past its K+1 rows hold none."""
+    import numpy as np
+    if batch.n_draft_rows != batch.B * batch.max_k:
+        return None
+    esz = 2 if batch.dtype == 1 else 4
+    chunk = 8192 // esz
+    nc = -(-batch.V // chunk)
+    bpr = -(-nc // 8)
+    head = rec[:, 0]
+    live = head != 0
+    rec, head = rec[live].astype(np.int64), head[live]
+    kind = (head & 0xFF).astype(int)
+    req = ((head >> 8) & 0xFFFFFF).astype(int)
+    grp = (head >> 32).astype(int)
+    t0 = rec[:, 1][rec[:, 1] > 0].min()
+    us = (rec - t0) * us_per_tick
+    s_m = (kind == 1) & (rec[:, 3] > 0)
+    nbytes = np.zeros(len(rec))
+    for i in np.nonzero(s_m)[0]:
+        b = req[i]
+        nrows = batch.max_k + 1 if batch.temperature[b] == 0 else 2 * batch.max_k + 1
+        row, blk = divmod(grp[i], bpr)
+        if row >= nrows:
+            continue
+        c0, c1 = blk * 8, min(blk * 8 + 8, nc)
+        tokens = min(c1 * chunk, batch.V) - c0 * chunk
+        nbytes[i] = tokens * esz
+    r_m = kind == 2
+    r_end = us[:, 1:].max(axis=1)
+    out = np.zeros((n_windows, 4))
+    for w in range(n_windows):
+        t = w * STREAM_WINDOW_US
+        done = s_m & (us[:, 3] > t) & (us[:, 3] <= t + STREAM_WINDOW_US)
+        out[w, 0] = nbytes[done].sum() / (STREAM_WINDOW_US * 1e6)
+        infl = s_m & (us[:, 2] <= t) & (us[:, 3] > t)
+        out[w, 1] = nbytes[infl].sum() / 1e6
+        out[w, 2] = (r_m & (us[:, 1] <= t) & (r_end > t)).sum()
+        out[w, 3] = ((kind == 1) & (us[:, 1] <= t) & (us[:, 2] > t)).sum()
+    return out
 
 
 def trace_summary(rec, batch, us_per_tick) -> dict:
