@@ -509,9 +509,11 @@ def stream_profile(rec, batch, us_per_tick, n_windows=80):
     block's bytes are its chunks of its row (8 KiB each, the row's last one
     shorter); a greedy request's groups past its K+1 rows hold none."""
     import numpy as np
+
+    from rejection_sampling_verify_scaled_amd import workloads as W
     if batch.n_draft_rows != batch.B * batch.max_k:
         return None
-    esz = 2 if batch.dtype == 1 else 4
+    esz = 2 if batch.dtype == W.DTYPE_BF16 else 4
     chunk = 8192 // esz
     nc = -(-batch.V // chunk)
     bpr = -(-nc // 8)
