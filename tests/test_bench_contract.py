@@ -67,3 +67,35 @@ def test_committed_traffic_is_tied_to_sources(name, sources):
             assert got == rec["hbm_bytes_per_launch"]
         else:
             assert got is None, f"{p} is stale but bench.py would report it"
+
+
+def test_stream_profile_counts_block_bytes():
+    """The stage trace's stream table from a synthetic trace (one tick = 1 us):
+    a sampled request's 36 blocks (9 rows) store at 3 us, a greedy request's
+    20 blocks with rows (5 rows; its 16 surplus groups hold none) at 5 us, a
+    race workgroup lives from 0 to 9 us.  Blocks of a row add up to the row."""
+    full = W.make_batch(2, 0)
+    batch = W.subset_requests(full, [0, 40])  # request 0 sampled, request 40 greedy
+    assert batch.temperature[0] > 0 and batch.temperature[1] == 0
+    rows = []
+    for b, stored in ((0, 3), (1, 5)):
+        for grp in range(36):
+            r = np.zeros(10, dtype=np.uint64)
+            r[0] = 1 | (b << 8) | (grp << 32)
+            r[1], r[2], r[3] = 100, 101, 100 + stored  # start, scalars loaded, partial stored
+            rows.append(r)
+    race = np.zeros(10, dtype=np.uint64)
+    race[0] = 2 | (0 << 8)
+    race[1], race[9] = 100, 109
+    rows.append(race)
+    prof = bench.stream_profile(np.stack(rows), batch, 1.0, n_windows=5)
+    row_mb = batch.V * 2 / 1e6
+    w = bench.STREAM_WINDOW_US
+    assert prof[1, 0] == pytest.approx(9 * row_mb / w)   # [2, 4): the sampled request's rows
+    assert prof[2, 0] == pytest.approx(5 * row_mb / w)   # [4, 6): the greedy request's rows
+    assert prof[1, 1] == pytest.approx(14 * row_mb)      # both in flight at 2 us
+    assert prof[2, 1] == pytest.approx(5 * row_mb)       # the greedy one at 4 us
+    assert prof[0, 3] == 72 and prof[1, 3] == 0          # all wait for scalars at 0 us
+    assert prof[1, 2] == 1 and prof[4, 2] == 1           # the race workgroup at 2 and 8 us
+    ragged = W.make_batch(5, 0)
+    assert bench.stream_profile(np.stack(rows), ragged, 1.0) is None  # column grouping
