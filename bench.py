@@ -1113,6 +1113,13 @@ def main():
         "copy_gbs": {"value": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                      "what": "1 GiB device-to-device copy on the same stream, read + written bytes"},
     }
+    # tokens emitted per step: the accepted drafts and one stop or bonus token
+    # per request that did not fail (every timed step runs the same inputs)
+    emitted = int(sum(int(a) + 1 for a in gpu_acc if a >= 0))
+    line["emitted_tokens_per_s"] = emitted / (ms_per_step * 1e-3)
+    if line["roofline"]["traffic"] is not None:
+        # counter bytes per launch over the kernel's duration in the timed region
+        line["traffic_gbs"] = line["roofline"]["traffic"] / (k_us * 1e-6) / 1e9
 
     if not args.no_cpu_baseline:
         import oracle
