@@ -82,6 +82,22 @@ def test_early_exit_mtp_race_layouts(B):
     assert tally.sampled + tally.greedy + tally.failed == b.B
 
 
+def test_early_exit_races_per_region_with_k0():
+    """B=512 requests with K in {0, 1} (V=129280, bf16, mixed temperatures):
+    max_k = 1 and more race workgroups than one resident generation, so the
+    races run per stage region; the K = 0 requests race their bonus row in
+    region 0.  Every request against the oracle."""
+    rng = np.random.default_rng(77)
+    B, V = 512, 129280
+    ks = [int(x) for x in rng.integers(0, 2, size=B)]
+    temps = rng.choice([0.0, 0.7, 1.0], size=B)
+    bt = W.make_custom_batch(rng, W.DTYPE_BF16, V, ks, temps, seed=91, max_k=1)
+    say("early exit races per region, K in {0, 1}")
+    tally = check(bt, run_ee(bt), oracle.verify_batch(bt))
+    print(tally)
+    assert tally.sampled + tally.greedy + tally.failed == bt.B
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_early_exit_large_workloads(cfg):
     b = W.make_batch(cfg, 0)
