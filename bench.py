@@ -96,6 +96,10 @@ def parse():
                     help="per-stage timeline of the verify kernel on --workload, from its "
                          "stage-trace build (libspecverify_trace.so): --steps traced calls "
                          "after --warmup untraced ones; prints a summary, no JSON line")
+    ap.add_argument("--crossover", action="store_true",
+                    help="full verify against the early-exit verify on the first B requests "
+                         "of workloads 2-5 (interleaved rounds, median); prints a table, no "
+                         "JSON line")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                     help="for hardware-counter runs: after the warmup, run --steps verify "
                          "calls, then 5 device copies of MIB MiB (the counters' reference "
@@ -550,6 +554,80 @@ def stream_profile(rec, batch, us_per_tick, n_windows=80):
     return out
 
 
+CROSSOVER_CASES = {2: (16, 32, 64), 4: (64, 128, 256, 512), 3: (16, 32, 64, 128, 256),
+                   5: (64, 128, 256, 512, 1024)}
+
+
+def crossover(rounds: int = 7):
+    """Full verify (spec_verify_sample) against the early-exit verify on the
+    first B requests of each workload: both entry points in one process on
+    the same inputs, rotated over enough input copies to leave the Infinity
+    Cache, timed with HIP events over back-to-back calls in `rounds`
+    interleaved rounds (median); the accept lengths of the two are compared."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_scaled_amd import binding
+    from rejection_sampling_verify_scaled_amd import workloads as W
+
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    vp = ctypes.c_void_p
+    print(f"full verify against early exit, us per call (median of {rounds} interleaved rounds)")
+    for wl, sizes in CROSSOVER_CASES.items():
+        full = W.make_batch(wl, 0)
+        for B in sizes:
+            batch = W.subset_requests(full, range(B)) if B < full.B else full
+            d = binding.to_device_batch(batch, dev)
+            V, K, n_d = batch.V, batch.max_k, batch.n_draft_rows
+            per_copy = d["target"].numel() * d["target"].element_size() + \
+                d["draft"].numel() * d["draft"].element_size()
+            copies = max(1, math.ceil(1.25e9 / per_copy))
+            tg = [d["target"]] + [d["target"].clone() for _ in range(copies - 1)]
+            dr = [d["draft"]] + [d["draft"].clone() for _ in range(copies - 1)]
+            acc = torch.empty(B, dtype=torch.int32, device=dev)
+            out = torch.empty(n_d + B, dtype=torch.int32, device=dev)
+            st = torch.cuda.current_stream(dev)
+            dt = binding.SV_BF16 if d["target"].dtype == torch.bfloat16 else binding.SV_F32
+            fns = [(lib.spec_verify_sample, binding.workspace_bytes(B, V, K)),
+                   (lib.spec_verify_sample_early_exit, binding.early_exit_workspace_bytes(B, V, K))]
+            wss = [torch.zeros(n, dtype=torch.uint8, device=dev) for _, n in fns]
+
+            def call(j, c):
+                f, n = fns[j]
+                rc = f(vp(tg[c].data_ptr()), vp(dr[c].data_ptr()), dt, B, V, K, n_d,
+                       vp(d["offsets"].data_ptr()), vp(d["tokens"].data_ptr()),
+                       vp(d["temperature"].data_ptr()), ctypes.c_uint64(batch.seed),
+                       vp(acc.data_ptr()), vp(out.data_ptr()), None, None, vp(wss[j].data_ptr()),
+                       n, vp(st.cuda_stream))
+                if rc != 0:
+                    raise SystemExit(f"call returned {rc}")
+            accs = []
+            for j in range(2):
+                for i in range(5):
+                    call(j, i % copies)
+                call(j, 0)
+                torch.cuda.synchronize()
+                accs.append(acc.cpu().numpy().copy())
+            steps = 50 if wl in (2, 4) else 10
+            T = np.zeros((rounds, 2))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            for r in range(rounds):
+                for j in ((0, 1) if r % 2 == 0 else (1, 0)):
+                    for i in range(3):
+                        call(j, i % copies)
+                    e0.record(st)
+                    for i in range(steps):
+                        call(j, i % copies)
+                    e1.record(st)
+                    torch.cuda.synchronize()
+                    T[r, j] = e0.elapsed_time(e1) * 1e3 / steps
+            same = int((accs[0] == accs[1]).sum())
+            print(f"  workload {wl} ({W.WORKLOADS[wl].name.split()[0]}) B={B:5d}  full {np.median(T[:, 0]):8.1f}"
+                  f"  early exit {np.median(T[:, 1]):8.1f}  accept_len agree {same}/{B}", flush=True)
+
+
 def trace_summary(rec, batch, us_per_tick) -> dict:
     """One traced call's stage figures (see stage_trace)."""
     import numpy as np
@@ -925,6 +1003,11 @@ def main():
         if args.gpus != 1:
             raise SystemExit("bench.py measures one GPU")
         stage_trace(args)
+        return
+    if args.crossover:
+        if args.gpus != 1:
+            raise SystemExit("bench.py measures one GPU")
+        crossover()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
