@@ -76,6 +76,8 @@ constexpr uint32_t kExpiredIdx = 0xFFFFFFFEu;  // race slot word: a wait expired
 // Workgroups of this kernel one CU holds at once (at most 96 VGPRs per lane:
 // five waves per SIMD, so five 4-wave workgroups per CU).
 constexpr int kWorkgroupsPerCu = 5;
+// XCDs of an MI355X; the dispatcher deals workgroups to them round robin.
+constexpr int kXcds = 8;
 
 // Stage timestamps (a build with SV_TRACE defined only; the product build
 // compiles them out).  Workgroup g records its role in word 0 of its record
@@ -1026,6 +1028,16 @@ int dispatch(const void* target, const void* draft, int32_t dtype, int32_t B, in
     prm.mr = std::min(prm.nc, prm.m * std::max(1, 6 / prm.m));
   }
   prm.ngr = static_cast<int32_t>(ceil_div(prm.nc, prm.mr));
+  // Workgroups go to the XCDs round robin by grid index, and a request's race
+  // workgroups sit ng + ngr after the previous request's.  With fewer race
+  // workgroups than XCDs and ng + ngr a multiple of the XCD count, every
+  // request's races would run on the same few XCDs (B=512 K=1 with four race
+  // workgroups of 8 or 9 chunks: 121-131 us, against 78-81 us with five or
+  // six of 6 or 7 chunks), so the race is narrowed until they rotate.
+  while (prm.ngr < kXcds && (prm.ng + prm.ngr) % kXcds == 0 && prm.mr > 1) {
+    --prm.mr;
+    prm.ngr = static_cast<int32_t>(ceil_div(prm.nc, prm.mr));
+  }
   // Race placement.  A race workgroup polls, holding its slot, until its
   // request's statistics are in; placed too early it idles a slot the stream
   // needs, too late it starts the request's dependent chain late.  The lag,

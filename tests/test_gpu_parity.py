@@ -115,6 +115,21 @@ def test_uniform_k_vocab(dtype, V, K):
     compare(b, gg, oracle.verify_batch(b, greedy_only=True), greedy_only=True)
 
 
+@pytest.mark.parametrize("dtype,V,K", [(W.DTYPE_BF16, 16385, 2), (W.DTYPE_F32, 12289, 2),
+                                        (W.DTYPE_BF16, 40961, 4), (W.DTYPE_BF16, 131073, 0)])
+def test_race_width_rotated_over_xcds(dtype, V, K):
+    """Shapes whose default race width would put every request's race
+    workgroups on the same XCDs (fewer than eight of them, ng + ngr a multiple
+    of eight), so the launch narrows the race (to one chunk per workgroup at
+    V=16385 and V=40961): same results as the oracle."""
+    rng = np.random.default_rng(V * 7 + K + dtype)
+    B = 40
+    temps = rng.choice([0.0, 0.6, 1.0, 1.4], size=B)
+    b = W.make_custom_batch(rng, dtype, V, [K] * B, temps, seed=V + 3, max_k=K)
+    say(f"race width rotation V={V} K={K} dtype={dtype}")
+    compare(b, run_gpu(b, "sample"), oracle.verify_batch(b))
+
+
 @pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
 @pytest.mark.parametrize("V", [262144, 300007])
 def test_large_vocab(dtype, V):
