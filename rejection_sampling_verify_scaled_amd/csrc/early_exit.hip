@@ -79,6 +79,8 @@ namespace {
 constexpr int kRaceChunks = 8;
 constexpr int kRaceChunksNarrow = 4;
 constexpr int64_t kNarrowRaceBelow = 512;
+// XCDs of an MI355X; the dispatcher deals workgroups to them round robin.
+constexpr int kEeXcds = 8;
 constexpr int kStageRows = 2;      // a stage streams target row s and draft row s
 constexpr int kDecSlots = 5;       // decision record: code, m_p, log2 S_p, m_q, log2 S_q
 constexpr uint32_t kCont = 1u, kRej = 2u, kDone = 3u;  // decision codes (low byte)
@@ -97,7 +99,7 @@ struct EeParams {
   int32_t B, V, max_k, n_draft_rows;
   int32_t nc;   // chunks per row
   int32_t ngs;  // statistics workgroups per (request, stage): ceil(2 nc / 8)
-  int32_t rcw;  // race chunks per race workgroup (kRaceChunks or kRaceChunksNarrow)
+  int32_t rcw;  // race chunks per race workgroup (kRaceChunks, kRaceChunksNarrow or fewer)
   int32_t ngr;  // race workgroups per (request, region): ceil(nc / rcw)
   uint64_t* part;  // [B][max_k + 1][2][nc] stage partials
   uint64_t* race;  // [B][ngr] race winners
@@ -782,6 +784,17 @@ int spec_verify_sample_early_exit(const void* target_logits, const void* draft_l
   // B=64 K=4 44.3 -> 40.3 us and B=64 K=1 31.8 -> 26.9 us.
   const int64_t resident = static_cast<int64_t>(bf16 ? 4 : 5) * device_compute_units();
   prm.endrace = max_k > 1 || static_cast<int64_t>(B) * prm.ngr <= resident;
+  // With the races in every region, a request's statistics and races span
+  // ngs + ngr workgroups, and the dispatcher deals workgroups to the XCDs
+  // round robin by index: with fewer race workgroups than XCDs and a span that
+  // is a multiple of the XCD count, every request's races would run on the
+  // same few XCDs.  Narrower races rotate them (B=512 K=1 V=70000 bf16:
+  // 93.3 -> 68.8 us; B=768 V=65600: 129.6 -> 92.4 us).
+  while (!prm.endrace && prm.ngr < kEeXcds && (prm.ngs + prm.ngr) % kEeXcds == 0 &&
+         prm.rcw > 1) {
+    --prm.rcw;
+    prm.ngr = static_cast<int32_t>(ee_ceil_div(prm.nc, prm.rcw));
+  }
   const int64_t grid =
       prm.endrace ? static_cast<int64_t>(max_k + 1) * B * prm.ngs + static_cast<int64_t>(B) * prm.ngr
                   : static_cast<int64_t>(max_k + 1) * B * (prm.ngs + prm.ngr);

@@ -98,6 +98,21 @@ def test_early_exit_races_per_region_with_k0():
     assert tally.sampled + tally.greedy + tally.failed == bt.B
 
 
+@pytest.mark.parametrize("B,V", [(512, 70000), (768, 65600)])
+def test_early_exit_races_rotated_over_xcds(B, V):
+    """K = 1 batches whose races run per stage region with three race
+    workgroups and five statistics workgroups per request: a span of eight,
+    which would put every request's races on the same XCDs, so the launch
+    narrows the race.  Every request against the oracle."""
+    rng = np.random.default_rng(B + V)
+    temps = rng.choice([0.0, 0.7, 1.0], size=B)
+    bt = W.make_custom_batch(rng, W.DTYPE_BF16, V, [1] * B, temps, seed=V, max_k=1)
+    say(f"early exit race rotation B={B} V={V}")
+    tally = check(bt, run_ee(bt), oracle.verify_batch(bt))
+    print(tally)
+    assert tally.sampled + tally.greedy + tally.failed == bt.B
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_early_exit_large_workloads(cfg):
     b = W.make_batch(cfg, 0)
