@@ -696,17 +696,18 @@ EeLayout ee_layout(int32_t B, int32_t V, int32_t max_k) {
   return L;
 }
 
-// After the verify kernel (same stream): zeroes the decision records, and
-// the stage partials still set (those streamed on speculation past a stop;
-// every other partial was zeroed by its reader).  The partials are read
-// first, so only the few still set are written.
+// After the verify kernel (same stream): zeroes the decision records and the
+// stage partials (those streamed on speculation past a stop are still set;
+// every other partial was zeroed by its reader).  Every slot takes a store,
+// with no load first: one memory round trip (B=64 K=4 bf16 40.6 -> 39.9 us
+// per call against loading each partial and storing the few still set).
 __global__ __launch_bounds__(kThreads) void ee_clear_records(uint64_t* dec, int64_t n_dec,
                                                               uint64_t* part, int64_t n_part) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
        i < n_dec + n_part; i += static_cast<int64_t>(gridDim.x) * kThreads) {
     if (i < n_dec)
       dec[i] = 0u;
-    else if (part[i - n_dec] != 0u)
+    else
       part[i - n_dec] = 0u;
   }
 }
