@@ -116,7 +116,8 @@ def test_uniform_k_vocab(dtype, V, K):
 
 
 @pytest.mark.parametrize("dtype,V,K", [(W.DTYPE_BF16, 16385, 2), (W.DTYPE_F32, 12289, 2),
-                                        (W.DTYPE_BF16, 40961, 4), (W.DTYPE_BF16, 131073, 0)])
+                                        (W.DTYPE_BF16, 40961, 4), (W.DTYPE_BF16, 131073, 0),
+                                        (W.DTYPE_BF16, 152064, 0)])
 def test_race_width_rotated_over_xcds(dtype, V, K):
     """Shapes whose default race width would put every request's race
     workgroups on the same XCDs (fewer than eight of them, ng + ngr a multiple
